@@ -1,0 +1,15 @@
+"""MI355X (gfx950) attention-space block retrieval and rematerialization.
+
+The per-step working-set update of KVMem ("Virtualizing Million-Token Agent
+Workspaces on a Consumer GPU", Sec. 4.2-4.4, Sec. 5) as a C-ABI library
+(``libkvm.so``, declared in ``include/kvm.h``) of hand-written HIP kernels,
+with this thin Python binding over it (same names as the C entry points).
+PyTorch supplies device memory and streams only.
+"""
+from .api import (  # noqa: F401
+    Dims, KvmCtx, KvmError, RematStats, dims_for, dtype_code, kvm_version, kvm_build_index,
+    kvm_score_ws_bytes, kvm_score_blocks, kvm_select_ws_bytes, kvm_select,
+    KVM_F32, KVM_BF16, KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED,
+    KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
+)
+from ._abi import EXPORTED, LIB_PATH  # noqa: F401

@@ -1,0 +1,147 @@
+"""Python names for the C entry points of include/kvm.h (marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+from ._abi import (  # noqa: F401
+    Dims, KvmError, RematStats, KVM_F32, KVM_BF16, KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED,
+    KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
+)
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def dims_for(wl) -> Dims:
+    """kvm_dims of a workload description (anything with the five fields)."""
+    return Dims(wl.n_layers, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.block_tokens)
+
+
+def dtype_code(dtype: str) -> int:
+    return KVM_F32 if dtype == "f32" else KVM_BF16
+
+
+def kvm_version() -> int:
+    return _abi.lib().kvm_version()
+
+
+def kvm_build_index(dims: Dims, dtype: int, k_raw, k_block_stride: int, first_block: int,
+                    n_blocks: int, index, index_cap_blocks: int, stream=None) -> None:
+    rc = _abi.lib().kvm_build_index(ctypes.byref(dims), dtype, _ptr(k_raw), k_block_stride,
+                                    first_block, n_blocks, _ptr(index), index_cap_blocks,
+                                    _stream(stream))
+    _abi.check(rc, "kvm_build_index")
+
+
+def kvm_score_ws_bytes(dims: Dims, dtype: int, n_q_tokens: int, n_blocks: int,
+                       index_loc: int = KVM_INDEX_DEVICE, tile_blocks: int = 0) -> int:
+    return int(_abi.lib().kvm_score_ws_bytes(ctypes.byref(dims), dtype, n_q_tokens, n_blocks,
+                                             index_loc, tile_blocks))
+
+
+def kvm_score_blocks(dims: Dims, dtype: int, q, n_q_tokens: int, index, index_cap_blocks: int,
+                     n_blocks: int, index_loc: int, tile_blocks: int, scores, ws, ws_bytes: int,
+                     stream=None) -> None:
+    rc = _abi.lib().kvm_score_blocks(ctypes.byref(dims), dtype, _ptr(q), n_q_tokens, _ptr(index),
+                                     index_cap_blocks, n_blocks, index_loc, tile_blocks,
+                                     _ptr(scores), _ptr(ws), ws_bytes, _stream(stream))
+    _abi.check(rc, "kvm_score_blocks")
+
+
+def kvm_select_ws_bytes(n_blocks: int) -> int:
+    return int(_abi.lib().kvm_select_ws_bytes(n_blocks))
+
+
+def kvm_select(scores, n_blocks: int, n_sink: int, n_recent: int, budget_blocks: int,
+               block_tokens: int, sel, n_sel, base_pos, ws=None, ws_bytes: int = 0,
+               stream=None) -> None:
+    rc = _abi.lib().kvm_select(_ptr(scores), n_blocks, n_sink, n_recent, budget_blocks,
+                               block_tokens, _ptr(sel), _ptr(n_sel), _ptr(base_pos), _ptr(ws),
+                               ws_bytes, _stream(stream))
+    _abi.check(rc, "kvm_select")
+
+
+class KvmCtx:
+    """Owner of one kvm_ctx (block records, side stream, staging, RoPE table)."""
+
+    def __init__(self, dims: Dims, dtype: int, k_view, v_view, k_shadow, n_slots: int,
+                 max_blocks: int, max_pos: int, rope_theta: float = 10000.0,
+                 rope_layout: int = 0, batch_blocks: int = 64, staging_blocks: int = 0):
+        d = _abi.CtxDesc()
+        d.dims = dims
+        d.dtype = dtype
+        d.rope_layout = rope_layout
+        d.rope_theta = rope_theta
+        d.max_pos = max_pos
+        d.n_slots = n_slots
+        d.k_view = _ptr(k_view)
+        d.v_view = _ptr(v_view)
+        d.k_shadow = _ptr(k_shadow)
+        d.max_blocks = max_blocks
+        d.batch_blocks = batch_blocks
+        d.staging_blocks = staging_blocks
+        h = ctypes.c_void_p()
+        _abi.check(_abi.lib().kvm_ctx_create(ctypes.byref(d), ctypes.byref(h)), "kvm_ctx_create")
+        self._h = h
+        self._keep = []           # callbacks and buffers the library points at
+
+    def close(self):
+        if self._h:
+            _abi.lib().kvm_ctx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def kvm_ctx_set_source(self, first_block: int, n_blocks: int, k_base, v_base,
+                           block_stride: int, loc: int) -> None:
+        rc = _abi.lib().kvm_ctx_set_source(self._h, first_block, n_blocks, _ptr(k_base),
+                                           _ptr(v_base), block_stride, loc)
+        _abi.check(rc, "kvm_ctx_set_source")
+
+    def kvm_ctx_set_gather(self, first_block: int, n_blocks: int, fn) -> None:
+        """fn(block, which, dst_ptr) -> int, called from library worker threads."""
+        cb = _abi.GATHER_FN(lambda user, b, which, dst: int(fn(int(b), int(which), int(dst))))
+        self._keep.append(cb)
+        rc = _abi.lib().kvm_ctx_set_gather(self._h, first_block, n_blocks, cb, None)
+        _abi.check(rc, "kvm_ctx_set_gather")
+
+    def kvm_ctx_register_resident(self, first_block: int, n_blocks: int, k_raw, v_raw,
+                                  block_stride: int, stream=None) -> None:
+        rc = _abi.lib().kvm_ctx_register_resident(self._h, first_block, n_blocks, _ptr(k_raw),
+                                                  _ptr(v_raw), block_stride, _stream(stream))
+        _abi.check(rc, "kvm_ctx_register_resident")
+
+    def kvm_rematerialize(self, sel, n_sel, page_table, stream=None) -> dict:
+        st = RematStats()
+        rc = _abi.lib().kvm_rematerialize(self._h, _ptr(sel), _ptr(n_sel), _ptr(page_table),
+                                          ctypes.byref(st), _stream(stream))
+        _abi.check(rc, "kvm_rematerialize")
+        return st.as_dict()
+
+    def kvm_ctx_sync(self) -> None:
+        _abi.check(_abi.lib().kvm_ctx_sync(self._h), "kvm_ctx_sync")
+
+    def kvm_ctx_block_state(self, block: int):
+        s, p = ctypes.c_int32(), ctypes.c_int32()
+        _abi.check(_abi.lib().kvm_ctx_block_state(self._h, block, ctypes.byref(s), ctypes.byref(p)),
+                   "kvm_ctx_block_state")
+        return s.value, p.value

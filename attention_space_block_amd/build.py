@@ -1,0 +1,34 @@
+"""Compile libkvm.so for gfx950 with hipcc (in-tree, no JIT cache)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SOURCES = ["api.hip", "build_index.hip", "score.hip", "select.hip", "remat.hip"]
+LIB = os.path.join(HERE, "libkvm.so")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def build(verbose: bool = False) -> str:
+    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = ["hipcc", *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
+           *srcs, "-o", tmp, "-lpthread"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,96 @@
+// Shared host/device helpers of libkvm (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kvm.h"
+
+namespace kvm {
+
+// ---- error reporting (thread-local last error) ---------------------------
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define KVM_CHECK_ARG(cond, ...)        \
+  do {                                  \
+    if (!(cond)) {                      \
+      ::kvm::set_error(__VA_ARGS__);    \
+      return KVM_EINVAL;                \
+    }                                   \
+  } while (0)
+
+#define KVM_HIP(call)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      ::kvm::set_error("%s failed: %s (%s:%d)", #call, hipGetErrorString(e_),      \
+                       __FILE__, __LINE__);                                        \
+      return KVM_EHIP;                                                             \
+    }                                                                              \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int dtype_bytes(int32_t dtype) { return dtype == KVM_F32 ? 4 : 2; }
+
+// Validate dims shared by every entry point.
+int check_dims(const kvm_dims* d, int32_t dtype);
+
+// ---- device helpers -------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Round-to-nearest-even double -> bf16 bits, directly (no float detour), for
+// normal-range finite values: keep 8 significant bits of the double.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  // bf16 keeps sign, 8 exponent bits (rebiased) and 7 mantissa bits. Round the
+  // 52-bit double mantissa to 7 bits, ties to even, then rebias.
+  uint64_t sign = u >> 63;
+  int64_t exp = (int64_t)((u >> 52) & 0x7ff);
+  uint64_t man = u & 0xfffffffffffffull;
+  if (exp == 0) return (uint16_t)(sign << 15);  // zero (subnormal doubles -> 0)
+  uint64_t keep = man >> 45;                     // 7 bits
+  uint64_t rest = man & ((1ull << 45) - 1);
+  uint64_t half = 1ull << 44;
+  if (rest > half || (rest == half && (keep & 1))) keep += 1;
+  if (keep == 128) { keep = 0; exp += 1; }
+  int64_t e8 = exp - 1023 + 127;
+  if (e8 <= 0) return (uint16_t)(sign << 15);    // below bf16 normal range
+  if (e8 >= 255) return (uint16_t)((sign << 15) | 0x7f80u);
+  return (uint16_t)((sign << 15) | ((uint64_t)e8 << 7) | keep);
+}
+
+// Streaming (non-temporal) 16-byte loads and stores.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt(void* p, const uint4& v) {
+  u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
+// XCD-aware remap of a linear workgroup id: hardware dispatches workgroup i to
+// XCD (i % 8). Returns a logical id such that each XCD receives one contiguous
+// range of logical ids (so neighbouring logical work shares one L2).
+// Requires total % 8 == 0.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+  return (bid & 7u) * (total >> 3) + (bid >> 3);
+}
+
+}  // namespace kvm

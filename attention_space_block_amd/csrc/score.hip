@@ -1,0 +1,786 @@
+// Block relevance, KVMem Sec. 4.3 Eq. (10), with the tiled/global-softmax
+// organisation of Sec. 5:
+//   R_b = 1/(L*Hq) sum_{l,h,m} softmax_b( q[l,h,m] . kbar[l,g(h),b] / sqrt(d) ).
+// All exponentials are exp2 of x = (q . kbar) * log2(e)/sqrt(d); LSE values
+// are kept in the log2 domain.
+//
+// Two organisations, chosen by the row count TG = T*G of one (layer, KV head):
+//
+// MFMA path (bf16, TG >= 64): per (l, g) the scores are the dense product
+// Q_g[TG x d] * Kbar^T[d x N] on v_mfma_f32_32x32x16_bf16. The per-row softmax
+// needs each row's log-sum-exp before any block's share is known, so:
+//   pass 1: rows stationary in registers (B operand), Mean-K tiles streamed
+//           through double-buffered LDS (A operand); the 32x32 result puts one
+//           query row in each lane (16 blocks per lane), so the running max /
+//           sum-exp is lane-local: a tile max, one rescale exp per tile and
+//           16 exps; tile sums folded in fp32, the running sum kept in fp64.
+//   pass 2: blocks stationary (B operand), query tiles and their LSE streamed
+//           through LDS (A operand); now one block per lane, so the column sum
+//           over query rows is lane-local again. Partial R per (l, g) go to a
+//           workspace and a fixed-order fp64 reduction makes R deterministic.
+// Workgroup ids are remapped so that each XCD works on whole (l, g) pairs and
+// the shared operand of a pair stays in that XCD's L2.
+//
+// Stored-score path (any dtype, small TG, and the host-tiled index): pass 1
+// computes every score once on the VALU, stores it (fp32) and emits per-chunk
+// (max, sum-exp) partials; a combine kernel forms the LSE in fp64; pass 2
+// reads the stored scores back and sums exp2(x - LSE) per block in fp64.
+// HBM-bound: one pass over the index plus a write and a read of TG*N*L*Hkv
+// floats. The host-tiled form streams 64 MiB-class tiles H2D through two
+// staging buffers on a side stream, double-buffered with events.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace kvm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+static constexpr float LOG2E = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// MFMA pass 1: partial (max, sum) of exp2(x) per query row and block split.
+// Workgroup: 4 waves x 64 query rows = 256 rows of one (l, g); loops over the
+// blocks of one split in LDS tiles of 64 blocks.
+template <int D>
+struct MfmaShape {
+  static constexpr int KS = D / 16;               // MFMA k-steps
+  static constexpr int ROW_B = D * 2;             // bytes of one bf16 row
+  static constexpr int LDS_ROW = ROW_B + 16;      // padded LDS row (bank spread)
+  static constexpr int TILE = 64;                 // rows staged per iteration
+  static constexpr int LOADS = TILE * ROW_B / (256 * 16);  // 16-B loads per thread
+};
+
+struct Pass1Args {
+  const uint16_t* q;        // [L][Hq][T][D]
+  const uint16_t* index;    // [L][Hkv][cap][D]
+  int64_t cap;
+  int32_t n_blocks;
+  int32_t T, Hq, Hkv, G, TG;
+  int32_t row_chunks;       // ceil(TG / 256)
+  int32_t nsplit;
+  int32_t split_blocks;     // blocks per split (multiple of 64)
+  float scale;              // log2(e)/sqrt(d)
+  float2* part;             // [nlg][nsplit][TGp] (max, sum)
+  int32_t TGp;              // row_chunks * 256
+  int32_t nlg;
+  uint32_t total_wg;        // padded to a multiple of 8
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
+  using S = MfmaShape<D>;
+  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE * S::LDS_ROW];
+  const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
+  const int32_t per_lg = a.row_chunks * a.nsplit;
+  const int32_t L_lg = (int32_t)(lid / per_lg);  // (l, g) flattened = l*Hkv + g
+  if (L_lg >= a.nlg) return;                     // grid padding
+  const int32_t rem = (int32_t)(lid % per_lg);
+  const int32_t split = rem / a.row_chunks;
+  const int32_t rchunk = rem % a.row_chunks;
+  const int l = L_lg / a.Hkv, g = L_lg % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  // B operand: two 32-row tiles of this wave's query rows (stationary).
+  bf16x8 bq[2][S::KS];
+  const int row_base = rchunk * 256 + wave * 64;
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int rho = row_base + ct * 32 + col;
+    const bool ok = rho < a.TG;
+    const int hh = g * a.G + (ok ? rho / a.T : 0);
+    const int m = ok ? rho % a.T : 0;
+    const uint16_t* qp = a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      bq[ct][ks] = as_bf16x8(v);
+    }
+  }
+
+  const int32_t b_begin = split * a.split_blocks;
+  int32_t b_end = b_begin + a.split_blocks;
+  if (b_end > a.n_blocks) b_end = a.n_blocks;
+  const int32_t ntiles = b_end > b_begin ? (b_end - b_begin + S::TILE - 1) / S::TILE : 0;
+  const uint16_t* kb = a.index + (int64_t)L_lg * a.cap * D;
+
+  float m_run[2] = {-INFINITY, -INFINITY};
+  double s_run[2] = {0.0, 0.0};
+
+  uint4 stage[S::LOADS];
+  auto gload = [&](int tile) {
+    const int32_t t0 = b_begin + tile * S::TILE;
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+      const int e = (i * 256 + threadIdx.x);      // 16-B piece id in the tile
+      const int r = e / (S::ROW_B / 16);
+      const int c = e % (S::ROW_B / 16);
+      const int32_t b = t0 + r;
+      stage[i] = b < b_end ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + c * 8)
+                           : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+      const int e = (i * 256 + threadIdx.x);
+      const int r = e / (S::ROW_B / 16);
+      const int c = e % (S::ROW_B / 16);
+      *reinterpret_cast<uint4*>(&lds[buf][r * S::LDS_ROW + c * 16]) = stage[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+    const int32_t t0 = b_begin + it * S::TILE;
+#pragma unroll
+    for (int at = 0; at < 2; ++at) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
+      const char* arow = &lds[buf][(at * 32 + col) * S::LDS_ROW + half * 16];
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bq[0][ks], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bq[1][ks], acc[1], 0, 0, 0);
+      }
+      const int32_t nvalid = b_end - (t0 + at * 32);  // blocks of this 32-tile that exist
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int i = 8 * (v >> 2) + 4 * half + (v & 3);
+          x[v] = (i < nvalid) ? acc[ct][v] * a.scale : -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+        const float m_new = fmaxf(m_run[ct], mx);
+        if (m_new == -INFINITY) continue;
+        float e[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) e[v] = exp2f(x[v] - m_new);
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int v = 0; v < w; ++v) e[v] += e[v + w];
+        const float resc = exp2f(m_run[ct] - m_new);
+        s_run[ct] = s_run[ct] * (double)resc + (double)e[0];
+        m_run[ct] = m_new;
+      }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // Merge the two lane halves (same query row, disjoint blocks).
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float mo = __shfl_xor(m_run[ct], 32);
+    const double so = __shfl_xor(s_run[ct], 32);
+    const float mm = fmaxf(m_run[ct], mo);
+    double s = 0.0;
+    if (mm != -INFINITY)
+      s = s_run[ct] * (double)exp2f(m_run[ct] - mm) + so * (double)exp2f(mo - mm);
+    if (half == 0) {
+      const int rho = row_base + ct * 32 + col;
+      a.part[((int64_t)L_lg * a.nsplit + split) * a.TGp + rho] = make_float2(mm, (float)s);
+    }
+  }
+}
+
+// LSE (log2 domain) per (l, g, row) from split partials, fp64.
+__global__ void score_lse_combine(const float2* __restrict__ part, int32_t nlg, int32_t nsplit,
+                                  int32_t TGp, int32_t TG, float* __restrict__ lse) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)nlg * TGp) return;
+  const int64_t lg = i / TGp;
+  const int32_t r = (int32_t)(i % TGp);
+  if (r >= TG) {
+    lse[i] = INFINITY;  // padded rows contribute exp2(-inf) = 0
+    return;
+  }
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(lg * nsplit + s) * TGp + r].x);
+  double sum = 0.0;
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 p = part[(lg * nsplit + s) * TGp + r];
+    if (p.x != -INFINITY) sum += (double)p.y * exp2((double)p.x - (double)M);
+  }
+  lse[i] = (float)((double)M + log2(sum));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA pass 2: column sums of exp2(x - lse) per (l, g) over all query rows.
+struct Pass2Args {
+  const uint16_t* q;
+  const uint16_t* index;
+  int64_t cap;
+  int32_t n_blocks;
+  int32_t T, Hq, Hkv, G, TG, TGp;
+  int32_t block_chunks;     // ceil(N / 256)
+  float scale;
+  const float* lse;         // [nlg][TGp]
+  float* rp;                // [nlg][N]
+  int32_t nlg;
+  uint32_t total_wg;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
+  using S = MfmaShape<D>;
+  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE * S::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][S::TILE];
+  const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
+  const int32_t lg = (int32_t)(lid / a.block_chunks);
+  if (lg >= a.nlg) return;                       // grid padding
+  const int32_t bchunk = (int32_t)(lid % a.block_chunks);
+  const int l = lg / a.Hkv, g = lg % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+
+  // B operand: this wave's two 32-block tiles (stationary).
+  bf16x8 bk[2][S::KS];
+  const int32_t blk_base = bchunk * 256 + wave * 64;
+  const uint16_t* kb = a.index + (int64_t)lg * a.cap * D;
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    const int32_t b = blk_base + bt * 32 + col;
+    const bool ok = b < a.n_blocks;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      uint4 v = ok ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + ks * 16 + half * 8)
+                   : make_uint4(0, 0, 0, 0);
+      bk[bt][ks] = as_bf16x8(v);
+    }
+  }
+  const float* lse_lg = a.lse + (int64_t)lg * a.TGp;
+  const int32_t ntiles = (a.TG + S::TILE - 1) / S::TILE;
+  uint4 stage[S::LOADS];
+  float lstage = 0.0f;
+  auto gload = [&](int tile) {
+    const int32_t r0 = tile * S::TILE;
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+      const int e = (i * 256 + threadIdx.x);
+      const int r = e / (S::ROW_B / 16);
+      const int c = e % (S::ROW_B / 16);
+      const int32_t rho = r0 + r;
+      if (rho < a.TG) {
+        const int hh = g * a.G + rho / a.T;
+        const int m = rho % a.T;
+        stage[i] = *reinterpret_cast<const uint4*>(
+            a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + c * 8);
+      } else {
+        stage[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (threadIdx.x < S::TILE) lstage = lse_lg[r0 + threadIdx.x];
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+      const int e = (i * 256 + threadIdx.x);
+      const int r = e / (S::ROW_B / 16);
+      const int c = e % (S::ROW_B / 16);
+      *reinterpret_cast<uint4*>(&lds[buf][r * S::LDS_ROW + c * 16]) = stage[i];
+    }
+    if (threadIdx.x < S::TILE) lse_s[buf][threadIdx.x] = lstage;
+  };
+  double colsum[2] = {0.0, 0.0};
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(it + 1);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 acc[2];
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[bt][v] = 0.0f;
+      const char* arow = &lds[buf][(rt * 32 + col) * S::LDS_ROW + half * 16];
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bk[0][ks], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bk[1][ks], acc[1], 0, 0, 0);
+      }
+      // LSE of the 16 rows this lane holds: rows 8*a + 4*half + b.
+      float ls[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v4 =
+            *reinterpret_cast<const float4*>(&lse_s[buf][rt * 32 + 8 * q4 + 4 * half]);
+        ls[4 * q4 + 0] = v4.x;
+        ls[4 * q4 + 1] = v4.y;
+        ls[4 * q4 + 2] = v4.z;
+        ls[4 * q4 + 3] = v4.w;
+      }
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt) {
+        float e[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) e[v] = exp2f(fmaf(acc[bt][v], a.scale, -ls[v]));
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+          for (int v = 0; v < w; ++v) e[v] += e[v + w];
+        colsum[bt] += (double)e[0];
+      }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int bt = 0; bt < 2; ++bt) {
+    const double tot = colsum[bt] + __shfl_xor(colsum[bt], 32);
+    const int32_t b = blk_base + bt * 32 + col;
+    if (half == 0 && b < a.n_blocks) a.rp[(int64_t)lg * a.n_blocks + b] = (float)tot;
+  }
+}
+
+// R[b] = (sum over (l, g) of rp[lg][b], fixed order, fp64) / (L*Hq).
+__global__ void score_reduce(const float* __restrict__ rp, int32_t nlg, int32_t n_blocks,
+                             double inv_lh, float* __restrict__ scores) {
+  const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_blocks) return;
+  double s = 0.0;
+  for (int32_t lg = 0; lg < nlg; ++lg) s += (double)rp[(int64_t)lg * n_blocks + b];
+  scores[b] = (float)(s * inv_lh);
+}
+
+// ---------------------------------------------------------------------------
+// Stored-score path. Pass 1: thread per block; the query rows of the (l, g)
+// sit in LDS as fp32; each thread keeps its Mean-K row in registers.
+template <typename T, int D>
+__device__ __forceinline__ void load_row(const T* p, float* x);
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 128>(const uint16_t* p, float* x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 64>(const uint16_t* p, float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+}
+template <>
+__device__ __forceinline__ void load_row<float, 128>(const float* p, float* x) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(p)[i];
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+  }
+}
+template <>
+__device__ __forceinline__ void load_row<float, 64>(const float* p, float* x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float4 v = reinterpret_cast<const float4*>(p)[i];
+    x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+
+struct StoredArgs {
+  const void* q;            // [L][Hq][T][D]
+  const void* index;        // rows of this launch: index + lg*lg_stride + (b - b_first)*D
+  int64_t lg_stride;        // elements between (l, g) row sets of `index`
+  int32_t b_first;          // first block of this launch (multiple of 256)
+  int32_t nb;               // blocks in this launch
+  int32_t n_blocks;         // N (layout of S)
+  int32_t T, Hq, Hkv, G, TG, nlg;
+  int32_t chunks_total;     // ceil(N / 256)
+  float scale;
+  float* S;                 // [nlg][N][TG]
+  float2* part;             // [nlg][chunks_total][TG]
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
+  extern __shared__ float smem[];       // q rows [TG][D] then reduction scratch
+  float* qs = smem;
+  float* red = smem + (int64_t)a.TG * D; // [2][4 waves]
+  const int32_t chunks_here = (a.nb + 255) / 256;
+  const int32_t lg = blockIdx.x / chunks_here;
+  const int32_t ch = blockIdx.x % chunks_here;
+  const int l = lg / a.Hkv, g = lg % a.Hkv;
+  const T* q = reinterpret_cast<const T*>(a.q);
+  for (int e = threadIdx.x; e < a.TG * D; e += 256) {
+    const int rho = e / D, t = e % D;
+    const int hh = g * a.G + rho / a.T, m = rho % a.T;
+    qs[e] = to_f32<T>(q[(((int64_t)l * a.Hq + hh) * a.T + m) * D + t]);
+  }
+  __syncthreads();
+  const int32_t bl = ch * 256 + threadIdx.x;       // block within this launch
+  const bool valid = bl < a.nb;
+  const int32_t b = a.b_first + bl;
+  float k[D];
+  if (valid)
+    load_row<T, D>(reinterpret_cast<const T*>(a.index) + (int64_t)lg * a.lg_stride +
+                       (int64_t)bl * D, k);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t gchunk = a.b_first / 256 + ch;
+  for (int rho = 0; rho < a.TG; ++rho) {
+    float x = -INFINITY;
+    if (valid) {
+      const float* qr = qs + rho * D;
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < D; ++t) acc = fmaf(qr[t], k[t], acc);
+      x = acc * a.scale;
+      a.S[((int64_t)lg * a.n_blocks + b) * a.TG + rho] = x;
+    }
+    // workgroup max, then sum of exp2(x - max), fp32 tree
+    float mx = x;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float e = valid ? exp2f(x - mx) : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
+    if (lane == 0) red[4 + wave] = e;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      a.part[((int64_t)lg * a.chunks_total + gchunk) * a.TG + rho] =
+          make_float2(mx, (red[4] + red[5]) + (red[6] + red[7]));
+    __syncthreads();
+  }
+}
+
+__global__ void score_stored_lse(const float2* __restrict__ part, int32_t nlg, int32_t chunks,
+                                 int32_t TG, float* __restrict__ lse) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)nlg * TG) return;
+  const int64_t lg = i / TG;
+  const int32_t r = (int32_t)(i % TG);
+  float M = -INFINITY;
+  for (int c = 0; c < chunks; ++c) M = fmaxf(M, part[(lg * chunks + c) * TG + r].x);
+  double sum = 0.0;
+  for (int c = 0; c < chunks; ++c) {
+    const float2 p = part[(lg * chunks + c) * TG + r];
+    if (p.x != -INFINITY) sum += (double)p.y * exp2((double)p.x - (double)M);
+  }
+  lse[i] = (float)((double)M + log2(sum));
+}
+
+__global__ __launch_bounds__(256) void score_stored_pass2(const float* __restrict__ S,
+                                                          const float* __restrict__ lse,
+                                                          int32_t nlg, int32_t TG,
+                                                          int32_t n_blocks, double inv_lh,
+                                                          float* __restrict__ scores) {
+  extern __shared__ float lse_s[];  // [nlg*TG]
+  for (int i = threadIdx.x; i < nlg * TG; i += 256) lse_s[i] = lse[i];
+  __syncthreads();
+  const int32_t b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= n_blocks) return;
+  double s = 0.0;
+  for (int32_t lg = 0; lg < nlg; ++lg) {
+    const float* row = S + ((int64_t)lg * n_blocks + b) * TG;
+    const float* ls = lse_s + lg * TG;
+    float t = 0.0f;
+    for (int r = 0; r < TG; ++r) t += exp2f(row[r] - ls[r]);
+    s += (double)t;
+  }
+  scores[b] = (float)(s * inv_lh);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+
+struct Plan {
+  bool mfma;
+  int32_t TG, TGp, nsplit, split_blocks, row_chunks, block_chunks, chunks;
+  size_t off_part, off_lse, off_rp, off_S, off_stage, bytes;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, int32_t loc,
+                      int64_t tile_blocks) {
+  Plan p{};
+  const int32_t G = d->n_q_heads / d->n_kv_heads;
+  const int32_t nlg = d->n_layers * d->n_kv_heads;
+  p.TG = T * G;
+  p.mfma = dtype == KVM_BF16 && p.TG >= 64 && d->head_dim == 128 && loc == KVM_INDEX_DEVICE;
+  size_t off = 0;
+  if (p.mfma) {
+    p.row_chunks = (p.TG + 255) / 256;
+    p.TGp = p.row_chunks * 256;
+    // enough workgroups to fill 256 CUs several times over
+    int32_t ns = 1;
+    while ((int64_t)nlg * p.row_chunks * ns < 2048 && (int64_t)ns * 64 * 2 <= N) ns *= 2;
+    p.nsplit = ns;
+    p.split_blocks = (int32_t)(((N + ns - 1) / ns + 63) / 64 * 64);
+    p.block_chunks = (int32_t)((N + 255) / 256);
+    p.off_part = off;
+    off = align256(off + (size_t)nlg * ns * p.TGp * sizeof(float2));
+    p.off_lse = off;
+    off = align256(off + (size_t)nlg * p.TGp * sizeof(float));
+    p.off_rp = off;
+    off = align256(off + (size_t)nlg * N * sizeof(float));
+  } else {
+    p.chunks = (int32_t)((N + 255) / 256);
+    p.off_S = off;
+    off = align256(off + (size_t)nlg * N * p.TG * sizeof(float));
+    p.off_part = off;
+    off = align256(off + (size_t)nlg * p.chunks * p.TG * sizeof(float2));
+    p.off_lse = off;
+    off = align256(off + (size_t)nlg * p.TG * sizeof(float));
+    if (loc == KVM_INDEX_HOST_TILED) {
+      p.off_stage = off;
+      off = align256(off + 2 * (size_t)nlg * tile_blocks * d->head_dim * dtype_bytes(dtype));
+    }
+  }
+  p.bytes = off;
+  return p;
+}
+
+// Cached per-thread side stream and events for the host-tiled form.
+struct TiledRes {
+  hipStream_t side = nullptr;
+  hipEvent_t h2d[2] = {nullptr, nullptr};
+  hipEvent_t used[2] = {nullptr, nullptr};
+  int device = -1;
+};
+static thread_local TiledRes g_tiled;
+
+static int tiled_res(TiledRes** out) {
+  int dev;
+  KVM_HIP(hipGetDevice(&dev));
+  TiledRes& r = g_tiled;
+  if (r.device != dev) {
+    KVM_HIP(hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking));
+    for (int i = 0; i < 2; ++i) {
+      KVM_HIP(hipEventCreateWithFlags(&r.h2d[i], hipEventDisableTiming));
+      KVM_HIP(hipEventCreateWithFlags(&r.used[i], hipEventDisableTiming));
+    }
+    r.device = dev;
+  }
+  *out = &r;
+  return KVM_OK;
+}
+
+template <typename T, int D>
+static void launch_stored_pass1(const StoredArgs& a, hipStream_t s) {
+  const int32_t chunks_here = (a.nb + 255) / 256;
+  const size_t shm = ((size_t)a.TG * D + 8) * sizeof(float);
+  score_stored_pass1<T, D><<<dim3((uint32_t)((int64_t)a.nlg * chunks_here)), dim3(256), shm, s>>>(a);
+}
+
+static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStream_t s) {
+  if (dtype == KVM_BF16) {
+    if (D == 128) launch_stored_pass1<uint16_t, 128>(a, s);
+    else launch_stored_pass1<uint16_t, 64>(a, s);
+  } else {
+    if (D == 128) launch_stored_pass1<float, 128>(a, s);
+    else launch_stored_pass1<float, 64>(a, s);
+  }
+}
+
+}  // namespace kvm
+
+extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
+                                     int64_t n_blocks, int32_t index_loc, int64_t tile_blocks) {
+  using namespace kvm;
+  if (check_dims(dims, dtype) || n_q_tokens < 1 || n_blocks < 1) return 0;
+  return make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks).bytes;
+}
+
+extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q,
+                                int32_t n_q_tokens, const void* index, int64_t index_cap_blocks,
+                                int64_t n_blocks, int32_t index_loc, int64_t tile_blocks,
+                                float* scores, void* ws, size_t ws_bytes, void* stream) {
+  using namespace kvm;
+  clear_error();
+  int rc = check_dims(dims, dtype);
+  if (rc) return rc;
+  KVM_CHECK_ARG(q && index && scores, "null pointer");
+  KVM_CHECK_ARG(n_q_tokens >= 1 && n_blocks >= 1 && n_blocks < (1LL << 30),
+                "n_q_tokens / n_blocks out of range");
+  KVM_CHECK_ARG(index_loc == KVM_INDEX_DEVICE || index_loc == KVM_INDEX_HOST_TILED,
+                "index_loc");
+  const int32_t D = dims->head_dim;
+  const int32_t G = dims->n_q_heads / dims->n_kv_heads;
+  const int32_t nlg = dims->n_layers * dims->n_kv_heads;
+  const int32_t TG = n_q_tokens * G;
+  if (index_loc == KVM_INDEX_DEVICE)
+    KVM_CHECK_ARG(n_blocks <= index_cap_blocks, "n_blocks > index_cap_blocks");
+  if (index_loc == KVM_INDEX_HOST_TILED) {
+    KVM_CHECK_ARG(tile_blocks >= 256 && tile_blocks % 256 == 0,
+                  "tile_blocks must be a positive multiple of 256");
+  }
+  const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
+  if (!p.mfma) {
+    const size_t shm = ((size_t)TG * D + 8) * sizeof(float);
+    const size_t shm2 = (size_t)nlg * TG * sizeof(float);
+    if (shm > 64 * 1024 || shm2 > 64 * 1024) {
+      set_error("T*G = %d (L*Hkv = %d) too large for the stored-score path", TG, nlg);
+      return KVM_ENOTSUP;
+    }
+  }
+  if (ws_bytes < p.bytes || !ws) {
+    set_error("workspace %zu < %zu bytes", ws_bytes, p.bytes);
+    return KVM_ENOMEM;
+  }
+  KVM_CHECK_ARG(((uintptr_t)q | (uintptr_t)index | (uintptr_t)ws) % 16 == 0,
+                "q, index and ws must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  char* w = reinterpret_cast<char*>(ws);
+  const float scale = LOG2E / sqrtf((float)D);
+  const double inv_lh = 1.0 / ((double)dims->n_layers * dims->n_q_heads);
+  if (p.mfma) {
+    Pass1Args a1{};
+    a1.q = reinterpret_cast<const uint16_t*>(q);
+    a1.index = reinterpret_cast<const uint16_t*>(index);
+    a1.cap = index_cap_blocks;
+    a1.n_blocks = (int32_t)n_blocks;
+    a1.T = n_q_tokens;
+    a1.Hq = dims->n_q_heads;
+    a1.Hkv = dims->n_kv_heads;
+    a1.G = G;
+    a1.TG = TG;
+    a1.row_chunks = p.row_chunks;
+    a1.nsplit = p.nsplit;
+    a1.split_blocks = p.split_blocks;
+    a1.scale = scale;
+    a1.part = reinterpret_cast<float2*>(w + p.off_part);
+    a1.TGp = p.TGp;
+    a1.nlg = nlg;
+    const int64_t wg1 = (int64_t)nlg * p.row_chunks * p.nsplit;
+    a1.total_wg = (uint32_t)((wg1 + 7) / 8 * 8);
+    score_pass1_mfma<128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
+    KVM_HIP(hipGetLastError());
+    const int64_t nl = (int64_t)nlg * p.TGp;
+    score_lse_combine<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
+        a1.part, nlg, p.nsplit, p.TGp, TG, reinterpret_cast<float*>(w + p.off_lse));
+    KVM_HIP(hipGetLastError());
+    Pass2Args a2{};
+    a2.q = a1.q;
+    a2.index = a1.index;
+    a2.cap = index_cap_blocks;
+    a2.n_blocks = (int32_t)n_blocks;
+    a2.T = n_q_tokens;
+    a2.Hq = dims->n_q_heads;
+    a2.Hkv = dims->n_kv_heads;
+    a2.G = G;
+    a2.TG = TG;
+    a2.TGp = p.TGp;
+    a2.block_chunks = p.block_chunks;
+    a2.scale = scale;
+    a2.lse = reinterpret_cast<const float*>(w + p.off_lse);
+    a2.rp = reinterpret_cast<float*>(w + p.off_rp);
+    a2.nlg = nlg;
+    const int64_t wg2 = (int64_t)nlg * p.block_chunks;
+    a2.total_wg = (uint32_t)((wg2 + 7) / 8 * 8);
+    score_pass2_mfma<128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
+    KVM_HIP(hipGetLastError());
+    score_reduce<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), 0, s>>>(
+        a2.rp, nlg, (int32_t)n_blocks, inv_lh, scores);
+    KVM_HIP(hipGetLastError());
+    return KVM_OK;
+  }
+  // Stored-score path.
+  StoredArgs a{};
+  a.q = q;
+  a.n_blocks = (int32_t)n_blocks;
+  a.T = n_q_tokens;
+  a.Hq = dims->n_q_heads;
+  a.Hkv = dims->n_kv_heads;
+  a.G = G;
+  a.TG = TG;
+  a.nlg = nlg;
+  a.chunks_total = p.chunks;
+  a.scale = scale;
+  a.S = reinterpret_cast<float*>(w + p.off_S);
+  a.part = reinterpret_cast<float2*>(w + p.off_part);
+  if (index_loc == KVM_INDEX_DEVICE) {
+    a.index = index;
+    a.lg_stride = index_cap_blocks * D;
+    a.b_first = 0;
+    a.nb = (int32_t)n_blocks;
+    stored_pass1(dtype, D, a, s);
+    KVM_HIP(hipGetLastError());
+  } else {
+    TiledRes* tr;
+    rc = tiled_res(&tr);
+    if (rc) return rc;
+    const int64_t ntile = (n_blocks + tile_blocks - 1) / tile_blocks;
+    const size_t tile_bytes = (size_t)nlg * tile_blocks * D * dtype_bytes(dtype);
+    char* stage[2] = {w + p.off_stage, w + p.off_stage + tile_bytes};
+    // The side stream starts after the caller's earlier work.
+    KVM_HIP(hipEventRecord(tr->used[0], s));
+    KVM_HIP(hipStreamWaitEvent(tr->side, tr->used[0], 0));
+    KVM_HIP(hipEventRecord(tr->used[1], s));
+    for (int64_t t = 0; t < ntile; ++t) {
+      const int bi = (int)(t & 1);
+      // staging buffer bi is free once the kernel that read it (tile t-2) ran
+      KVM_HIP(hipStreamWaitEvent(tr->side, tr->used[bi], 0));
+      KVM_HIP(hipMemcpyAsync(stage[bi], (const char*)index + (size_t)t * tile_bytes, tile_bytes,
+                             hipMemcpyHostToDevice, tr->side));
+      KVM_HIP(hipEventRecord(tr->h2d[bi], tr->side));
+      KVM_HIP(hipStreamWaitEvent(s, tr->h2d[bi], 0));
+      a.index = stage[bi];
+      a.lg_stride = tile_blocks * D;
+      a.b_first = (int32_t)(t * tile_blocks);
+      a.nb = (int32_t)std::min<int64_t>(tile_blocks, n_blocks - t * tile_blocks);
+      stored_pass1(dtype, D, a, s);
+      KVM_HIP(hipGetLastError());
+      KVM_HIP(hipEventRecord(tr->used[bi], s));
+    }
+  }
+  const int64_t nl = (int64_t)nlg * TG;
+  score_stored_lse<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
+      a.part, nlg, p.chunks, TG, reinterpret_cast<float*>(w + p.off_lse));
+  KVM_HIP(hipGetLastError());
+  const size_t shm2 = (size_t)nlg * TG * sizeof(float);
+  score_stored_pass2<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), shm2, s>>>(
+      a.S, reinterpret_cast<const float*>(w + p.off_lse), nlg, TG, (int32_t)n_blocks, inv_lh,
+      scores);
+  KVM_HIP(hipGetLastError());
+  return KVM_OK;
+}

@@ -1,0 +1,239 @@
+/*
+ * kvm.h - C ABI of libkvm: the per-step working-set update of attention-space
+ * block retrieval (KVMem, "Virtualizing Million-Token Agent Workspaces on a
+ * Consumer GPU"), for AMD Instinct MI355X (gfx950).
+ *
+ * Four calls make one agent step (KVMem Sec. 4.2: one update after prefill,
+ * before decode):
+ *   kvm_build_index    Mean-K index rows of completed blocks       (Sec. 4.3, Sec. 5)
+ *   kvm_score_blocks   block relevance R_b, Eq. (10)                (Sec. 4.3, Sec. 5)
+ *   kvm_select         sink + recent + top-k, chronological order    (Sec. 4.3)
+ *   kvm_rematerialize  delta plan, H2D of misses, re-RoPE K, copy V  (Sec. 4.4, Fig. 3)
+ *
+ * Conventions shared by every entry point
+ *  - Plain pointers and sizes only. "device" pointers are HIP device memory of
+ *    the current device; "pinned host" pointers come from hipHostMalloc (or an
+ *    equivalent page-locked allocation).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    device work is enqueued on it; calls return once the work is enqueued.
+ *    No entry point synchronises the device; only kvm_rematerialize waits for
+ *    `stream` (to read the selection) and kvm_ctx_sync waits for ctx work.
+ *  - The caller owns every buffer it passes (inputs, outputs, workspaces,
+ *    pools). The library never frees caller memory and allocates device memory
+ *    only inside kvm_ctx_create.
+ *  - Return value: KVM_OK or a negative kvm_status. Argument validation is
+ *    synchronous and leaves outputs untouched. HIP errors return KVM_EHIP;
+ *    the text is in kvm_last_error() (thread-local). No C++ exception crosses
+ *    this interface.
+ *  - Element types: KVM_F32 (IEEE binary32) or KVM_BF16 (bfloat16 bit
+ *    patterns). Supported head_dim: 64 and 128; block_tokens: 32.
+ */
+#ifndef KVM_H
+#define KVM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVM_OK = 0,
+  KVM_EINVAL = -1,  /* bad shape, pointer, alignment or enum value */
+  KVM_ENOMEM = -2,  /* workspace, pool or record capacity too small */
+  KVM_EHIP = -3,    /* a HIP runtime call failed; see kvm_last_error() */
+  KVM_ERANGE = -4,  /* budget < sink + recent, block id out of range, block
+                       without a source, NaN or negative score */
+  KVM_ENOTSUP = -5  /* valid but unsupported combination (dtype, head_dim) */
+} kvm_status;
+
+typedef enum { KVM_F32 = 0, KVM_BF16 = 1 } kvm_dtype;
+
+/* Where kvm_score_blocks finds the index. */
+typedef enum { KVM_INDEX_DEVICE = 0, KVM_INDEX_HOST_TILED = 1 } kvm_index_loc;
+
+/* Where a block's lower-tier raw K/V copy lives (KVMem Sec. 5 block records). */
+typedef enum { KVM_SRC_NONE = 0, KVM_SRC_HOST_PINNED = 1, KVM_SRC_DEVICE = 2 } kvm_src_loc;
+
+typedef struct {
+  int32_t n_layers;     /* L: scored attention layers */
+  int32_t n_kv_heads;   /* Hkv */
+  int32_t n_q_heads;    /* Hq, a multiple of Hkv; query head h uses KV head h / (Hq/Hkv) */
+  int32_t head_dim;     /* d */
+  int32_t block_tokens; /* B: tokens per logical block (32) */
+} kvm_dims;
+
+/* Version of this interface (major*100 + minor). */
+int kvm_version(void);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* kvm_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Mean-K index build / append.
+ * KVMem Sec. 4.3: a block is represented, per layer and KV head, by the mean of
+ * its position-independent (pre-RoPE) K vectors; Sec. 5: each completed block
+ * is indexed while its K is still on the GPU, so appending is the same call.
+ *
+ * k_raw   device, block-major raw K: block i at (char*)k_raw + i*k_block_stride,
+ *         each block [L][Hkv][B][d] contiguous in `dtype`.
+ * index   device, [L][Hkv][index_cap_blocks][d] in `dtype`; the call writes rows
+ *         [first_block, first_block + n_blocks) of every (l, g) and nothing else.
+ * Result: index[l][g][first_block+i][t] = round(mean_j k_raw[i][l][g][j][t]),
+ *         the sum formed exactly (float64) and rounded once to nearest-even, so
+ *         the stored mean is the correctly rounded block mean.
+ * Errors: KVM_EINVAL (null pointer, n_blocks < 0, stride smaller than a block,
+ *         first_block + n_blocks > index_cap_blocks), KVM_ENOTSUP (head_dim,
+ *         block_tokens). n_blocks == 0 is a no-op. */
+int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
+                    int64_t k_block_stride, int64_t first_block, int64_t n_blocks,
+                    void* index, int64_t index_cap_blocks, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Block relevance, KVMem Sec. 4.3 Eq. (10) (tiled form: Sec. 5):
+ *   R_b = 1/(L*Hq) * sum_l sum_h sum_m softmax_b( q[l][h][m] . kbar[l][g(h)][b] / sqrt(d) )
+ * with the softmax over all n_blocks indexed blocks for each fixed (l, m, h)
+ * and g(h) = h / (Hq/Hkv). sum_b R_b = n_q_tokens.
+ *
+ * q       device, pre-RoPE queries [L][Hq][n_q_tokens][d] in `dtype`.
+ * index   KVM_INDEX_DEVICE: device [L][Hkv][index_cap_blocks][d];
+ *         KVM_INDEX_HOST_TILED: pinned host, tile-major: tile t (blocks
+ *         [t*tile_blocks, (t+1)*tile_blocks)) is [L][Hkv][tile_blocks][d] at
+ *         element offset t*L*Hkv*tile_blocks*d (the last tile is full-sized,
+ *         rows past n_blocks are ignored). Tiles are streamed through two device
+ *         staging buffers in `ws`; the softmax normalisation is global, so the
+ *         result equals the resident form.
+ * scores  device float[n_blocks] (R_b).
+ * ws      device workspace of at least kvm_score_ws_bytes(...) bytes.
+ * Errors: KVM_EINVAL (shapes, null pointers, n_blocks < 1, n_q_tokens < 1),
+ *         KVM_ENOMEM (ws_bytes too small), KVM_ENOTSUP (dtype/head_dim). */
+size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
+                          int64_t n_blocks, int32_t index_loc, int64_t tile_blocks);
+
+int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q, int32_t n_q_tokens,
+                     const void* index, int64_t index_cap_blocks, int64_t n_blocks,
+                     int32_t index_loc, int64_t tile_blocks, float* scores, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Default selector and compact positions, KVMem Sec. 4.3 (sink and recent
+ * regions always kept, the rest of the budget to the largest R_b, then
+ * chronological order) and Sec. 4.4 / Sec. 5 (contiguous compact positions).
+ *
+ * scores    device float[n_blocks], finite and >= 0.
+ * sel       device int32[budget_blocks]: ascending block ids; the first *n_sel
+ *           entries are valid.
+ * n_sel     device int32[1]: min(n_blocks, budget_blocks), or KVM_ERANGE (-4)
+ *           if a score is NaN or negative (detected on the device; sel is then
+ *           unspecified and kvm_rematerialize reports KVM_ERANGE).
+ * base_pos  device int32[budget_blocks]: base_pos[i] = i * block_tokens.
+ * Selection: blocks [0, n_sink) and [n_blocks - n_recent, n_blocks) always;
+ *           k = budget - n_sink - n_recent more from the rest by descending
+ *           score, exact ties to the lower block id; every block when
+ *           n_blocks <= budget_blocks.
+ * ws        device workspace of at least kvm_select_ws_bytes(n_blocks) bytes.
+ * Errors: KVM_ERANGE (n_sink + n_recent > budget_blocks), KVM_EINVAL, KVM_ENOMEM. */
+size_t kvm_select_ws_bytes(int64_t n_blocks);
+
+int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
+               int32_t budget_blocks, int32_t block_tokens, int32_t* sel, int32_t* n_sel,
+               int32_t* base_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Working-set context: block records, the bounded GPU page pool and the
+ * rematerialization data plane (KVMem Sec. 4.4, Sec. 5, Fig. 3).
+ *
+ * Pool (caller-owned device memory, n_slots pages each [L][Hkv][B][d] in dtype):
+ *   k_view    K encoded at the block's current compact position (what attention reads)
+ *   v_view    V, a verbatim copy of the block's raw V
+ *   k_shadow  the block's raw pre-RoPE K (the reconstruction source for hits
+ *             whose compact position changes)
+ * The ctx owns only host-side state, a side stream, events, a pinned staging
+ * ring, a small device job list and the RoPE cos/sin table (fp64 angles,
+ * rounded to fp32; positions [0, max_pos)). */
+typedef struct {
+  kvm_dims dims;
+  int32_t dtype;
+  int32_t rope_layout;    /* 0: pairs (2t, 2t+1); 1: pairs (t, t + d/2) */
+  double rope_theta;      /* base of theta_t = base^(-2t/d), e.g. 10000 */
+  int32_t max_pos;        /* compact positions must stay below this */
+  int32_t n_slots;        /* pool pages */
+  void* k_view;
+  void* v_view;
+  void* k_shadow;
+  int64_t max_blocks;     /* block-record capacity (block ids < max_blocks) */
+  int32_t batch_blocks;   /* misses per H2D batch / event (default 64 if <= 0) */
+  int32_t staging_blocks; /* pinned ring capacity in blocks for gathered sources (>= 2*batch) */
+} kvm_ctx_desc;
+
+typedef struct kvm_ctx kvm_ctx;
+
+typedef struct {
+  int32_t n_sel;        /* blocks in the new execution view */
+  int32_t hits;         /* selected blocks already resident in the pool */
+  int32_t misses;       /* selected blocks staged in this call */
+  int32_t rotated;      /* blocks whose K was (re)encoded this call */
+  int32_t evicted;      /* resident blocks whose page was reclaimed */
+  int32_t batches;      /* H2D batches (events) issued */
+  int64_t h2d_bytes;    /* bytes copied host -> device */
+  int64_t d2d_bytes;    /* bytes read + written by the remat kernels */
+} kvm_remat_stats;
+
+/* Host-gather callback for lower tiers that are not pinned (pageable or
+ * procedural stores): write block `block`'s raw K (which=0) or V (which=1),
+ * [L][Hkv][B][d] in dtype, to `dst` (pinned). Return 0 on success. Called from
+ * library worker threads, possibly concurrently for different blocks. */
+typedef int (*kvm_gather_fn)(void* user, int64_t block, int32_t which, void* dst);
+
+int kvm_ctx_create(const kvm_ctx_desc* desc, kvm_ctx** out);
+void kvm_ctx_destroy(kvm_ctx* ctx);
+
+/* Record the lower-tier copy of blocks [first_block, first_block + n_blocks):
+ * block first_block+i has raw K at (char*)k_base + i*block_stride and raw V at
+ * (char*)v_base + i*block_stride, in pinned host memory (KVM_SRC_HOST_PINNED,
+ * staged by DMA straight into the destination page) or device memory
+ * (KVM_SRC_DEVICE, read by the remat kernel directly). */
+int kvm_ctx_set_source(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks, const void* k_base,
+                       const void* v_base, int64_t block_stride, int32_t loc);
+
+/* Record blocks [first_block, first_block + n_blocks) as served by a host
+ * gather callback (packed through the pinned staging ring, KVMem Sec. 4.4). */
+int kvm_ctx_set_gather(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks, kvm_gather_fn fn,
+                       void* user);
+
+/* Register freshly prefilled blocks as GPU-resident (KVMem Sec. 5: new blocks
+ * start in their original frame; here their K page is marked stale so the next
+ * selection encodes it). Copies raw K and V (device, block stride as above)
+ * into free pool pages on `stream`. KVM_ENOMEM if no free page remains. */
+int kvm_ctx_register_resident(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks,
+                              const void* k_raw, const void* v_raw, int64_t block_stride,
+                              void* stream);
+
+/* Make the execution view for a selection (KVMem Sec. 4.4, Sec. 5, Fig. 3):
+ * reads n_sel/sel from the device (one small copy, then waits for `stream`),
+ * plans hits / misses / evictions against the pool, stages misses H2D on the
+ * side stream in event-tracked batches, and enqueues on `stream` the kernels
+ * that write k_view = RoPE(raw K, compact position) for misses and for hits
+ * whose position changed, and v_view = raw V for misses. page_table_dev
+ * (device int32[n_sel]) receives the pool page of sel[i]. Selected block i
+ * occupies positions [i*B, i*B + B). Returns once everything is enqueued;
+ * later work on `stream` sees the finished view. stats_host may be NULL.
+ * Errors: KVM_ERANGE (selection invalid or a miss without a source; n_sel
+ * reported as KVM_ERANGE by kvm_select), KVM_ENOMEM (pool smaller than the
+ * view), KVM_EHIP. */
+int kvm_rematerialize(kvm_ctx* ctx, const int32_t* sel_dev, const int32_t* n_sel_dev,
+                      int32_t* page_table_dev, kvm_remat_stats* stats_host, void* stream);
+
+/* Wait for the ctx's side-stream work (H2D batches). */
+int kvm_ctx_sync(kvm_ctx* ctx);
+
+/* Inspection: pool page of `block` (or -1) and its baked compact position
+ * (-1 = K page stale). */
+int kvm_ctx_block_state(kvm_ctx* ctx, int64_t block, int32_t* slot, int32_t* baked_pos);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVM_H */

@@ -1,0 +1,121 @@
+"""Helpers shared by the GPU tests: run the library on a seeded workspace.
+
+Inputs come from ``synth``; every computed value comes from the HIP library
+through its C ABI (``attention_space_block_amd``); expected values come from
+``oracle``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+
+
+def torch_dtype(wl):
+    import torch
+    return torch.float32 if wl.dtype == "f32" else torch.int16
+
+
+def to_dev(a: np.ndarray, dev):
+    import torch
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_host_bits(t) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def raw_to_device(wl, which: str, b0: int, nb: int, dev, chunk: int = 256):
+    """Raw K or V of blocks [b0, b0+nb) as one device tensor [nb][block_elems]."""
+    import torch
+    out = torch.empty((nb, wl.block_elems), dtype=torch_dtype(wl), device=dev)
+    for s in range(0, nb, chunk):
+        n = min(chunk, nb - s)
+        h = synth.kv_blocks(wl, which, b0 + s, n).reshape(n, -1)
+        out[s:s + n].copy_(to_dev(h, "cpu"))
+    return out
+
+
+def build_index_dev(k, wl, raw_k, dev, cap: int | None = None, first: int = 0):
+    import torch
+    N = raw_k.shape[0]
+    cap = cap or N
+    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim), dtype=torch_dtype(wl),
+                        device=dev)
+    k.kvm_build_index(k.dims_for(wl), k.dtype_code(wl.dtype), raw_k, wl.block_bytes, first, N,
+                      index, cap)
+    return index
+
+
+def score_dev(k, wl, q_dev, index, n_blocks: int, cap: int, dev, loc: int = 0,
+              tile_blocks: int = 0, host_index=None):
+    import torch
+    dims = k.dims_for(wl)
+    dt = k.dtype_code(wl.dtype)
+    T = q_dev.shape[2]
+    ws_b = k.kvm_score_ws_bytes(dims, dt, T, n_blocks, loc, tile_blocks)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    scores = torch.empty(n_blocks, dtype=torch.float32, device=dev)
+    src = index if loc == 0 else host_index
+    k.kvm_score_blocks(dims, dt, q_dev, T, src, cap, n_blocks, loc, tile_blocks, scores, ws, ws_b)
+    return scores
+
+
+def select_dev(k, scores, n_blocks: int, n_sink: int, n_recent: int, budget: int, dev, B: int = 32):
+    import torch
+    sel = torch.full((budget,), -7, dtype=torch.int32, device=dev)
+    n_sel = torch.zeros(1, dtype=torch.int32, device=dev)
+    base = torch.full((budget,), -7, dtype=torch.int32, device=dev)
+    k.kvm_select(scores, n_blocks, n_sink, n_recent, budget, B, sel, n_sel, base)
+    return sel, n_sel, base
+
+
+class Pool:
+    """A page pool plus its context."""
+
+    def __init__(self, k, wl, n_slots: int, max_blocks: int, max_pos: int, dev,
+                 batch_blocks: int = 64, staging_blocks: int = 0):
+        import torch
+        dt = torch_dtype(wl)
+        self.k_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        self.v_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        self.k_shadow = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        self.ctx = k.KvmCtx(k.dims_for(wl), k.dtype_code(wl.dtype), self.k_view, self.v_view,
+                            self.k_shadow, n_slots, max_blocks, max_pos, wl.theta,
+                            wl.rope_layout, batch_blocks, staging_blocks)
+        self.page = torch.full((n_slots,), -1, dtype=torch.int32, device=dev)
+
+
+def check_view(wl, sel: np.ndarray, page: np.ndarray, pool: Pool, blocks=None, atol=None):
+    """Compare the K and V pages of selected blocks with the oracle.
+
+    K: |K_gpu - RoPE(raw K)| within 2e-2 (bf16) or 1e-5*max(1,|K|) (fp32),
+    against the unrounded float64 oracle; V: bit-exact."""
+    from oracle.pipeline import expected_view_k, expected_view_v_bits
+    B = wl.block_tokens
+    idx = range(len(sel)) if blocks is None else blocks
+    worst = 0.0
+    for i in idx:
+        b = int(sel[i])
+        slot = int(page[i])
+        want = expected_view_k(wl, b, B * i)
+        got = as_f64(to_host_bits(pool.k_view[slot])).reshape(want.shape)
+        err = np.abs(got - want)
+        if wl.dtype == "bf16":
+            ok = np.all(err <= (atol if atol is not None else 2e-2))
+        else:
+            ok = np.all(err <= 1e-5 * np.maximum(1.0, np.abs(want)))
+        worst = max(worst, float(err.max()))
+        assert ok, f"K of block {b} (view slot {i}) off by {err.max()}"
+        vb = to_host_bits(pool.v_view[slot])
+        assert np.array_equal(vb, expected_view_v_bits(wl, b).ravel()), f"V of block {b}"
+    return worst

@@ -1,0 +1,286 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Tolerances: Mean-K, selections, compact positions, page tables and V are
+bit-exact; scores within 1e-5 relative; re-RoPE'd K within 2e-2 absolute
+(bf16) or 1e-5 relative (fp32) of the unrounded float64 oracle.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import select_blocks, compact_positions
+from oracle import pipeline as op
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def k():
+    import torch
+    import attention_space_block_amd as kvm
+    assert torch.cuda.is_available()
+    kvm._abi.lib()
+    return kvm
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- Mean-K ----
+
+@pytest.mark.parametrize("name,nb,layers", [("tiny", 128, None), ("ctx64k", 300, 2)])
+def test_build_index_bit_exact(k, dev, name, nb, layers):
+    wl = synth.get_workload(name)
+    if layers:
+        wl = wl.scaled(n_layers=layers)
+    say("build_index", name, nb)
+    raw = gc.raw_to_device(wl, "K", 0, nb, dev)
+    idx = gc.build_index_dev(k, wl, raw, dev)
+    want = op.index_rows(wl, 0, nb)
+    got = gc.as_f64(gc.to_host_bits(idx))
+    assert np.array_equal(got, want)
+
+
+def test_build_index_append_and_stride(k, dev):
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    raw = gc.raw_to_device(wl, "K", 0, 100, dev)
+    full = gc.build_index_dev(k, wl, raw, dev, cap=128)
+    part = torch.zeros_like(full)
+    dims, dt = k.dims_for(wl), k.KVM_BF16
+    k.kvm_build_index(dims, dt, raw, wl.block_bytes, 0, 37, part, 128)
+    k.kvm_build_index(dims, dt, raw[37:], wl.block_bytes, 37, 63, part, 128)
+    assert torch.equal(full, part)
+    # strided source: every other block of a doubled buffer
+    dbl = torch.zeros((200, wl.block_elems), dtype=raw.dtype, device=dev)
+    dbl[0::2] = raw
+    st = torch.zeros_like(full)
+    k.kvm_build_index(dims, dt, dbl, 2 * wl.block_bytes, 0, 100, st, 128)
+    assert torch.equal(full, st)
+    assert int(full[:, :, 100:].abs().sum()) == 0     # rows past the range untouched
+
+
+# ---------------------------------------------------------------- scores ----
+
+def _score_case(k, dev, wl, N):
+    index = op.index_rows(wl, 0, N)
+    q = op.query_stored(wl, 0, index)
+    ref = op.block_scores(op.as_f64(q, wl.dtype), index)
+    raw = gc.raw_to_device(wl, "K", 0, N, dev)
+    idx_dev = gc.build_index_dev(k, wl, raw, dev)
+    got = gc.score_dev(k, wl, gc.to_dev(q, dev), idx_dev, N, N, dev).cpu().numpy()
+    return got.astype(np.float64), ref
+
+
+@pytest.mark.parametrize("name,N,scale", [
+    ("tiny", 128, {}),
+    ("ctx64k", 2048, {}),                              # MFMA path, full size
+    ("ctx64k", 1000, {"n_layers": 2, "n_q_tokens": 77}),  # ragged rows and blocks
+    ("ctx64k", 700, {"n_layers": 2, "n_q_tokens": 1}),    # stored path, bf16, d = 128
+    ("ctx64k", 333, {"n_layers": 1, "n_q_tokens": 5}),    # stored path, ragged
+])
+def test_scores_match_oracle(k, dev, name, N, scale):
+    wl = synth.get_workload(name).scaled(**scale) if scale else synth.get_workload(name)
+    say("scores", name, N, scale)
+    got, ref = _score_case(k, dev, wl, N)
+    assert abs(got.sum() - wl.n_q_tokens) <= 1e-5 * wl.n_q_tokens
+    rel = np.abs(got - ref) / ref
+    assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
+
+
+def test_host_tiled_scores_equal_resident(k, dev):
+    import torch
+    wl = synth.get_workload("ws10m").scaled(n_layers=4, n_blocks=1300, tile_blocks=256)
+    N, tb, nlg, d = wl.n_blocks, wl.tile_blocks, wl.n_layers * wl.n_kv_heads, wl.head_dim
+    say("host tiled", N, tb)
+    ntile = (N + tb - 1) // tb
+    index = synth.index_direct(wl, 0, N)                      # [L][Hkv][N][d]
+    host = torch.zeros((ntile, nlg, tb, d), dtype=torch.int16).pin_memory()
+    hv = host.numpy().view(np.uint16)
+    ix = index.reshape(nlg, N, d)
+    for t in range(ntile):
+        n = min(tb, N - t * tb)
+        hv[t, :, :n] = ix[:, t * tb:t * tb + n]
+    q = synth.query(wl)
+    qd = gc.to_dev(q, dev)
+    idx_dev = gc.to_dev(index, dev)
+    res = gc.score_dev(k, wl, qd, idx_dev, N, N, dev).cpu().numpy()
+    til = gc.score_dev(k, wl, qd, None, N, N, dev, loc=1, tile_blocks=tb,
+                       host_index=host).cpu().numpy()
+    assert np.array_equal(res, til)
+    ref = op.block_scores(op.as_f64(q, "bf16"), op.as_f64(index, "bf16"))
+    assert np.max(np.abs(res - ref) / ref) <= 1e-5
+
+
+# ---------------------------------------------------------------- select ----
+
+@pytest.mark.parametrize("N,sink,recent,budget,kind", [
+    (128, 1, 2, 11, "cont"), (2048, 1, 64, 512, "ties"), (32768, 1, 64, 4096, "cont"),
+    (32768, 1, 64, 4096, "ties"), (312500, 1, 256, 2048, "cont"), (5000, 0, 0, 100, "const"),
+    (600, 3, 5, 8, "ties"), (500, 1, 64, 512, "cont"), (512, 1, 64, 512, "ties"), (1, 1, 0, 1, "cont"),
+])
+def test_select_bit_exact(k, dev, N, sink, recent, budget, kind):
+    say("select", N, sink, recent, budget, kind)
+    R = synth.scores_f32(N + budget, N, kind=kind, levels=4)
+    sel, n_sel, base = gc.select_dev(k, gc.to_dev(R, dev), N, sink, recent, budget, dev)
+    want = select_blocks(R, sink, recent, budget)
+    n = int(n_sel.item())
+    assert n == len(want) == min(N, budget)
+    assert np.array_equal(sel.cpu().numpy()[:n], want)
+    assert np.array_equal(base.cpu().numpy()[:n], compact_positions(n))
+
+
+def test_select_error_paths(k, dev):
+    R = synth.scores_f32(9, 1000)
+    for bad in (np.nan, -1.0, np.inf):
+        R2 = R.copy()
+        R2[500] = bad
+        _, n_sel, _ = gc.select_dev(k, gc.to_dev(R2, dev), 1000, 1, 8, 100, dev)
+        assert int(n_sel.item()) == k.api._abi.KVM_ERANGE
+    with pytest.raises(k.KvmError) as e:
+        gc.select_dev(k, gc.to_dev(R, dev), 1000, 60, 60, 100, dev)
+    assert e.value.code == k.api._abi.KVM_ERANGE
+
+
+# ------------------------------------------------------ rematerialization ----
+
+def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0):
+    import torch
+    pool = gc.Pool(k, wl, n_slots, N, wl.budget_blocks * wl.block_tokens, dev, batch, staging)
+    keep = []
+    if src == "device":
+        rk = gc.raw_to_device(wl, "K", 0, N, dev)
+        rv = gc.raw_to_device(wl, "V", 0, N, dev)
+        pool.ctx.kvm_ctx_set_source(0, N, rk, rv, wl.block_bytes, k.KVM_SRC_DEVICE)
+        keep += [rk, rv]
+    elif src == "pinned":
+        rk = torch.empty((N, wl.block_elems), dtype=gc.torch_dtype(wl)).pin_memory()
+        rv = torch.empty((N, wl.block_elems), dtype=gc.torch_dtype(wl)).pin_memory()
+        synth.kv_blocks(wl, "K", 0, N, out=rk.numpy().view(
+            np.float32 if wl.dtype == "f32" else np.uint16))
+        synth.kv_blocks(wl, "V", 0, N, out=rv.numpy().view(
+            np.float32 if wl.dtype == "f32" else np.uint16))
+        pool.ctx.kvm_ctx_set_source(0, N, rk, rv, wl.block_bytes, k.KVM_SRC_HOST_PINNED)
+        keep += [rk, rv]
+    else:
+        import ctypes
+
+        def gather(block, which, dst):
+            buf = (ctypes.c_char * wl.block_bytes).from_address(dst)
+            arr = np.frombuffer(buf, dtype=np.float32 if wl.dtype == "f32" else np.uint16)
+            synth.kv_blocks(wl, "K" if which == 0 else "V", block, 1, out=arr, nthreads=1)
+            return 0
+        pool.ctx.kvm_ctx_set_gather(0, N, gather)
+    return pool, keep
+
+
+@pytest.mark.parametrize("src", ["device", "pinned", "gather"])
+def test_remat_view_matches_oracle(k, dev, src):
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, budget_blocks=96, n_recent=8)
+    N = 400
+    say("remat", src)
+    pool, keep = _remat_setup(k, dev, wl, N, 130, src, batch=16, staging=32)
+    R = synth.scores_f32(21, N)
+    sel, n_sel, base = gc.select_dev(k, gc.to_dev(R, dev), N, wl.n_sink, wl.n_recent,
+                                     wl.budget_blocks, dev)
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    import torch
+    torch.cuda.synchronize()
+    n = int(n_sel.item())
+    s = sel.cpu().numpy()[:n]
+    pg = pool.page.cpu().numpy()[:n]
+    assert st["n_sel"] == n == 96 and st["misses"] == 96 and st["hits"] == 0
+    assert len(set(pg.tolist())) == n and pg.min() >= 0 and pg.max() < 130
+    gc.check_view(wl, s, pg, pool)
+    # next step: a shifted selection; hits keep their pages, positions change
+    R2 = synth.scores_f32(22, N)
+    R2[s[::2]] += 10.0                       # keep about half of the old view
+    sel2, n_sel2, _ = gc.select_dev(k, gc.to_dev(R2, dev), N, wl.n_sink, wl.n_recent,
+                                    wl.budget_blocks, dev)
+    st2 = pool.ctx.kvm_rematerialize(sel2, n_sel2, pool.page)
+    torch.cuda.synchronize()
+    s2 = sel2.cpu().numpy()[:n]
+    pg2 = pool.page.cpu().numpy()[:n]
+    old = dict(zip(s.tolist(), pg.tolist()))
+    hits = [b for b in s2.tolist() if b in old]
+    assert st2["hits"] == len(hits) and st2["misses"] == n - len(hits)
+    for b, p in zip(s2.tolist(), pg2.tolist()):
+        if b in old:
+            assert p == old[b]               # GPU hits reuse their page in place
+    assert len(set(pg2.tolist())) == n
+    gc.check_view(wl, s2, pg2, pool)
+    pool.ctx.close()
+
+
+def test_remat_unchanged_position_is_not_rewritten(k, dev):
+    import torch
+    wl = synth.get_workload("tiny")
+    pool, keep = _remat_setup(k, dev, wl, 128, 16)
+    sel = torch.tensor(list(range(11)), dtype=torch.int32, device=dev)
+    n_sel = torch.tensor([11], dtype=torch.int32, device=dev)
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    st2 = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    assert st["rotated"] == 11 and st2["rotated"] == 0 and st2["hits"] == 11
+    torch.cuda.synchronize()
+    gc.check_view(wl, sel.cpu().numpy(), pool.page.cpu().numpy()[:11], pool)
+
+
+def test_remat_error_paths(k, dev):
+    import torch
+    wl = synth.get_workload("tiny")
+    pool = gc.Pool(k, wl, 8, 128, 11 * 32, dev)
+    sel = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    n_sel = torch.tensor([3], dtype=torch.int32, device=dev)
+    with pytest.raises(k.KvmError) as e:          # no source recorded
+        pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    assert e.value.code == k.api._abi.KVM_ERANGE
+    n_sel.fill_(9)
+    with pytest.raises(k.KvmError) as e:          # view larger than the pool
+        pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    assert e.value.code == k.api._abi.KVM_ENOMEM
+    n_sel.fill_(-4)
+    with pytest.raises(k.KvmError) as e:          # invalid selection from kvm_select
+        pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    assert e.value.code == k.api._abi.KVM_ERANGE
+
+
+# ------------------------------------------------------------ end to end ----
+
+@pytest.mark.parametrize("name", ["tiny", "ctx64k"])
+def test_end_to_end_step(k, dev, name):
+    import torch
+    wl = synth.get_workload(name)
+    N = wl.n_blocks
+    say("end to end", name)
+    ref = op.run_step(wl)
+    raw_k = gc.raw_to_device(wl, "K", 0, N, dev)
+    raw_v = gc.raw_to_device(wl, "V", 0, N, dev)
+    idx = gc.build_index_dev(k, wl, raw_k, dev)
+    assert np.array_equal(gc.as_f64(gc.to_host_bits(idx)), ref["index"])
+    q = gc.to_dev(op.query_stored(wl, 0, ref["index"]), dev)
+    scores = gc.score_dev(k, wl, q, idx, N, N, dev)
+    R = scores.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(R - ref["R"]) / ref["R"]) <= 1e-5
+    sel, n_sel, base = gc.select_dev(k, scores, N, wl.n_sink, wl.n_recent, wl.budget_blocks, dev)
+    n = int(n_sel.item())
+    say("margin", ref["margin"])
+    if ref["margin"] > 1e-5:
+        assert np.array_equal(sel.cpu().numpy()[:n], ref["sel"])
+    assert np.array_equal(base.cpu().numpy()[:n], ref["base_pos"])
+    pool = gc.Pool(k, wl, wl.budget_blocks + 8, N, wl.budget_blocks * wl.block_tokens, dev)
+    pool.ctx.kvm_ctx_set_source(0, N, raw_k, raw_v, wl.block_bytes, k.KVM_SRC_DEVICE)
+    pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy()[:n]
+    pg = pool.page.cpu().numpy()[:n]
+    blocks = range(n) if n <= 64 else sorted(set(np.linspace(0, n - 1, 48).astype(int)))
+    gc.check_view(wl, s, pg, pool, blocks=blocks)
+    pool.ctx.close()
