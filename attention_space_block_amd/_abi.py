@@ -21,7 +21,8 @@ EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
     "kvm_select_ws_bytes", "kvm_select", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
-    "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
+    "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state", "kvm_ctx_evict",
+    "kvm_profile_enable", "kvm_profile_read",
 ]
 
 
@@ -54,6 +55,11 @@ class RematStats(ctypes.Structure):
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 
 GATHER_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
@@ -90,6 +96,10 @@ def lib():
             "kvm_ctx_sync": (ctypes.c_int, [vp]),
             "kvm_ctx_block_state": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32),
                                                    ctypes.POINTER(i32)]),
+            "kvm_ctx_evict": (ctypes.c_int, [vp, i64, i64]),
+            "kvm_profile_enable": (ctypes.c_int, [i32]),
+            "kvm_profile_read": (ctypes.c_int, [ctypes.POINTER(KernelStat), i32,
+                                                ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)

@@ -76,6 +76,19 @@ def kvm_select(scores, n_blocks: int, n_sink: int, n_recent: int, budget_blocks:
     _abi.check(rc, "kvm_select")
 
 
+def kvm_profile_enable(on: bool) -> None:
+    _abi.check(_abi.lib().kvm_profile_enable(1 if on else 0), "kvm_profile_enable")
+
+
+def kvm_profile_read() -> dict:
+    """{kernel name: (launches, total_ms)} since profiling was enabled."""
+    n = ctypes.c_int32()
+    buf = (_abi.KernelStat * 64)()
+    _abi.check(_abi.lib().kvm_profile_read(buf, 64, ctypes.byref(n)), "kvm_profile_read")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n.value, 64))}
+
+
 class KvmCtx:
     """Owner of one kvm_ctx (block records, side stream, staging, RoPE table)."""
 
@@ -136,6 +149,9 @@ class KvmCtx:
                                           ctypes.byref(st), _stream(stream))
         _abi.check(rc, "kvm_rematerialize")
         return st.as_dict()
+
+    def kvm_ctx_evict(self, first_block: int, n_blocks: int) -> None:
+        _abi.check(_abi.lib().kvm_ctx_evict(self._h, first_block, n_blocks), "kvm_ctx_evict")
 
     def kvm_ctx_sync(self) -> None:
         _abi.check(_abi.lib().kvm_ctx_sync(self._h), "kvm_ctx_sync")

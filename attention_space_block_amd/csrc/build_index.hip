@@ -9,6 +9,7 @@
 // rounded once to the index dtype, so it is the correctly rounded block mean.
 // HBM-bound: per (block, l, g) it reads B*d*e bytes and writes d*e bytes.
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace kvm {
 
@@ -97,6 +98,7 @@ static void launch_build(const void* k_raw, int64_t stride, int64_t n, int32_t n
                          int64_t cap, void* index, hipStream_t s) {
   const int64_t rows = n * nlg;
   const int64_t grid = (rows + 3) / 4;
+  KernelTimer tm("build_index", s);
   build_index_kernel<T, D><<<dim3((uint32_t)grid), dim3(256), 0, s>>>(
       reinterpret_cast<const char*>(k_raw), stride, n, nlg, first, cap,
       reinterpret_cast<T*>(index));

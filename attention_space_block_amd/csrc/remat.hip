@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace kvm {
 
@@ -163,6 +164,7 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, const RematAr
   const int64_t grid = std::min<int64_t>(units, 256 * 32);
   if (grid <= 0) return;
   dim3 g((uint32_t)grid), b(256);
+  KernelTimer tm("remat", s);
 #define KVM_REMAT(T, D, LAY) remat_kernel<T, D, LAY><<<g, b, 0, s>>>(a)
   if (dtype == KVM_BF16) {
     if (d == 128) { if (layout == 0) KVM_REMAT(uint16_t, 128, 0); else KVM_REMAT(uint16_t, 128, 1); }
@@ -503,6 +505,23 @@ extern "C" int kvm_ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_
     KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)sl * c->page_bytes,
                            (const char*)v_raw + i * block_stride, c->page_bytes,
                            hipMemcpyDeviceToDevice, s));
+  }
+  return KVM_OK;
+}
+
+extern "C" int kvm_ctx_evict(kvm_ctx* c, int64_t first_block, int64_t n_blocks) {
+  using namespace kvm;
+  clear_error();
+  KVM_CHECK_ARG(c, "ctx is NULL");
+  KVM_CHECK_ARG(first_block >= 0 && n_blocks >= 0 && first_block + n_blocks <= c->d.max_blocks,
+                "block range outside the record capacity");
+  for (int64_t b = first_block; b < first_block + n_blocks; ++b) {
+    BlockRec& r = c->rec[b];
+    if (r.slot < 0) continue;
+    c->slot_block[r.slot] = -1;
+    c->free_slots.push_back(r.slot);
+    r.slot = -1;
+    r.baked = -1;
   }
   return KVM_OK;
 }

@@ -33,6 +33,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace kvm {
 
@@ -609,6 +610,7 @@ template <typename T, int D>
 static void launch_stored_pass1(const StoredArgs& a, hipStream_t s) {
   const int32_t chunks_here = (a.nb + 255) / 256;
   const size_t shm = ((size_t)a.TG * D + 8) * sizeof(float);
+  KernelTimer tm("score_stored_pass1", s);
   score_stored_pass1<T, D><<<dim3((uint32_t)((int64_t)a.nlg * chunks_here)), dim3(256), shm, s>>>(a);
 }
 
@@ -693,11 +695,13 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     a1.nlg = nlg;
     const int64_t wg1 = (int64_t)nlg * p.row_chunks * p.nsplit;
     a1.total_wg = (uint32_t)((wg1 + 7) / 8 * 8);
-    score_pass1_mfma<128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
+    { KernelTimer tm("score_pass1_mfma", s);
+    score_pass1_mfma<128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1); }
     KVM_HIP(hipGetLastError());
     const int64_t nl = (int64_t)nlg * p.TGp;
+    { KernelTimer tm("score_lse_combine", s);
     score_lse_combine<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
-        a1.part, nlg, p.nsplit, p.TGp, TG, reinterpret_cast<float*>(w + p.off_lse));
+        a1.part, nlg, p.nsplit, p.TGp, TG, reinterpret_cast<float*>(w + p.off_lse)); }
     KVM_HIP(hipGetLastError());
     Pass2Args a2{};
     a2.q = a1.q;
@@ -717,10 +721,12 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     a2.nlg = nlg;
     const int64_t wg2 = (int64_t)nlg * p.block_chunks;
     a2.total_wg = (uint32_t)((wg2 + 7) / 8 * 8);
-    score_pass2_mfma<128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
+    { KernelTimer tm("score_pass2_mfma", s);
+    score_pass2_mfma<128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
     KVM_HIP(hipGetLastError());
+    { KernelTimer tm("score_reduce", s);
     score_reduce<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), 0, s>>>(
-        a2.rp, nlg, (int32_t)n_blocks, inv_lh, scores);
+        a2.rp, nlg, (int32_t)n_blocks, inv_lh, scores); }
     KVM_HIP(hipGetLastError());
     return KVM_OK;
   }
@@ -774,13 +780,15 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     }
   }
   const int64_t nl = (int64_t)nlg * TG;
+  { KernelTimer tm("score_stored_lse", s);
   score_stored_lse<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
-      a.part, nlg, p.chunks, TG, reinterpret_cast<float*>(w + p.off_lse));
+      a.part, nlg, p.chunks, TG, reinterpret_cast<float*>(w + p.off_lse)); }
   KVM_HIP(hipGetLastError());
   const size_t shm2 = (size_t)nlg * TG * sizeof(float);
+  { KernelTimer tm("score_stored_pass2", s);
   score_stored_pass2<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), shm2, s>>>(
       a.S, reinterpret_cast<const float*>(w + p.off_lse), nlg, TG, (int32_t)n_blocks, inv_lh,
-      scores);
+      scores); }
   KVM_HIP(hipGetLastError());
   return KVM_OK;
 }

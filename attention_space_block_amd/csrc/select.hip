@@ -18,6 +18,7 @@
 //     its tie rank and its output offset, so ties go to the lowest ids and the
 //     output is ascending without a sort.
 #include "common.hpp"
+#include "profile.hpp"
 
 namespace kvm {
 
@@ -184,6 +185,7 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     return KVM_ERANGE;
   }
   KVM_CHECK_ARG((int64_t)budget_blocks * block_tokens < 0x7fffffffLL, "positions overflow int32");
+  KernelTimer tm("select", as_stream(stream));
   select_kernel<<<1, 1024, 0, as_stream(stream)>>>(scores, n_blocks, n_sink, n_recent,
                                                    budget_blocks, block_tokens, sel, n_sel,
                                                    base_pos);

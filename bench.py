@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""One working-set update step on a seeded 1M-token workspace, on one MI355X.
+
+Workspace: 32768 blocks of 32 tokens, 64 layers, 8 KV heads, 48 query heads,
+head dim 128, bf16; 512 query tokens; budget 4096 blocks (sink 1, recent 64);
+half of the selected blocks already resident in the page pool (prefilled,
+K page stale), the other half staged from their lower-tier copy.
+
+A timed step is the whole hot path: Mean-K append of the step's 16 freshly
+prefilled blocks, scoring of all 32768 blocks (Eq. (10) of the KVMem paper),
+selection, and rematerialization of the 4096-block view (2048 hits re-encoded
+from their raw-K shadow pages, 2048 misses gathered + re-RoPE'd + V copied).
+For `value` the misses' raw K/V sit in HBM; a second leg repeats the step
+with the misses in pinned host memory (DMA on a side stream overlapped with
+the scatter kernel) and is reported separately.
+
+Prints one JSON line. See --help for options.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("history blocks scored/s + rematerialized KV GB/s (fraction of HBM peak), 1M-tok")
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--pcie-steps", type=int, default=2,
+                    help="steps of the pinned-host leg (0 to skip)")
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle sample")
+    ap.add_argument("--cpu-pairs", type=int, default=6,
+                    help="(layer, KV head) pairs in the CPU oracle sample")
+    ap.add_argument("--workload", default="ws1m")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="first run a plain device copy of 2 GiB (counter calibration)")
+    return ap.parse_args()
+
+
+class Workspace:
+    """Device-resident inputs and the page pool of one seeded workspace."""
+
+    def __init__(self, k, wl, dev):
+        import torch
+        import synth
+        self.k, self.wl, self.dev = k, wl, dev
+        self.dims = k.dims_for(wl)
+        self.dt = k.KVM_BF16
+        N, nbytes = wl.n_blocks, wl.block_bytes
+        self.N = N
+        self.n_new = wl.n_q_tokens // wl.block_tokens          # blocks of this step's prefill
+        self.index = torch.zeros((wl.n_layers, wl.n_kv_heads, N, wl.head_dim),
+                                 dtype=torch.int16, device=dev)
+        # --- Mean-K of the history, built from generated raw K in chunks ----
+        chunk = 256
+        stage = [torch.empty((chunk, wl.block_elems), dtype=torch.int16).pin_memory()
+                 for _ in range(2)]
+        dchunk = torch.empty((chunk, wl.block_elems), dtype=torch.int16, device=dev)
+        n_hist = N - self.n_new
+        starts = list(range(0, n_hist, chunk))
+        gen_err = []
+
+        def gen(i):
+            s = starts[i]
+            n = min(chunk, n_hist - s)
+            try:
+                synth.kv_blocks(wl, "K", s, n, out=stage[i & 1].numpy()[:n].view(np.uint16))
+            except Exception as e:  # pragma: no cover
+                gen_err.append(e)
+
+        t0 = time.time()
+        build_ms, build_launch = 0.0, 0
+        th = threading.Thread(target=gen, args=(0,))
+        th.start()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i, s in enumerate(starts):
+            th.join()
+            if gen_err:
+                raise gen_err[0]
+            n = min(chunk, n_hist - s)
+            dchunk[:n].copy_(stage[i & 1][:n], non_blocking=True)
+            torch.cuda.current_stream().synchronize()
+            if i + 1 < len(starts):
+                th = threading.Thread(target=gen, args=(i + 1,))
+                th.start()
+            ev0.record()
+            k.kvm_build_index(self.dims, self.dt, dchunk, nbytes, s, n, self.index, N)
+            ev1.record()
+            ev1.synchronize()
+            build_ms += ev0.elapsed_time(ev1)
+            build_launch += 1
+            if i % 16 == 0:
+                log(f"index build {s + n}/{n_hist} blocks, {time.time() - t0:.1f}s")
+        self.build_stats = {"launches": build_launch, "blocks": n_hist, "ms": build_ms}
+        del dchunk, stage
+        # this step's freshly prefilled blocks: raw K/V on the device
+        self.new_k = self._gen_dev("K", n_hist, self.n_new)
+        self.new_v = self._gen_dev("V", n_hist, self.n_new)
+        k.kvm_build_index(self.dims, self.dt, self.new_k, nbytes, n_hist, self.n_new,
+                          self.index, N)
+        self.q = torch.from_numpy(synth.query(wl).view(np.int16)).to(dev)
+        T = wl.n_q_tokens
+        self.ws_bytes = k.kvm_score_ws_bytes(self.dims, self.dt, T, N)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.scores = torch.empty(N, dtype=torch.float32, device=dev)
+        Kb = wl.budget_blocks
+        self.sel = torch.empty(Kb, dtype=torch.int32, device=dev)
+        self.n_sel = torch.empty(1, dtype=torch.int32, device=dev)
+        self.base = torch.empty(Kb, dtype=torch.int32, device=dev)
+        self.page = torch.empty(Kb, dtype=torch.int32, device=dev)
+        log(f"index ready in {time.time() - t0:.1f}s")
+
+    def _gen_dev(self, which, b0, nb):
+        import synth
+        import torch
+        h = torch.empty((nb, self.wl.block_elems), dtype=torch.int16).pin_memory()
+        synth.kv_blocks(self.wl, which, b0, nb, out=h.numpy().view(np.uint16))
+        return h.to(self.dev)
+
+    def score_select(self):
+        k, wl = self.k, self.wl
+        k.kvm_score_blocks(self.dims, self.dt, self.q, wl.n_q_tokens, self.index, self.N, self.N,
+                           k.KVM_INDEX_DEVICE, 0, self.scores, self.ws, self.ws_bytes)
+        k.kvm_select(self.scores, self.N, wl.n_sink, wl.n_recent, wl.budget_blocks,
+                     wl.block_tokens, self.sel, self.n_sel, self.base)
+
+    def setup_pool(self, sel: np.ndarray):
+        """Pool + context; even-ranked selected blocks resident, odd-ranked staged."""
+        import synth
+        import torch
+        k, wl, dev = self.k, self.wl, self.dev
+        self.hits = sel[0::2].copy()
+        self.misses = sel[1::2].copy()
+        n_slots = wl.budget_blocks + wl.append_blocks + 64
+        dt = torch.int16
+        self.k_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        self.v_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        self.k_shadow = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        max_pos = (wl.budget_blocks + wl.reserve_blocks) * wl.block_tokens
+        self.ctx = k.KvmCtx(self.dims, self.dt, self.k_view, self.v_view, self.k_shadow, n_slots,
+                            wl.final_blocks, max_pos, wl.theta, wl.rope_layout, 64)
+        nh, nm = len(self.hits), len(self.misses)
+        # raw K/V of the resident half (device; re-registered before every step)
+        self.hit_k = torch.empty((nh, wl.block_elems), dtype=dt, device=dev)
+        self.hit_v = torch.empty((nh, wl.block_elems), dtype=dt, device=dev)
+        # lower-tier copies of the missing half: pinned host, and an HBM copy
+        self.miss_k_h = torch.empty((nm, wl.block_elems), dtype=dt).pin_memory()
+        self.miss_v_h = torch.empty((nm, wl.block_elems), dtype=dt).pin_memory()
+        tmp = torch.empty((64, wl.block_elems), dtype=dt).pin_memory()
+        tv = tmp.numpy().view(np.uint16)
+        for which, dst in (("K", self.hit_k), ("V", self.hit_v)):
+            for i, b in enumerate(self.hits):
+                synth.kv_blocks(wl, which, int(b), 1, out=tv[i % 64:i % 64 + 1])
+                if i % 64 == 63 or i == nh - 1:
+                    s = i - (i % 64)
+                    dst[s:i + 1].copy_(tmp[:i + 1 - s])
+            torch.cuda.synchronize()
+        for which, dst in (("K", self.miss_k_h), ("V", self.miss_v_h)):
+            dv = dst.numpy().view(np.uint16)
+            for i, b in enumerate(self.misses):
+                synth.kv_blocks(wl, which, int(b), 1, out=dv[i:i + 1])
+        self.miss_k_d = self.miss_k_h.to(dev)
+        self.miss_v_d = self.miss_v_h.to(dev)
+        torch.cuda.synchronize()
+
+    def set_miss_sources(self, where: str):
+        k, wl = self.k, self.wl
+        kk, vv, loc = ((self.miss_k_d, self.miss_v_d, k.KVM_SRC_DEVICE) if where == "hbm" else
+                       (self.miss_k_h, self.miss_v_h, k.KVM_SRC_HOST_PINNED))
+        for i, b in enumerate(self.misses):
+            self.ctx.kvm_ctx_set_source(int(b), 1, kk[i], vv[i], wl.block_bytes, loc)
+
+    def reset_pool(self):
+        """Back to the step's start: all pages free, then the resident half
+        registered again as freshly prefilled (K page stale)."""
+        wl = self.wl
+        self.ctx.kvm_ctx_evict(0, wl.final_blocks)
+        for i, b in enumerate(self.hits):
+            self.ctx.kvm_ctx_register_resident(int(b), 1, self.hit_k[i], self.hit_v[i],
+                                               wl.block_bytes)
+
+    def step(self):
+        """The timed hot path of one agent step."""
+        k, wl = self.k, self.wl
+        k.kvm_build_index(self.dims, self.dt, self.new_k, wl.block_bytes, self.N - self.n_new,
+                          self.n_new, self.index, self.N)
+        self.score_select()
+        return self.ctx.kvm_rematerialize(self.sel, self.n_sel, self.page)
+
+
+def cpu_baseline(wl, pairs: int) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same step."""
+    import synth
+    from oracle import pipeline as op
+    from oracle.scores import lg_partial_scores
+    from oracle.select import select_blocks
+    from oracle.meank import mean_k
+    from oracle.rope import rope_rotate
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    N, d = wl.n_blocks, wl.head_dim
+    G, T = wl.group, wl.n_q_tokens
+    rng = np.random.default_rng(0)
+    # scoring: `pairs` (layer, KV head) pairs over all N blocks (index drawn
+    # directly, same shape; the oracle's cost does not depend on the values)
+    sub = wl.scaled(n_layers=1)
+    idx = op.as_f64(synth.index_direct(sub, 0, N), "bf16")          # [1][Hkv][N][d]
+    q = op.as_f64(synth.query(sub), "bf16")                          # [1][Hq][T][d]
+    t0 = time.perf_counter()
+    for p in range(pairs):
+        lg_partial_scores(q, idx, 0, p % wl.n_kv_heads)
+    t_pair = (time.perf_counter() - t0) / pairs
+    # Mean-K of the step's new blocks (16 of them), selection, re-RoPE of 8 blocks
+    t0 = time.perf_counter()
+    nb = 2
+    mean_k(op.raw_blocks(wl, "K", 0, nb), "bf16")
+    t_mk = (time.perf_counter() - t0) / nb
+    R = rng.random(N)
+    t0 = time.perf_counter()
+    select_blocks(R, wl.n_sink, wl.n_recent, wl.budget_blocks)
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    nr = 4
+    for i in range(nr):
+        kb = op.raw_blocks(wl, "K", i, 1)[0]
+        rope_rotate(kb, 32 * i + np.arange(32), wl.theta, wl.rope_layout)
+    t_rope = (time.perf_counter() - t0) / nr
+    n_pairs = wl.n_layers * wl.n_kv_heads
+    est = t_pair * n_pairs + t_mk * (T // 32) + t_sel + t_rope * wl.budget_blocks
+    return {"value": N / est, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"float64 NumPy oracle: Eq. (10) partial scores of {pairs} of "
+                       f"{n_pairs} (layer, KV head) pairs over all {N} blocks "
+                       f"({t_pair:.2f} s each), Mean-K of {nb} blocks, one selection, "
+                       f"re-RoPE of {nr} blocks; extrapolated to one full step "
+                       f"({est:.0f} s)"),
+            "est_step_s": est}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; pass --gpus 1"}))
+        sys.exit(2)
+    import torch
+    import attention_space_block_amd as k
+    import synth
+    k._abi.lib()
+    wl = synth.get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        # a plain elementwise copy of known size: 2 GiB read + 2 GiB written
+        a = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.add(a, 0.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    t_setup = time.time()
+    ws = Workspace(k, wl, dev)
+    ws.score_select()
+    torch.cuda.synchronize()
+    n = int(ws.n_sel.item())
+    sel0 = ws.sel.cpu().numpy()[:n]
+    ws.setup_pool(sel0)
+    ws.set_miss_sources("hbm")
+    log(f"setup done in {time.time() - t_setup:.1f}s; view {n} blocks, "
+        f"{len(ws.hits)} resident, {len(ws.misses)} staged")
+
+    def run(n_steps, profile):
+        times, stats = [], None
+        for _ in range(n_steps):
+            ws.reset_pool()
+            torch.cuda.synchronize()
+            if profile and not times:
+                k.kvm_profile_enable(True)
+            t0 = time.perf_counter()
+            stats = ws.step()
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+        return times, stats
+
+    run(args.warmup, False)
+    times, stats = run(args.steps, True)
+    prof = k.kvm_profile_read()
+    k.kvm_profile_enable(False)
+    ms = 1e3 * sum(times) / len(times)
+    sel_now = ws.sel.cpu().numpy()[:n]
+    assert np.array_equal(sel_now, sel0), "selection changed between steps"
+    log(f"value leg: {ms:.2f} ms/step, stats {stats}")
+    kern = {name: {"launches": c, "avg_ms": t / c} for name, (c, t) in prof.items()}
+    L, Hq, T, N, d = wl.n_layers, wl.n_q_heads, wl.n_q_tokens, wl.n_blocks, wl.head_dim
+    flops_pass = 2.0 * L * Hq * T * N * d
+    page = wl.block_bytes
+    nh, nm = len(ws.hits), len(ws.misses)
+    remat_bytes = nh * 2 * page + nm * 5 * page
+    remat = kern.get("remat")
+    remat_gbps = remat_bytes / (remat["avg_ms"] * 1e-3) / 1e9 if remat else None
+    # dominant kernel of the step
+    dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
+    name, info = dom
+    if name.startswith("score_pass"):
+        ach = flops_pass / (info["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": name, "bound": "mfma", "achieved": ach,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    elif name == "remat":
+        roof = {"kernel": name, "bound": "hbm", "achieved": remat_gbps, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS, "traffic": None}
+    else:
+        roof = {"kernel": name, "bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+    bst = ws.build_stats
+    build_bytes = bst["blocks"] * (page + L * wl.n_kv_heads * d * 2)
+    build_gbps = build_bytes / (bst["ms"] * 1e-3) / 1e9
+    # PCIe leg: misses from pinned host memory
+    pcie = None
+    if args.pcie_steps > 0:
+        ws.set_miss_sources("pinned")
+        ptimes, pst = run(args.pcie_steps, False)
+        pms = 1e3 * sum(ptimes) / len(ptimes)
+        pcie = {"ms_per_step": pms, "blocks_per_s": N / (pms * 1e-3),
+                "h2d_bytes": pst["h2d_bytes"], "batches": pst["batches"],
+                "step_h2d_GBps": pst["h2d_bytes"] / (pms * 1e-3) / 1e9}
+        log(f"pcie leg: {pms:.2f} ms/step")
+        ws.set_miss_sources("hbm")
+    cpu = None
+    if args.cpu_baseline:
+        log("timing the CPU oracle sample")
+        cpu = cpu_baseline(wl, args.cpu_pairs)
+    out = {
+        "metric": METRIC,
+        "value": N / (ms * 1e-3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; no dataset)",
+        "config": {"workload": "1M-token workspace: 32768 blocks x 32 tokens, 64 layers, "
+                               "8 KV / 48 query heads, d 128, 512 query tokens, budget 4096 "
+                               "blocks (sink 1, recent 64), half of the view resident",
+                   "n_blocks": N, "n_q_tokens": T, "budget_blocks": wl.budget_blocks},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "remat": {"avg_ms": remat["avg_ms"] if remat else None, "bytes": remat_bytes,
+                  "GBps": remat_gbps,
+                  "hbm_frac": remat_gbps / HBM_PEAK_GBPS if remat_gbps else None,
+                  "hits": nh, "misses": nm},
+        "score": {"ms": sum(v["avg_ms"] for kk, v in kern.items() if kk.startswith("score")),
+                  "blocks_per_s": None, "tflops_per_pass": flops_pass / 1e12},
+        "build": {"blocks": bst["blocks"], "GBps": build_gbps,
+                  "hbm_frac": build_gbps / HBM_PEAK_GBPS},
+        "pcie_leg": pcie,
+        "kernels": kern,
+    }
+    out["score"]["blocks_per_s"] = N / (out["score"]["ms"] * 1e-3)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

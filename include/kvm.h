@@ -232,6 +232,27 @@ int kvm_ctx_sync(kvm_ctx* ctx);
  * (-1 = K page stale). */
 int kvm_ctx_block_state(kvm_ctx* ctx, int64_t block, int32_t* slot, int32_t* baked_pos);
 
+/* Reclaim the pool pages of resident blocks [first_block, first_block + n_blocks)
+ * (KVMem Sec. 4.4: a page can be reclaimed at once because the block keeps a
+ * valid lower-tier copy; the block becomes a miss for later selections).
+ * Blocks that are not resident are skipped. Host-side bookkeeping only. */
+int kvm_ctx_evict(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (tracing aid). While enabled, every kernel launch of the
+ * library is bracketed by a HIP event pair on its stream. kvm_profile_read
+ * waits for the recorded events and returns, per kernel name, the number of
+ * launches and their summed duration since profiling was (re)enabled; *n is
+ * the number of distinct kernels (entries beyond `max` are not written). */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} kvm_kernel_stat;
+
+int kvm_profile_enable(int32_t on);
+int kvm_profile_read(kvm_kernel_stat* out, int32_t max, int32_t* n);
+
 #ifdef __cplusplus
 }
 #endif
