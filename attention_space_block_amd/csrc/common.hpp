@@ -74,6 +74,11 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   return (uint16_t)((sign << 15) | ((uint64_t)e8 << 7) | keep);
 }
 
+// exp2 as the single hardware instruction (v_exp_f32). Results below the fp32
+// normal range may flush to zero, which is harmless for softmax terms that are
+// at least 2^126 times smaller than the row maximum.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Streaming (non-temporal) 16-byte loads and stores.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt(const void* p) {
@@ -85,6 +90,10 @@ __device__ __forceinline__ void st_nt(void* p, const uint4& v) {
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
+// Plain (cached) 16-byte loads and stores: measured faster than the
+// non-temporal forms for read-modify-write streams on gfx950.
+__device__ __forceinline__ uint4 ld_plain(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st_plain(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 // XCD-aware remap of a linear workgroup id: hardware dispatches workgroup i to
 // XCD (i % 8). Returns a logical id such that each XCD receives one contiguous
 // range of logical ids (so neighbouring logical work shares one L2).

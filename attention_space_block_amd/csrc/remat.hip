@@ -41,11 +41,14 @@ struct RematJob {
 };
 enum { JOB_WRITE_SHADOW = 1, JOB_COPY_V = 2 };
 
+// (l, g) units of 32 token rows handled by one workgroup
+static constexpr int REMAT_UNITS = 4;
+
 struct RematArgs {
   const RematJob* jobs;
   int32_t n_jobs;
-  int32_t units_per_job;     // work units per block
-  int32_t rows_per_unit;     // rows (tokens of one (l, g)) per unit
+  int32_t wg_per_job;        // ceil(L * Hkv / REMAT_UNITS) workgroups per block
+  int32_t rows_per_page;     // L * Hkv * B
   int64_t page_bytes;
   char* k_view;
   char* v_view;
@@ -88,80 +91,106 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
                     __float_as_uint(x[3]));
 }
 
-// Each thread owns two 16-byte pieces of one row (one token of one (l, g)):
+// Work split: a flat grid; workgroup w handles UNITS consecutive (l, g) units
+// (32 token rows each) of job w / units_per_wg_count, so concurrently running
+// workgroups stream neighbouring bytes of the same page (DRAM locality like a
+// plain copy). A thread always sees the same token index j of its rows, so its
+// (cos, sin) pairs for position pos + j are loaded once into registers.
+// Each thread owns two 16-byte pieces of a row:
 // LAYOUT 0 (pairs (2t, 2t+1)): pieces [t0, t0+P) and [t0+P, t0+2P);
 // LAYOUT 1 (pairs (t, t+d/2)): pieces [t0, t0+P) and [t0+d/2, t0+d/2+P).
+// All loads of a workgroup's rows are issued before the first store; loads and
+// stores are plain (cached) ones, faster here than the non-temporal forms.
 template <typename T, int D, int LAYOUT>
 __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
   constexpr int TPR = D / (2 * P);               // threads per row
   constexpr int RPI = 256 / TPR;                 // rows per workgroup pass
   constexpr int ROW_BYTES = D * sizeof(T);
+  constexpr int HALF = D / 2;
+  constexpr int ROWS = REMAT_UNITS * 32;         // rows per workgroup
+  constexpr int NR = ROWS / RPI;                 // rows per thread
+  constexpr int NJ = RPI >= 32 ? 1 : 32 / RPI;   // distinct token indices per thread
+  constexpr int NC = LAYOUT == 0 ? P : P;        // (cos, sin) pairs per piece pair
+  const int32_t jid = blockIdx.x / a.wg_per_job;
+  const int32_t wpart = blockIdx.x % a.wg_per_job;
+  if (jid >= a.n_jobs) return;
+  const RematJob job = a.jobs[jid];
   const int trow = threadIdx.x / TPR;
   const int tcol = threadIdx.x % TPR;
   const int t0 = LAYOUT == 0 ? tcol * 2 * P : tcol * P;            // first element
   const int off1 = LAYOUT == 0 ? P : D / 2;                         // second piece offset
-  const int64_t total_units = (int64_t)a.n_jobs * a.units_per_job;
-  for (int64_t u = blockIdx.x; u < total_units; u += gridDim.x) {
-    const int32_t jid = (int32_t)(u / a.units_per_job);
-    const int32_t uid = (int32_t)(u % a.units_per_job);
-    const RematJob job = a.jobs[jid];
-    const int64_t page = (int64_t)job.slot * a.page_bytes;
-    for (int r = trow; r < a.rows_per_unit; r += RPI) {
-      const int64_t row = (int64_t)uid * a.rows_per_unit + r;     // row within the page
-      const int j = (int)(row & 31);                                // token within block
-      const int64_t b0 = row * ROW_BYTES + (int64_t)t0 * sizeof(T);
-      const int64_t b1 = b0 + (int64_t)off1 * sizeof(T);
-      const uint4 k0 = ld_nt(job.src_k + b0);
-      const uint4 k1 = ld_nt(job.src_k + b1);
-      float x0[P], x1[P];
-      unpack<T>(k0, x0);
-      unpack<T>(k1, x1);
-      const float2* cs = a.table + (int64_t)(job.pos + j) * (D / 2);
-      float y0[P], y1[P];
-      if (LAYOUT == 0) {
+  // (cos, sin) of the pairs this thread rotates, for each of its token indices
+  float2 cs[NJ][NC];
 #pragma unroll
-        for (int q = 0; q < P / 2; ++q) {
-          const float2 c0 = cs[t0 / 2 + q];
-          const float2 c1 = cs[(t0 + P) / 2 + q];
-          y0[2 * q] = x0[2 * q] * c0.x - x0[2 * q + 1] * c0.y;
-          y0[2 * q + 1] = x0[2 * q] * c0.y + x0[2 * q + 1] * c0.x;
-          y1[2 * q] = x1[2 * q] * c1.x - x1[2 * q + 1] * c1.y;
-          y1[2 * q + 1] = x1[2 * q] * c1.y + x1[2 * q + 1] * c1.x;
-        }
-      } else {
+  for (int s = 0; s < NJ; ++s) {
+    const int j = (trow + s * RPI) & 31;
+    const float2* row = a.table + (int64_t)(job.pos + j) * HALF;
 #pragma unroll
-        for (int q = 0; q < P; ++q) {
-          const float2 c = cs[t0 + q];
-          y0[q] = x0[q] * c.x - x1[q] * c.y;
-          y1[q] = x0[q] * c.y + x1[q] * c.x;
-        }
+    for (int q = 0; q < NC; ++q)
+      cs[s][q] = LAYOUT == 0 ? row[t0 / 2 + q] : row[t0 + q];
+  }
+  const int64_t page = (int64_t)job.slot * a.page_bytes;
+  const int64_t row0 = (int64_t)wpart * ROWS;
+  const bool wshadow = (job.flags & JOB_WRITE_SHADOW) != 0;
+  const bool copyv = (job.flags & JOB_COPY_V) != 0;
+  uint4 k0[NR], k1[NR], v0[NR], v1[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    if (row0 + trow + u * RPI >= a.rows_per_page) continue;   // ragged last workgroup
+    const int64_t b0 = (row0 + trow + u * RPI) * ROW_BYTES + (int64_t)t0 * sizeof(T);
+    k0[u] = ld_plain(job.src_k + b0);
+    k1[u] = ld_plain(job.src_k + b0 + (int64_t)off1 * sizeof(T));
+    if (copyv) {
+      v0[u] = ld_plain(job.src_v + b0);
+      v1[u] = ld_plain(job.src_v + b0 + (int64_t)off1 * sizeof(T));
+    }
+  }
+  char* kv = a.k_view + page;
+  char* sh = a.k_shadow + page;
+  char* vv = a.v_view + page;
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    if (row0 + trow + u * RPI >= a.rows_per_page) continue;
+    const int64_t b0 = (row0 + trow + u * RPI) * ROW_BYTES + (int64_t)t0 * sizeof(T);
+    const int64_t b1 = b0 + (int64_t)off1 * sizeof(T);
+    const float2* c = cs[u % NJ];
+    float x0[P], x1[P], y0[P], y1[P];
+    unpack<T>(k0[u], x0);
+    unpack<T>(k1[u], x1);
+    if (LAYOUT == 0) {
+#pragma unroll
+      for (int q = 0; q < P / 2; ++q) {
+        const float2 c0 = c[q];
+        const float2 c1 = c[P / 2 + q];
+        y0[2 * q] = x0[2 * q] * c0.x - x0[2 * q + 1] * c0.y;
+        y0[2 * q + 1] = x0[2 * q] * c0.y + x0[2 * q + 1] * c0.x;
+        y1[2 * q] = x1[2 * q] * c1.x - x1[2 * q + 1] * c1.y;
+        y1[2 * q + 1] = x1[2 * q] * c1.y + x1[2 * q + 1] * c1.x;
       }
-      char* kv = a.k_view + page;
-      *reinterpret_cast<uint4*>(kv + b0) = pack<T>(y0);
-      *reinterpret_cast<uint4*>(kv + b1) = pack<T>(y1);
-      if (job.flags & JOB_WRITE_SHADOW) {
-        char* sh = a.k_shadow + page;
-        st_nt(sh + b0, k0);
-        st_nt(sh + b1, k1);
+    } else {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        y0[q] = x0[q] * c[q].x - x1[q] * c[q].y;
+        y1[q] = x0[q] * c[q].y + x1[q] * c[q].x;
       }
-      if (job.flags & JOB_COPY_V) {
-        const uint4 v0 = ld_nt(job.src_v + b0);
-        const uint4 v1 = ld_nt(job.src_v + b1);
-        char* vv = a.v_view + page;
-        *reinterpret_cast<uint4*>(vv + b0) = v0;
-        *reinterpret_cast<uint4*>(vv + b1) = v1;
-      }
+    }
+    st_plain(kv + b0, pack<T>(y0));
+    st_plain(kv + b1, pack<T>(y1));
+    if (wshadow) {
+      st_plain(sh + b0, k0[u]);
+      st_plain(sh + b1, k1[u]);
+    }
+    if (copyv) {
+      st_plain(vv + b0, v0[u]);
+      st_plain(vv + b1, v1[u]);
     }
   }
 }
 
-typedef void (*remat_fn)(RematArgs);
-
 static void launch_remat(int32_t dtype, int32_t d, int32_t layout, const RematArgs& a,
                          hipStream_t s) {
-  const int64_t units = (int64_t)a.n_jobs * a.units_per_job;
-  const int64_t grid = std::min<int64_t>(units, 256 * 32);
+  const int64_t grid = (int64_t)a.n_jobs * a.wg_per_job;
   if (grid <= 0) return;
   dim3 g((uint32_t)grid), b(256);
   KernelTimer tm("remat", s);
@@ -650,8 +679,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     KVM_HIP(hipMemcpyAsync(c->d_jobs, J, (size_t)nj * sizeof(RematJob), hipMemcpyHostToDevice, s));
   const kvm_dims& dm = c->d.dims;
   RematArgs a{};
-  a.units_per_job = dm.n_layers * dm.n_kv_heads;  // one unit = the B rows of one (l, g)
-  a.rows_per_unit = B;
+  a.rows_per_page = dm.n_layers * dm.n_kv_heads * B;
+  a.wg_per_job = (dm.n_layers * dm.n_kv_heads + REMAT_UNITS - 1) / REMAT_UNITS;
   a.page_bytes = c->page_bytes;
   a.k_view = (char*)c->d.k_view;
   a.v_view = (char*)c->d.v_view;

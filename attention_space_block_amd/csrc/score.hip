@@ -56,6 +56,7 @@ struct MfmaShape {
   static constexpr int ROW_B = D * 2;             // bytes of one bf16 row
   static constexpr int LDS_ROW = ROW_B + 16;      // padded LDS row (bank spread)
   static constexpr int TILE = 64;                 // rows staged per iteration
+  static constexpr int SUB = TILE / 32;           // 32-row subtiles per stage
   static constexpr int LOADS = TILE * ROW_B / (256 * 16);  // 16-B loads per thread
 };
 
@@ -74,6 +75,70 @@ struct Pass1Args {
   int32_t nlg;
   uint32_t total_wg;        // padded to a multiple of 8
 };
+
+// Interleave hint for the scheduler: one MFMA, then `valu` VALU instructions,
+// `n` times, so the matrix pipe and the VALU work on different subtiles at
+// once inside one wavefront.
+template <int N_MFMA, int VALU>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < N_MFMA; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  }
+}
+
+// 32 rows of the staged LDS tile (A operand, one 16-byte piece per lane and
+// k-step) times the wave's two stationary B tiles.
+template <int KS>
+__device__ __forceinline__ void mfma_subtile(f32x16 (&acc)[2], const char* arow,
+                                             const bf16x8 (&bop)[2][KS]) {
+  bf16x8 av[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[0][ks], acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[1][ks], acc[1], 0, 0, 0);
+  }
+}
+
+// Online (max, sum-exp) update of one lane's query row with 16 new scores
+// (raw dot products; x = acc * scale). Branch-free: a lane that has seen only
+// -inf keeps m = -inf and s = 0.
+__device__ __forceinline__ void lse_update(const f32x16& acc, float scale, float& m_run,
+                                           double& s_run) {
+  float mx = acc[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+  const float m_new = fmaxf(m_run, mx * scale);
+  const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m_use));
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int v = 0; v < w; ++v) e[v] += e[v + w];
+  const float resc = hw_exp2(m_run - m_use);
+  s_run = s_run * (double)resc + (double)e[0];
+  m_run = m_new;
+}
+
+__device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nvalid) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int i = 8 * (v >> 2) + 4 * half + (v & 3);
+      if (i >= nvalid) acc[c][v] = -INFINITY;
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
@@ -119,14 +184,24 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   uint4 stage[S::LOADS];
   auto gload = [&](int tile) {
     const int32_t t0 = b_begin + tile * S::TILE;
+    if (t0 + S::TILE <= b_end) {
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int e = (i * 256 + threadIdx.x);      // 16-B piece id in the tile
-      const int r = e / (S::ROW_B / 16);
-      const int c = e % (S::ROW_B / 16);
-      const int32_t b = t0 + r;
-      stage[i] = b < b_end ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + c * 8)
-                           : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int e = (i * 256 + threadIdx.x);      // 16-B piece id in the tile
+        const int r = e / (S::ROW_B / 16);
+        const int c = e % (S::ROW_B / 16);
+        stage[i] = *reinterpret_cast<const uint4*>(kb + (int64_t)(t0 + r) * D + c * 8);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int e = (i * 256 + threadIdx.x);
+        const int r = e / (S::ROW_B / 16);
+        const int c = e % (S::ROW_B / 16);
+        const int32_t b = t0 + r;
+        stage[i] = b < b_end ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + c * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -138,7 +213,18 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
       *reinterpret_cast<uint4*>(&lds[buf][r * S::LDS_ROW + c * 16]) = stage[i];
     }
   };
+  auto arow = [&](int buf, int sub) -> const char* {
+    return &lds[buf][(sub * 32 + col) * S::LDS_ROW + half * 16];
+  };
+  auto update = [&](f32x16 (&acc)[2], int32_t nvalid) {
+    if (nvalid < 32) mask_rows(acc, half, nvalid);   // uniform: only a split's last tile
+    lse_update(acc[0], a.scale, m_run[0], s_run[0]);
+    lse_update(acc[1], a.scale, m_run[1], s_run[1]);
+  };
 
+  // A stage holds SUB subtiles of 32 blocks; the next stage's global loads
+  // are in flight while all of them are multiplied and reduced.
+  f32x16 acc[2];
   if (ntiles > 0) {
     gload(0);
     lstore(0);
@@ -146,49 +232,15 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
     const int32_t t0 = b_begin + it * S::TILE;
-#pragma unroll
-    for (int at = 0; at < 2; ++at) {
-      f32x16 acc[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ct][v] = 0.0f;
-      const char* arow = &lds[buf][(at * 32 + col) * S::LDS_ROW + half * 16];
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bq[0][ks], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bq[1][ks], acc[1], 0, 0, 0);
-      }
-      const int32_t nvalid = b_end - (t0 + at * 32);  // blocks of this 32-tile that exist
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        float x[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int i = 8 * (v >> 2) + 4 * half + (v & 3);
-          x[v] = (i < nvalid) ? acc[ct][v] * a.scale : -INFINITY;
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
-        const float m_new = fmaxf(m_run[ct], mx);
-        if (m_new == -INFINITY) continue;
-        float e[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) e[v] = exp2f(x[v] - m_new);
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int v = 0; v < w; ++v) e[v] += e[v + w];
-        const float resc = exp2f(m_run[ct] - m_new);
-        s_run[ct] = s_run[ct] * (double)resc + (double)e[0];
-        m_run[ct] = m_new;
-      }
+    const bool more = it + 1 < ntiles;
+    if (more) gload(it + 1);
+#pragma unroll 1
+    for (int sub = 0; sub < S::SUB; ++sub) {
+      mfma_subtile<S::KS>(acc, arow(buf, sub), bq);
+      update(acc, b_end - (t0 + 32 * sub));
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1);
     __syncthreads();
   }
   // Merge the two lane halves (same query row, disjoint blocks).
@@ -199,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
     const float mm = fmaxf(m_run[ct], mo);
     double s = 0.0;
     if (mm != -INFINITY)
-      s = s_run[ct] * (double)exp2f(m_run[ct] - mm) + so * (double)exp2f(mo - mm);
+      s = s_run[ct] * (double)hw_exp2(m_run[ct] - mm) + so * (double)hw_exp2(mo - mm);
     if (half == 0) {
       const int rho = row_base + ct * 32 + col;
       a.part[((int64_t)L_lg * a.nsplit + split) * a.TGp + rho] = make_float2(mm, (float)s);
@@ -244,6 +296,19 @@ struct Pass2Args {
   uint32_t total_wg;
 };
 
+// Column sums over one subtile's 16 rows per lane: sum of exp2(acc*scale - lse).
+__device__ __forceinline__ void colsum_update(const f32x16& acc, const float (&ls)[16],
+                                              float scale, double& colsum) {
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -ls[v]));
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int v = 0; v < w; ++v) e[v] += e[v + w];
+  colsum += (double)e[0];
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   using S = MfmaShape<D>;
@@ -278,19 +343,33 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   float lstage = 0.0f;
   auto gload = [&](int tile) {
     const int32_t r0 = tile * S::TILE;
+    if (r0 + S::TILE <= a.TG) {
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int e = (i * 256 + threadIdx.x);
-      const int r = e / (S::ROW_B / 16);
-      const int c = e % (S::ROW_B / 16);
-      const int32_t rho = r0 + r;
-      if (rho < a.TG) {
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int e = (i * 256 + threadIdx.x);
+        const int r = e / (S::ROW_B / 16);
+        const int c = e % (S::ROW_B / 16);
+        const int32_t rho = r0 + r;
         const int hh = g * a.G + rho / a.T;
         const int m = rho % a.T;
         stage[i] = *reinterpret_cast<const uint4*>(
             a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + c * 8);
-      } else {
-        stage[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int e = (i * 256 + threadIdx.x);
+        const int r = e / (S::ROW_B / 16);
+        const int c = e % (S::ROW_B / 16);
+        const int32_t rho = r0 + r;
+        if (rho < a.TG) {
+          const int hh = g * a.G + rho / a.T;
+          const int m = rho % a.T;
+          stage[i] = *reinterpret_cast<const uint4*>(
+              a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + c * 8);
+        } else {
+          stage[i] = make_uint4(0, 0, 0, 0);
+        }
       }
     }
     if (threadIdx.x < S::TILE) lstage = lse_lg[r0 + threadIdx.x];
@@ -305,51 +384,39 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
     }
     if (threadIdx.x < S::TILE) lse_s[buf][threadIdx.x] = lstage;
   };
+  auto arow = [&](int buf, int sub) -> const char* {
+    return &lds[buf][(sub * 32 + col) * S::LDS_ROW + half * 16];
+  };
+  // LSE of the 16 rows a lane holds in a subtile: rows 8*q4 + 4*half + 0..3.
+  auto load_lse = [&](float (&ls)[16], int buf, int sub) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 v4 =
+          *reinterpret_cast<const float4*>(&lse_s[buf][sub * 32 + 8 * q4 + 4 * half]);
+      ls[4 * q4 + 0] = v4.x;
+      ls[4 * q4 + 1] = v4.y;
+      ls[4 * q4 + 2] = v4.z;
+      ls[4 * q4 + 3] = v4.w;
+    }
+  };
   double colsum[2] = {0.0, 0.0};
+  f32x16 acc[2];
+  float ls[16];
   gload(0);
   lstore(0);
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
-    if (it + 1 < ntiles) gload(it + 1);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 acc[2];
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[bt][v] = 0.0f;
-      const char* arow = &lds[buf][(rt * 32 + col) * S::LDS_ROW + half * 16];
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bk[0][ks], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bk[1][ks], acc[1], 0, 0, 0);
-      }
-      // LSE of the 16 rows this lane holds: rows 8*a + 4*half + b.
-      float ls[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v4 =
-            *reinterpret_cast<const float4*>(&lse_s[buf][rt * 32 + 8 * q4 + 4 * half]);
-        ls[4 * q4 + 0] = v4.x;
-        ls[4 * q4 + 1] = v4.y;
-        ls[4 * q4 + 2] = v4.z;
-        ls[4 * q4 + 3] = v4.w;
-      }
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt) {
-        float e[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) e[v] = exp2f(fmaf(acc[bt][v], a.scale, -ls[v]));
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-          for (int v = 0; v < w; ++v) e[v] += e[v + w];
-        colsum[bt] += (double)e[0];
-      }
+    const bool more = it + 1 < ntiles;
+    if (more) gload(it + 1);
+#pragma unroll 1
+    for (int sub = 0; sub < S::SUB; ++sub) {
+      mfma_subtile<S::KS>(acc, arow(buf, sub), bk);
+      load_lse(ls, buf, sub);
+      colsum_update(acc[0], ls, a.scale, colsum[0]);
+      colsum_update(acc[1], ls, a.scale, colsum[1]);
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1);
     __syncthreads();
   }
 #pragma unroll
@@ -481,7 +548,7 @@ __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
     if (lane == 0) red[wave] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float e = valid ? exp2f(x - mx) : 0.0f;
+    float e = valid ? hw_exp2(x - mx) : 0.0f;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
     if (lane == 0) red[4 + wave] = e;
@@ -524,7 +591,7 @@ __global__ __launch_bounds__(256) void score_stored_pass2(const float* __restric
     const float* row = S + ((int64_t)lg * n_blocks + b) * TG;
     const float* ls = lse_s + lg * TG;
     float t = 0.0f;
-    for (int r = 0; r < TG; ++r) t += exp2f(row[r] - ls[r]);
+    for (int r = 0; r < TG; ++r) t += hw_exp2(row[r] - ls[r]);
     s += (double)t;
   }
   scores[b] = (float)(s * inv_lh);
@@ -554,9 +621,9 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
     p.TGp = p.row_chunks * 256;
     // enough workgroups to fill 256 CUs several times over
     int32_t ns = 1;
-    while ((int64_t)nlg * p.row_chunks * ns < 2048 && (int64_t)ns * 64 * 2 <= N) ns *= 2;
+    while ((int64_t)nlg * p.row_chunks * ns < 2048 && (int64_t)ns * 128 * 2 <= N) ns *= 2;
     p.nsplit = ns;
-    p.split_blocks = (int32_t)(((N + ns - 1) / ns + 63) / 64 * 64);
+    p.split_blocks = (int32_t)(((N + ns - 1) / ns + 127) / 128 * 128);
     p.block_chunks = (int32_t)((N + 255) / 256);
     p.off_part = off;
     off = align256(off + (size_t)nlg * ns * p.TGp * sizeof(float2));

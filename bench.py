@@ -71,7 +71,7 @@ class Workspace:
         self.index = torch.zeros((wl.n_layers, wl.n_kv_heads, N, wl.head_dim),
                                  dtype=torch.int16, device=dev)
         # --- Mean-K of the history, built from generated raw K in chunks ----
-        chunk = 256
+        chunk = 1024
         stage = [torch.empty((chunk, wl.block_elems), dtype=torch.int16).pin_memory()
                  for _ in range(2)]
         dchunk = torch.empty((chunk, wl.block_elems), dtype=torch.int16, device=dev)
