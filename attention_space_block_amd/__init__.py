@@ -14,3 +14,4 @@ from .api import (  # noqa: F401
     KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
 )
 from ._abi import EXPORTED, LIB_PATH  # noqa: F401
+from .step import WorkingSetUpdater  # noqa: F401

@@ -137,6 +137,16 @@ class KvmCtx:
         rc = _abi.lib().kvm_ctx_set_gather(self._h, first_block, n_blocks, cb, None)
         _abi.check(rc, "kvm_ctx_set_gather")
 
+    def kvm_ctx_set_gather_raw(self, first_block: int, n_blocks: int, fn_ptr: int,
+                               user_ptr: int) -> None:
+        """Same as kvm_ctx_set_gather with a C function pointer (no Python in
+        the gather path); the caller keeps `user_ptr` alive."""
+        cb = ctypes.cast(ctypes.c_void_p(fn_ptr), _abi.GATHER_FN)
+        self._keep.append(cb)
+        rc = _abi.lib().kvm_ctx_set_gather(self._h, first_block, n_blocks, cb,
+                                           ctypes.c_void_p(user_ptr))
+        _abi.check(rc, "kvm_ctx_set_gather")
+
     def kvm_ctx_register_resident(self, first_block: int, n_blocks: int, k_raw, v_raw,
                                   block_stride: int, stream=None) -> None:
         rc = _abi.lib().kvm_ctx_register_resident(self._h, first_block, n_blocks, _ptr(k_raw),

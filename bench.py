@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle sample")
     ap.add_argument("--cpu-pairs", type=int, default=6,
                     help="(layer, KV head) pairs in the CPU oracle sample")
-    ap.add_argument("--workload", default="ws1m")
+    ap.add_argument("--workload", default="ws1m", choices=["ws1m", "ctx64k", "churn"])
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="first run a plain device copy of 2 GiB (counter calibration)")
     return ap.parse_args()
@@ -258,6 +258,102 @@ def cpu_baseline(wl, pairs: int) -> dict:
             "est_step_s": est}
 
 
+def index_from_generated_k(k, upd, wl, dev, n_blocks: int, chunk: int = 1024):
+    """Mean-K of the history built with the library from raw K generated on the
+    host in chunks (double-buffered pinned staging); returns build stats."""
+    import torch
+    import synth
+    stage = [torch.empty((chunk, wl.block_elems), dtype=torch.int16).pin_memory()
+             for _ in range(2)]
+    dchunk = torch.empty((chunk, wl.block_elems), dtype=torch.int16, device=dev)
+    starts = list(range(0, n_blocks, chunk))
+
+    def gen(i):
+        s0 = starts[i]
+        synth.kv_blocks(wl, "K", s0, min(chunk, n_blocks - s0),
+                        out=stage[i & 1].numpy()[:min(chunk, n_blocks - s0)].view(np.uint16))
+
+    th = threading.Thread(target=gen, args=(0,))
+    th.start()
+    t0 = time.time()
+    for i, s0 in enumerate(starts):
+        th.join()
+        n = min(chunk, n_blocks - s0)
+        dchunk[:n].copy_(stage[i & 1][:n])
+        if i + 1 < len(starts):
+            th = threading.Thread(target=gen, args=(i + 1,))
+            th.start()
+        upd.build(dchunk, s0, n)
+        torch.cuda.synchronize()
+        if i % 8 == 0:
+            log(f"index build {s0 + n}/{n_blocks} blocks, {time.time() - t0:.1f}s")
+
+
+def run_churn(args, k, wl, dev):
+    """The step-churn workspace: every step appends 64 freshly prefilled blocks
+    and updates the working set; resident pages are reused, misses are gathered
+    from a generator-backed lower tier through the pinned staging ring."""
+    import torch
+    import synth
+    steps = min(args.steps, wl.steps)
+    Kb, B = wl.budget_blocks, wl.block_tokens
+    upd = k.WorkingSetUpdater(k.dims_for(wl), k.KVM_BF16, wl.final_blocks, Kb, wl.n_sink,
+                              wl.n_recent, Kb + wl.append_blocks + 64,
+                              (Kb + wl.reserve_blocks) * B, dev, wl.theta, wl.rope_layout,
+                              batch_blocks=64, staging_blocks=256)
+    index_from_generated_k(k, upd, wl, dev, wl.n_blocks)
+    fn, user, keep = synth.gather_store(wl)
+    upd.ctx.kvm_ctx_set_gather_raw(0, wl.final_blocks, fn, user)
+    new_k = torch.empty((wl.append_blocks, wl.block_elems), dtype=torch.int16, device=dev)
+    new_v = torch.empty_like(new_k)
+    rows, prev = [], None
+    k.kvm_profile_enable(True)
+    for t in range(steps):
+        q = torch.from_numpy(synth.query(wl, step=t).view(np.int16)).to(dev)
+        if t > 0:
+            b0 = upd.n_blocks
+            new_k.copy_(torch.from_numpy(synth.kv_blocks(wl, "K", b0, wl.append_blocks).view(
+                np.int16).reshape(wl.append_blocks, -1)))
+            new_v.copy_(torch.from_numpy(synth.kv_blocks(wl, "V", b0, wl.append_blocks).view(
+                np.int16).reshape(wl.append_blocks, -1)))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if t > 0:
+            upd.append(new_k, new_v, wl.append_blocks)
+        st = upd.update(q, wl.n_q_tokens)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        n = int(upd.n_sel.item())
+        sel = upd.sel.cpu().numpy()[:n]
+        cand = set(sel[(sel >= wl.n_sink) & (sel < upd.n_blocks - wl.n_recent)].tolist())
+        ov = None if prev is None else len(cand & prev) / max(1, len(cand))
+        prev = cand
+        rows.append({"step": t, "ms": dt * 1e3, "n_blocks": upd.n_blocks, "overlap": ov, **st})
+        log(f"churn step {t}: {dt * 1e3:.1f} ms, hits {st['hits']}, misses {st['misses']}, "
+            f"evicted {st['evicted']}, overlap {ov}")
+    prof = k.kvm_profile_read()
+    k.kvm_profile_enable(False)
+    upd.close()
+    later = rows[1:] if len(rows) > 1 else rows
+    ms = sum(r["ms"] for r in later) / len(later)
+    ovs = [r["overlap"] for r in rows if r["overlap"] is not None]
+    out = {
+        "metric": METRIC, "value": wl.final_blocks / (ms * 1e-3), "unit": "blocks/s",
+        "n_gpus": 1, "steps": steps, "warmup": 0, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; no dataset)",
+        "config": {"workload": "step churn: 1M-token workspace, +64 blocks per step, "
+                               "lower tier regenerated on demand by host gather workers",
+                   "steps": steps},
+        "mean_overlap": sum(ovs) / len(ovs) if ovs else None,
+        "mean_hits": sum(r["hits"] for r in later) / len(later),
+        "mean_misses": sum(r["misses"] for r in later) / len(later),
+        "steps_detail": rows,
+        "kernels": {n: {"launches": c, "avg_ms": t / c} for n, (c, t) in prof.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -269,6 +365,9 @@ def main():
     k._abi.lib()
     wl = synth.get_workload(args.workload)
     dev = torch.device("cuda:0")
+    if args.workload == "churn":
+        run_churn(args, k, wl, dev)
+        return
     if args.calibrate_copy:
         # a plain elementwise copy of known size: 2 GiB read + 2 GiB written
         a = torch.ones(1 << 29, dtype=torch.float32, device=dev)

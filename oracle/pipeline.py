@@ -29,12 +29,16 @@ def raw_blocks(wl, which: str, b0: int, nb: int) -> np.ndarray:
     return as_f64(synth.kv_blocks(wl, which, b0, nb), wl.dtype)
 
 
-def index_rows(wl, b0: int, nb: int, chunk: int = 64, threads: int | None = None) -> np.ndarray:
-    """Stored Mean-K of blocks [b0, b0+nb) as float64 [L][Hkv][nb][d]."""
+def index_rows(wl, b0: int, nb: int, chunk: int = 64, threads: int | None = None,
+               out_dtype=np.float64) -> np.ndarray:
+    """Stored Mean-K of blocks [b0, b0+nb) as [L][Hkv][nb][d].
+
+    The stored values are bf16 or fp32 numbers, so out_dtype=np.float32 holds
+    them exactly at half the memory of float64."""
     L, Hkv, d = wl.n_layers, wl.n_kv_heads, wl.head_dim
-    out = np.empty((L, Hkv, nb, d))
+    out = np.empty((L, Hkv, nb, d), dtype=out_dtype)
     if wl.index_direct:
-        return as_f64(synth.index_direct(wl, b0, nb), "bf16")
+        return as_f64(synth.index_direct(wl, b0, nb), "bf16").astype(out_dtype)
     starts = list(range(0, nb, chunk))
 
     def work(s):
@@ -42,7 +46,7 @@ def index_rows(wl, b0: int, nb: int, chunk: int = 64, threads: int | None = None
         m = mean_k(raw_blocks(wl, "K", b0 + s, n), wl.dtype)          # [n][L][Hkv][d]
         out[:, :, s:s + n, :] = np.transpose(m, (1, 2, 0, 3))
 
-    threads = threads or min(8, os.cpu_count() or 1)
+    threads = threads or min(16, os.cpu_count() or 1)
     if threads > 1 and len(starts) > 1:
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(work, starts))

@@ -26,26 +26,36 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 
-def lg_partial_scores(q: np.ndarray, index: np.ndarray, l: int, g: int) -> np.ndarray:
-    """sum over (m, h in group g) of softmax_b(q[l,h,m] . kbar[l,g,b] / sqrt(d)).
-
-    q: [L][Hq][T][d] float64; index: [L][Hkv][N][d] float64. Returns [N]."""
-    L, Hq, T, d = q.shape
-    Hkv = index.shape[1]
-    G = Hq // Hkv
-    rows = q[l, g * G:(g + 1) * G].reshape(G * T, d)       # heads h with h // G == g
-    s = rows @ index[l, g].T / np.sqrt(d)                   # [G*T][N]
+def pair_softmax_sums(rows: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """Column sums over the query rows of one (layer, KV head) of the row-wise
+    softmax of rows . kbar^T / sqrt(d). rows: [G*T][d]; kbar: [N][d]."""
+    rows = np.asarray(rows, dtype=np.float64)
+    kbar = np.asarray(kbar, dtype=np.float64)
+    d = rows.shape[1]
+    s = rows @ kbar.T / np.sqrt(d)                          # [G*T][N]
     s = s - s.max(axis=1, keepdims=True)
     e = np.exp(s)
     p = e / e.sum(axis=1, keepdims=True)                    # softmax over blocks, per row
     return p.sum(axis=0)
 
 
+def lg_partial_scores(q: np.ndarray, index: np.ndarray, l: int, g: int) -> np.ndarray:
+    """sum over (m, h in group g) of softmax_b(q[l,h,m] . kbar[l,g,b] / sqrt(d)).
+
+    q: [L][Hq][T][d]; index: [L][Hkv][N][d]. Returns [N]."""
+    L, Hq, T, d = q.shape
+    Hkv = index.shape[1]
+    G = Hq // Hkv
+    # query heads h with h // G == g share KV head g
+    return pair_softmax_sums(q[l, g * G:(g + 1) * G].reshape(G * T, d), index[l, g])
+
+
 def block_scores(q: np.ndarray, index: np.ndarray, threads: int | None = None,
                  return_partials: bool = False):
-    """R[N] for all blocks; optionally also the [L*Hkv][N] per-(l,g) sums."""
-    q = np.asarray(q, dtype=np.float64)
-    index = np.asarray(index, dtype=np.float64)
+    """R[N] for all blocks; optionally also the [L*Hkv][N] per-(l,g) sums.
+
+    q and index may be float32 arrays holding exact bf16/fp32 values; each
+    (l, g) slice is widened to float64 before use."""
     L, Hq, T, d = q.shape
     Lx, Hkv, N, dx = index.shape
     if Lx != L or dx != d or Hq % Hkv:
@@ -64,3 +74,27 @@ def block_scores(q: np.ndarray, index: np.ndarray, threads: int | None = None,
     if return_partials:
         return R, np.stack(parts)
     return R
+
+
+
+def block_scores_streamed(q: np.ndarray, index_slice, n_kv_heads: int, n_blocks: int,
+                          threads: int | None = None) -> np.ndarray:
+    """The same R[N] as block_scores, for indexes too large to hold at once:
+    index_slice(l, g) returns the [N][d] Mean-K rows of one (layer, KV head);
+    each pair's softmax sums are formed exactly as in lg_partial_scores and the
+    pairs are added in the same (l, g) order."""
+    L, Hq, T, d = q.shape
+    G = Hq // n_kv_heads
+    pairs = [(l, g) for l in range(L) for g in range(n_kv_heads)]
+
+    def one(lg):
+        l, g = lg
+        return pair_softmax_sums(q[l, g * G:(g + 1) * G].reshape(G * T, d), index_slice(l, g))
+
+    threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(threads) as ex:
+        parts = list(ex.map(one, pairs))
+    total = np.zeros(n_blocks)
+    for p in parts:
+        total += p
+    return total / (L * Hq)

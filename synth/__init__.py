@@ -18,4 +18,5 @@ from .generate import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     stream_key,
+    gather_store,
 )

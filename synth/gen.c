@@ -173,25 +173,45 @@ void synth_query(uint64_t seed, int32_t tensor, int32_t L, int32_t Hq, int32_t T
  * offset-plus-noise K (used where the raw K would not fit anywhere):
  * idx(l,g,b,t) = bf16( off_sigma*unit(key(seed, off_tensor, b, l*Hkv+g), t)
  *                      + float32(1/sqrt(32))*unit(key(seed, tensor, b, l*Hkv+g), t) )
- * Row (l,g,b0+i) is written at out + (lg*lg_stride_elems + i*d) elements. */
+ * Rows of (l, g) pairs lg0 .. lg0+n_lg-1 and blocks b0 .. b0+nb-1 are written;
+ * row (lg0+k, b0+i) goes to out + (k*lg_stride_elems + i*d) elements. */
 void synth_index_direct(uint64_t seed, int32_t tensor, int32_t off_tensor, float off_sigma,
-                        int64_t b0, int64_t nb, int32_t L, int32_t Hkv, int32_t d,
+                        int64_t b0, int64_t nb, int64_t lg0, int64_t n_lg, int32_t d,
                         uint16_t* out, int64_t lg_stride_elems, int32_t nthreads) {
-  const int64_t nlg = (int64_t)L * Hkv;
-  const int64_t rows = nlg * nb;
+  const int64_t rows = n_lg * nb;
   const float cs = c_inv_sqrt32();
   if (nthreads < 1) nthreads = 1;
 #pragma omp parallel for schedule(static) num_threads(nthreads)
   for (int64_t r = 0; r < rows; ++r) {
-    const int64_t lg = r / nb, i = r % nb;
+    const int64_t k = r / nb, i = r % nb;
     const uint64_t b = (uint64_t)(b0 + i);
-    const uint64_t kx = synth_key(seed, (uint64_t)tensor, b, (uint64_t)lg);
-    const uint64_t ko = synth_key(seed, (uint64_t)off_tensor, b, (uint64_t)lg);
-    uint16_t* row = out + lg * lg_stride_elems + i * d;
+    const uint64_t lg = (uint64_t)(lg0 + k);
+    const uint64_t kx = synth_key(seed, (uint64_t)tensor, b, lg);
+    const uint64_t ko = synth_key(seed, (uint64_t)off_tensor, b, lg);
+    uint16_t* row = out + k * lg_stride_elems + i * d;
     for (int t = 0; t < d; ++t) {
       float a = off_sigma * unit_at(ko, (uint64_t)t);
       float c = cs * unit_at(kx, (uint64_t)t);
       row[t] = to_bf16(a + c);
     }
   }
+}
+
+/* A host-gather callback over the generator: writes block `block`'s raw K
+ * (which = 0) or V (which = 1) to dst. `user` points to a synth_store. It has
+ * the signature of a lower-tier gather function (int(void*, int64, int32, void*))
+ * so a store that regenerates blocks on demand can stand in for a host tier too
+ * large to materialise. */
+typedef struct {
+  uint64_t seed;
+  float off_sigma;
+  int32_t L, Hkv, B, d, dtype;
+} synth_store;
+
+int synth_gather_kv(void* user, int64_t block, int32_t which, void* dst) {
+  const synth_store* s = (const synth_store*)user;
+  const int64_t bytes = (int64_t)s->L * s->Hkv * s->B * s->d * (s->dtype == 0 ? 4 : 2);
+  synth_kv_blocks(s->seed, which == 0 ? 1 : 2, which == 0 ? 3 : 4, s->off_sigma, block, 1,
+                  s->L, s->Hkv, s->B, s->d, s->dtype, dst, bytes, 1);
+  return 0;
 }

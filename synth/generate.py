@@ -53,7 +53,7 @@ def _load():
             lib.synth_query.restype = None
             lib.synth_query.argtypes = [u64, i32, i32, i32, i32, i32, vp, i32, vp, i32]
             lib.synth_index_direct.restype = None
-            lib.synth_index_direct.argtypes = [u64, i32, i32, f32, i64, i64, i32, i32, i32,
+            lib.synth_index_direct.argtypes = [u64, i32, i32, f32, i64, i64, i64, i64, i32,
                                                vp, i64, i32]
             _lib = lib
     return _lib
@@ -102,6 +102,9 @@ def kv_blocks(wl: Workload, which: str, b0: int, nb: int, out: np.ndarray | None
     return out
 
 
+_shift_cache: dict = {}
+
+
 def churn_shift(wl: Workload, step: int) -> np.ndarray:
     """Query topic u(step) [L][Hq][d] fp32 of the churn workload.
 
@@ -119,10 +122,16 @@ def churn_shift(wl: Workload, step: int) -> np.ndarray:
                 arr[l, h] = unit_stream(stream_key(wl.seed, TENSOR["WSTEP"] + t, l, h), 0, d)
         return arr
 
-    u = (s * w(0)).astype(np.float32)
-    for t in range(1, step + 1):
+    key = (wl.seed, L, Hq, d, wl.topic_rho, wl.topic_scale)
+    t0, u = 0, (s * w(0)).astype(np.float32)
+    for t in range(step, 0, -1):                 # resume from the latest cached step
+        if (key, t) in _shift_cache:
+            t0, u = t, _shift_cache[(key, t)]
+            break
+    for t in range(t0 + 1, step + 1):
         u = (rho * u).astype(np.float32) + (c * w(t)).astype(np.float32)
         u = u.astype(np.float32)
+    _shift_cache[(key, step)] = u
     return u
 
 
@@ -151,17 +160,22 @@ def query(wl: Workload, step: int = 0, shift: np.ndarray | None = None,
 
 
 def index_direct(wl: Workload, b0: int, nb: int, out: np.ndarray | None = None,
-                 lg_stride_elems: int | None = None, nthreads: int | None = None) -> np.ndarray:
-    """A directly drawn bf16 index for blocks [b0, b0+nb): rows (l,g,b).
+                 lg_stride_elems: int | None = None, nthreads: int | None = None,
+                 lg0: int = 0, n_lg: int | None = None) -> np.ndarray:
+    """A directly drawn bf16 index for blocks [b0, b0+nb) of (l, g) pairs
+    [lg0, lg0+n_lg) (all pairs by default), rows flattened as l*Hkv + g.
 
-    Default layout [L][Hkv][nb][d]; pass ``out``/``lg_stride_elems`` to write
-    into a larger [L][Hkv][cap][d] buffer or a tile."""
+    Default layout [L][Hkv][nb][d] (or [n_lg][nb][d] for a pair range); pass
+    ``out``/``lg_stride_elems`` to write into a larger buffer or a tile."""
     L, Hkv, d = wl.n_layers, wl.n_kv_heads, wl.head_dim
+    all_pairs = n_lg is None
+    n_lg = L * Hkv if all_pairs else n_lg
     if out is None:
-        out = np.empty((L, Hkv, nb, d), dtype=np.uint16)
+        shape = (L, Hkv, nb, d) if all_pairs and lg0 == 0 else (n_lg, nb, d)
+        out = np.empty(shape, dtype=np.uint16)
         lg_stride_elems = nb * d
     _load().synth_index_direct(wl.seed, TENSOR["IDX"], TENSOR["KOFF"], wl.off_sigma, b0, nb,
-                               L, Hkv, d, _ptr(out), lg_stride_elems,
+                               lg0, n_lg, d, _ptr(out), lg_stride_elems,
                                nthreads or default_threads())
     return out
 
@@ -188,3 +202,20 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     u = u + 0x7FFF + ((u >> 16) & 1)
     return (u >> 16).astype(np.uint16)
+
+
+class _Store(ctypes.Structure):
+    _fields_ = [("seed", ctypes.c_uint64), ("off_sigma", ctypes.c_float),
+                ("L", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("B", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def gather_store(wl: Workload):
+    """(C function pointer, user pointer, keep-alive) of a generator-backed
+    lower tier: the function writes any block's raw K or V on demand."""
+    assert TENSOR["K"] == 1 and TENSOR["V"] == 2 and TENSOR["KOFF"] == 3 and TENSOR["VOFF"] == 4
+    lib = _load()
+    st = _Store(wl.seed, wl.off_sigma, wl.n_layers, wl.n_kv_heads, wl.block_tokens,
+                wl.head_dim, _dtype_code(wl.dtype))
+    fn = ctypes.cast(lib.synth_gather_kv, ctypes.c_void_p).value
+    return fn, ctypes.addressof(st), st

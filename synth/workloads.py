@@ -102,6 +102,10 @@ WORKLOADS = {
                       off_sigma=0.5, steps=32, append_blocks=64,
                       topic_rho=0.9, topic_scale=0.35, reserve_blocks=2048),
 }
+# The churn workspace with 4 layers and 8 steps: the same history, queries,
+# budget and step structure at 1/16 of the scoring work, so the CPU oracle can
+# produce every step's expected selection.
+WORKLOADS["churn_l4"] = WORKLOADS["churn"].scaled(name="churn_l4", n_layers=4, steps=8)
 
 
 def get_workload(name: str) -> Workload:

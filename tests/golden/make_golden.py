@@ -1,0 +1,80 @@
+"""Write the oracle's expected values for the full-size workspaces.
+
+Calls only the CPU oracle (which draws its inputs from the seeded generator).
+Usage: python tests/golden/make_golden.py ws1m|ws10m|churn [threads]
+Outputs tests/golden/<name>_oracle.npz.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import synth  # noqa: E402
+from oracle import pipeline as op  # noqa: E402
+from oracle.scores import block_scores, block_scores_streamed  # noqa: E402
+from oracle.select import select_blocks, cutoff_margin  # noqa: E402
+
+
+def one_step(wl, index, step, threads):
+    q = op.query_f64(wl, step, index).astype(np.float32)       # exact bf16 values
+    R = block_scores(q, index, threads=threads)
+    sel = select_blocks(R, wl.n_sink, wl.n_recent, wl.budget_blocks)
+    return R, sel, cutoff_margin(R, wl.n_sink, wl.n_recent, wl.budget_blocks)
+
+
+def main():
+    name = sys.argv[1]
+    threads = int(sys.argv[2]) if len(sys.argv) > 2 else 8
+    wl = synth.get_workload(name)
+    t0 = time.time()
+    out = {}
+    if name == "ws10m":
+        # the 41 GB index is drawn one (layer, KV head) slice at a time
+        q = op.query_f64(wl, 0)
+        Hkv = wl.n_kv_heads
+
+        def slice_fn(l, g):
+            return op.as_f64(synth.index_direct(wl, 0, wl.n_blocks, lg0=l * Hkv + g, n_lg=1,
+                                                nthreads=2)[0], "bf16")
+        R = block_scores_streamed(q, slice_fn, Hkv, wl.n_blocks, threads=threads)
+        sel = select_blocks(R, wl.n_sink, wl.n_recent, wl.budget_blocks)
+        out.update(R=R, sel=sel,
+                   margin=np.float64(cutoff_margin(R, wl.n_sink, wl.n_recent, wl.budget_blocks)))
+    elif name == "ws1m":
+        index = op.index_rows(wl, 0, wl.n_blocks, threads=threads, out_dtype=np.float32)
+        print(f"index {time.time() - t0:.0f}s", flush=True)
+        R, sel, margin = one_step(wl, index, 0, threads)
+        out.update(R=R, sel=sel, margin=np.float64(margin))
+        # Mean-K of a few sampled blocks, for the full-size build check
+        rng = np.random.default_rng(7)
+        blocks = np.sort(rng.choice(wl.n_blocks, 16, replace=False))
+        out.update(sample_blocks=blocks, sample_index=index[:, :, blocks, :])
+    elif name.startswith("churn"):
+        # every step: append the step's blocks, score with the step's queries
+        N_end = wl.final_blocks
+        index = op.index_rows(wl, 0, N_end, threads=threads, out_dtype=np.float32)
+        print(f"index {time.time() - t0:.0f}s", flush=True)
+        rng = np.random.default_rng(11)
+        sels, margins, samples, sampleR, sums = [], [], [], [], []
+        for t in range(wl.steps):
+            N = wl.n_blocks + t * wl.append_blocks
+            R, sel, margin = one_step(wl, index[:, :, :N, :], t, threads)
+            pick = np.sort(rng.choice(N, 1024, replace=False))
+            sels.append(sel.astype(np.int32))
+            margins.append(margin)
+            samples.append(pick)
+            sampleR.append(R[pick])
+            sums.append(R.sum())
+            print(f"step {t}: {time.time() - t0:.0f}s margin {margin:.2e}", flush=True)
+        out.update(sel=np.stack(sels), margin=np.array(margins), sample_blocks=np.stack(samples),
+                   sample_R=np.stack(sampleR), R_sum=np.array(sums))
+    print(f"done {time.time() - t0:.0f}s", flush=True)
+    np.savez_compressed(os.path.join(HERE, f"{name}_oracle.npz"), **out)
+
+
+if __name__ == "__main__":
+    main()

@@ -119,3 +119,48 @@ def check_view(wl, sel: np.ndarray, page: np.ndarray, pool: Pool, blocks=None, a
         vb = to_host_bits(pool.v_view[slot])
         assert np.array_equal(vb, expected_view_v_bits(wl, b).ravel()), f"V of block {b}"
     return worst
+
+
+def build_index_streamed(k, wl, dev, n_blocks=None, chunk: int = 1024, cap=None):
+    """Mean-K of blocks [0, n_blocks) built on the device from raw K that is
+    generated on the host chunk by chunk (double-buffered pinned staging)."""
+    import threading
+    import torch
+    N = n_blocks or wl.n_blocks
+    cap = cap or N
+    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim), dtype=torch_dtype(wl),
+                        device=dev)
+    stage = [torch.empty((chunk, wl.block_elems), dtype=torch_dtype(wl)).pin_memory()
+             for _ in range(2)]
+    dchunk = torch.empty((chunk, wl.block_elems), dtype=torch_dtype(wl), device=dev)
+    starts = list(range(0, N, chunk))
+    view = (lambda t: t.numpy().view(np.uint16)) if wl.dtype == "bf16" else (lambda t: t.numpy())
+
+    def gen(i):
+        s = starts[i]
+        n = min(chunk, N - s)
+        synth.kv_blocks(wl, "K", s, n, out=view(stage[i & 1])[:n])
+
+    th = threading.Thread(target=gen, args=(0,))
+    th.start()
+    for i, s in enumerate(starts):
+        th.join()
+        n = min(chunk, N - s)
+        dchunk[:n].copy_(stage[i & 1][:n])
+        if i + 1 < len(starts):
+            th = threading.Thread(target=gen, args=(i + 1,))
+            th.start()
+        k.kvm_build_index(k.dims_for(wl), k.dtype_code(wl.dtype), dchunk, wl.block_bytes, s, n,
+                          index, cap)
+        torch.cuda.synchronize()
+    return index
+
+
+def raw_blocks_to_device(wl, which: str, blocks, dev):
+    """Raw K or V of an arbitrary list of blocks as one device tensor."""
+    import torch
+    h = torch.empty((len(blocks), wl.block_elems), dtype=torch_dtype(wl)).pin_memory()
+    view = h.numpy().view(np.uint16) if wl.dtype == "bf16" else h.numpy()
+    for i, b in enumerate(blocks):
+        synth.kv_blocks(wl, which, int(b), 1, out=view[i:i + 1])
+    return h.to(dev)

@@ -1,0 +1,131 @@
+"""GPU parity at the full workspace sizes, in the launch configuration the
+benchmark times. Expected values come from tests/golden/make_golden.py (the CPU
+oracle); K/V pages are checked on sampled blocks against the oracle's re-RoPE.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import compact_positions
+from oracle.pipeline import as_f64
+from tests import gpu_common as gc
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def golden(name):
+    path = os.path.join(HERE, "golden", f"{name}_oracle.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return np.load(path)
+
+
+@pytest.fixture(scope="module")
+def k():
+    import torch
+    import attention_space_block_amd as kvm
+    assert torch.cuda.is_available()
+    kvm._abi.lib()
+    return kvm
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.timeout(600)
+def test_ws1m_full_step(k, dev):
+    import torch
+    g = golden("ws1m")
+    wl = synth.get_workload("ws1m")
+    N, B = wl.n_blocks, wl.block_tokens
+    say("ws1m: building the 1M-token index on the device")
+    index = gc.build_index_streamed(k, wl, dev)
+    blocks = g["sample_blocks"]
+    got = gc.to_host_bits(index[:, :, torch.as_tensor(blocks, device=dev), :])
+    assert np.array_equal(gc.as_f64(got), g["sample_index"].astype(np.float64))
+    say("ws1m: scoring")
+    q = gc.to_dev(synth.query(wl), dev)
+    scores = gc.score_dev(k, wl, q, index, N, N, dev)
+    R = scores.cpu().numpy().astype(np.float64)
+    rel = np.abs(R - g["R"]) / g["R"]
+    say("max rel err", rel.max(), "sum", R.sum(), "margin", float(g["margin"]))
+    assert rel.max() <= 1e-5
+    sel, n_sel, base = gc.select_dev(k, scores, N, wl.n_sink, wl.n_recent, wl.budget_blocks, dev)
+    n = int(n_sel.item())
+    s = sel.cpu().numpy()[:n]
+    assert n == wl.budget_blocks
+    if float(g["margin"]) > 1e-5:
+        assert np.array_equal(s, g["sel"])
+    assert np.array_equal(base.cpu().numpy()[:n], compact_positions(n))
+    del index
+    say("ws1m: rematerializing (half resident, half from HBM sources)")
+    hits, misses = s[0::2], s[1::2]
+    pool = gc.Pool(k, wl, n + 64, N, (n + wl.reserve_blocks) * B, dev)
+    hk = gc.raw_blocks_to_device(wl, "K", hits, dev)
+    hv = gc.raw_blocks_to_device(wl, "V", hits, dev)
+    for i, b in enumerate(hits):
+        pool.ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv[i], wl.block_bytes)
+    del hk, hv
+    mk = gc.raw_blocks_to_device(wl, "K", misses, dev)
+    mv = gc.raw_blocks_to_device(wl, "V", misses, dev)
+    for i, b in enumerate(misses):
+        pool.ctx.kvm_ctx_set_source(int(b), 1, mk[i], mv[i], wl.block_bytes, k.KVM_SRC_DEVICE)
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    assert st["hits"] == len(hits) and st["misses"] == len(misses) and st["rotated"] == n
+    pg = pool.page.cpu().numpy()[:n]
+    assert len(set(pg.tolist())) == n
+    rng = np.random.default_rng(3)
+    check = sorted(set(rng.choice(n, 24, replace=False).tolist()) | {0, n - 1})
+    worst = gc.check_view(wl, s, pg, pool, blocks=check)
+    say("worst K error", worst)
+    pool.ctx.close()
+
+
+@pytest.mark.timeout(600)
+def test_ws10m_scores_resident_and_host_tiled(k, dev):
+    import torch
+    g = golden("ws10m")
+    wl = synth.get_workload("ws10m")
+    N, tb, d = wl.n_blocks, wl.tile_blocks, wl.head_dim
+    nlg = wl.n_layers * wl.n_kv_heads
+    ntile = (N + tb - 1) // tb
+    say("ws10m: drawing the 41 GB index into pinned tiles")
+    host = torch.empty((ntile, nlg, tb, d), dtype=torch.int16).pin_memory()
+    hv = host.numpy().view(np.uint16)
+    for t in range(ntile):
+        nb = min(tb, N - t * tb)
+        synth.index_direct(wl, t * tb, nb, out=hv[t], lg_stride_elems=tb * d)
+    say("ws10m: device copy of the index")
+    index = torch.empty((wl.n_layers, wl.n_kv_heads, N, d), dtype=torch.int16, device=dev)
+    iv = index.view(nlg, N, d)
+    for t in range(ntile):
+        nb = min(tb, N - t * tb)
+        iv[:, t * tb:t * tb + nb, :].copy_(host[t, :, :nb, :].to(dev, non_blocking=False))
+    q = gc.to_dev(synth.query(wl), dev)
+    say("ws10m: scoring, index in HBM")
+    res = gc.score_dev(k, wl, q, index, N, N, dev).cpu().numpy()
+    del index, iv
+    say("ws10m: scoring, index streamed from pinned host tiles")
+    til = gc.score_dev(k, wl, q, None, N, N, dev, loc=1, tile_blocks=tb, host_index=host)
+    til = til.cpu().numpy()
+    assert np.array_equal(res, til)
+    rel = np.abs(res.astype(np.float64) - g["R"]) / g["R"]
+    say("max rel err", rel.max(), "margin", float(g["margin"]))
+    assert rel.max() <= 1e-5
+    sel, n_sel, base = gc.select_dev(k, torch.from_numpy(res).to(dev), N, wl.n_sink,
+                                     wl.n_recent, wl.budget_blocks, dev)
+    n = int(n_sel.item())
+    assert n == wl.budget_blocks
+    if float(g["margin"]) > 1e-5:
+        assert np.array_equal(sel.cpu().numpy()[:n], g["sel"])

@@ -60,3 +60,15 @@ def test_churn_topic_is_deterministic_ar1():
     u1 = synth.churn_shift(wl, 1)
     c = np.corrcoef(u1.ravel(), u2.ravel())[0, 1]
     assert 0.8 < c < 0.97
+
+
+def test_gather_store_writes_the_generated_block():
+    import ctypes
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    fn, user, keep = synth.gather_store(wl)
+    f = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                         ctypes.c_void_p)(fn)
+    for which, name in ((0, "K"), (1, "V")):
+        buf = np.empty(wl.block_elems, np.uint16)
+        assert f(user, 1234, which, buf.ctypes.data) == 0
+        assert np.array_equal(buf, synth.kv_blocks(wl, name, 1234, 1).ravel())
