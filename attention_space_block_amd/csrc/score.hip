@@ -10,7 +10,10 @@
 // Q_g[TG x d] * Kbar^T[d x N] on v_mfma_f32_32x32x16_bf16. The per-row softmax
 // needs each row's log-sum-exp before any block's share is known, so:
 //   pass 1: rows stationary in registers (B operand), Mean-K tiles streamed
-//           through double-buffered LDS (A operand); the 32x32 result puts one
+//           through double-buffered LDS (A operand) with direct global->LDS
+//           copies (global_load_lds_dwordx4: no staging registers, no LDS
+//           store instructions; 16-byte pieces XOR-swizzled per row so the
+//           operand reads are bank-conflict free); the 32x32 result puts one
 //           query row in each lane (16 blocks per lane), so the running max /
 //           sum-exp is lane-local: a tile max, one rescale exp per tile and
 //           16 exps; tile sums folded in fp32, the running sum kept in fp64.
@@ -54,7 +57,7 @@ template <int D>
 struct MfmaShape {
   static constexpr int KS = D / 16;               // MFMA k-steps
   static constexpr int ROW_B = D * 2;             // bytes of one bf16 row
-  static constexpr int LDS_ROW = ROW_B + 16;      // padded LDS row (bank spread)
+  static constexpr int LDS_ROW = ROW_B;           // rows unpadded; 16-byte pieces XOR-swizzled
   static constexpr int TILE = 64;                 // rows staged per iteration
   static constexpr int SUB = TILE / 32;           // 32-row subtiles per stage
   static constexpr int LOADS = TILE * ROW_B / (256 * 16);  // 16-B loads per thread
@@ -76,6 +79,18 @@ struct Pass1Args {
   uint32_t total_wg;        // padded to a multiple of 8
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// One wave-wide direct global->LDS copy: lane L's 16 bytes land at dst + 16*L.
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)lds_dst, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Interleave hint for the scheduler: one MFMA, then `valu` VALU instructions,
 // `n` times, so the matrix pipe and the VALU work on different subtiles at
 // once inside one wavefront.
@@ -91,12 +106,12 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // 32 rows of the staged LDS tile (A operand, one 16-byte piece per lane and
 // k-step) times the wave's two stationary B tiles.
 template <int KS>
-__device__ __forceinline__ void mfma_subtile(f32x16 (&acc)[2], const char* arow,
+__device__ __forceinline__ void mfma_subtile(f32x16 (&acc)[2], const char* arow, int half, int xr,
                                              const bf16x8 (&bop)[2][KS]) {
   bf16x8 av[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + ks * 32));
+    av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((ks * 2 + half) ^ xr) << 4)));
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -181,40 +196,23 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   float m_run[2] = {-INFINITY, -INFINITY};
   double s_run[2] = {0.0, 0.0};
 
-  uint4 stage[S::LOADS];
-  auto gload = [&](int tile) {
+  // Direct global->LDS tile copy: slot S (16 bytes) of the tile receives
+  // piece (S & 15) ^ (row & 15) of row S >> 4, so the MFMA operand reads below
+  // (row r, piece c at (c ^ (r & 15))) hit distinct banks. Rows past the end
+  // re-read the last valid row (finite values, masked to -inf later).
+  auto dma_tile = [&](int tile, int buf) {
     const int32_t t0 = b_begin + tile * S::TILE;
-    if (t0 + S::TILE <= b_end) {
-#pragma unroll
-      for (int i = 0; i < S::LOADS; ++i) {
-        const int e = (i * 256 + threadIdx.x);      // 16-B piece id in the tile
-        const int r = e / (S::ROW_B / 16);
-        const int c = e % (S::ROW_B / 16);
-        stage[i] = *reinterpret_cast<const uint4*>(kb + (int64_t)(t0 + r) * D + c * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::LOADS; ++i) {
-        const int e = (i * 256 + threadIdx.x);
-        const int r = e / (S::ROW_B / 16);
-        const int c = e % (S::ROW_B / 16);
-        const int32_t b = t0 + r;
-        stage[i] = b < b_end ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + c * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < S::LOADS; ++i) {
-      const int e = (i * 256 + threadIdx.x);
-      const int r = e / (S::ROW_B / 16);
-      const int c = e % (S::ROW_B / 16);
-      *reinterpret_cast<uint4*>(&lds[buf][r * S::LDS_ROW + c * 16]) = stage[i];
+      const int slot = (i * 4 + wave) * 64 + lane;
+      const int r = slot >> 4;
+      const int c = (slot & 15) ^ (r & 15);
+      const int32_t b = t0 + r < b_end ? t0 + r : b_end - 1;
+      dma16(kb + (int64_t)b * D + c * 8, &lds[buf][(i * 4 + wave) * 1024]);
     }
   };
   auto arow = [&](int buf, int sub) -> const char* {
-    return &lds[buf][(sub * 32 + col) * S::LDS_ROW + half * 16];
+    return &lds[buf][(sub * 32 + col) * S::LDS_ROW];
   };
   auto update = [&](f32x16 (&acc)[2], int32_t nvalid) {
     if (nvalid < 32) mask_rows(acc, half, nvalid);   // uniform: only a split's last tile
@@ -225,22 +223,21 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   // A stage holds SUB subtiles of 32 blocks; the next stage's global loads
   // are in flight while all of them are multiplied and reduced.
   f32x16 acc[2];
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  const int xr = col & 15;
+  if (ntiles > 0) dma_tile(0, 0);
+  wait_dma();
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int32_t t0 = b_begin + it * S::TILE;
     const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
+    if (more) dma_tile(it + 1, buf ^ 1);
 #pragma unroll 1
     for (int sub = 0; sub < S::SUB; ++sub) {
-      mfma_subtile<S::KS>(acc, arow(buf, sub), bq);
+      mfma_subtile<S::KS>(acc, arow(buf, sub), half, xr, bq);
       update(acc, b_end - (t0 + 32 * sub));
     }
-    if (more) lstore(buf ^ 1);
+    wait_dma();
     __syncthreads();
   }
   // Merge the two lane halves (same query row, disjoint blocks).
@@ -339,53 +336,22 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   }
   const float* lse_lg = a.lse + (int64_t)lg * a.TGp;
   const int32_t ntiles = (a.TG + S::TILE - 1) / S::TILE;
-  uint4 stage[S::LOADS];
-  float lstage = 0.0f;
-  auto gload = [&](int tile) {
+  // Query rows of (l, g) are contiguous: heads g*G .. g*G+G-1, tokens 0..T-1.
+  const uint16_t* qg = a.q + ((int64_t)l * a.Hq + (int64_t)g * a.G) * a.T * D;
+  auto dma_tile = [&](int tile, int buf) {
     const int32_t r0 = tile * S::TILE;
-    if (r0 + S::TILE <= a.TG) {
-#pragma unroll
-      for (int i = 0; i < S::LOADS; ++i) {
-        const int e = (i * 256 + threadIdx.x);
-        const int r = e / (S::ROW_B / 16);
-        const int c = e % (S::ROW_B / 16);
-        const int32_t rho = r0 + r;
-        const int hh = g * a.G + rho / a.T;
-        const int m = rho % a.T;
-        stage[i] = *reinterpret_cast<const uint4*>(
-            a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + c * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < S::LOADS; ++i) {
-        const int e = (i * 256 + threadIdx.x);
-        const int r = e / (S::ROW_B / 16);
-        const int c = e % (S::ROW_B / 16);
-        const int32_t rho = r0 + r;
-        if (rho < a.TG) {
-          const int hh = g * a.G + rho / a.T;
-          const int m = rho % a.T;
-          stage[i] = *reinterpret_cast<const uint4*>(
-              a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + c * 8);
-        } else {
-          stage[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-    if (threadIdx.x < S::TILE) lstage = lse_lg[r0 + threadIdx.x];
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < S::LOADS; ++i) {
-      const int e = (i * 256 + threadIdx.x);
-      const int r = e / (S::ROW_B / 16);
-      const int c = e % (S::ROW_B / 16);
-      *reinterpret_cast<uint4*>(&lds[buf][r * S::LDS_ROW + c * 16]) = stage[i];
+      const int slot = (i * 4 + wave) * 64 + lane;
+      const int r = slot >> 4;
+      const int c = (slot & 15) ^ (r & 15);
+      const int32_t rho = r0 + r < a.TG ? r0 + r : a.TG - 1;  // padded rows: lse = +inf
+      dma16(qg + (int64_t)rho * D + c * 8, &lds[buf][(i * 4 + wave) * 1024]);
     }
-    if (threadIdx.x < S::TILE) lse_s[buf][threadIdx.x] = lstage;
+    if (wave == 0) dma4(lse_lg + r0 + lane, &lse_s[buf][0]);
   };
   auto arow = [&](int buf, int sub) -> const char* {
-    return &lds[buf][(sub * 32 + col) * S::LDS_ROW + half * 16];
+    return &lds[buf][(sub * 32 + col) * S::LDS_ROW];
   };
   // LSE of the 16 rows a lane holds in a subtile: rows 8*q4 + 4*half + 0..3.
   auto load_lse = [&](float (&ls)[16], int buf, int sub) {
@@ -402,21 +368,22 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   double colsum[2] = {0.0, 0.0};
   f32x16 acc[2];
   float ls[16];
-  gload(0);
-  lstore(0);
+  const int xr = col & 15;
+  dma_tile(0, 0);
+  wait_dma();
   __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const bool more = it + 1 < ntiles;
-    if (more) gload(it + 1);
+    if (more) dma_tile(it + 1, buf ^ 1);
 #pragma unroll 1
     for (int sub = 0; sub < S::SUB; ++sub) {
-      mfma_subtile<S::KS>(acc, arow(buf, sub), bk);
+      mfma_subtile<S::KS>(acc, arow(buf, sub), half, xr, bk);
       load_lse(ls, buf, sub);
       colsum_update(acc[0], ls, a.scale, colsum[0]);
       colsum_update(acc[1], ls, a.scale, colsum[1]);
     }
-    if (more) lstore(buf ^ 1);
+    wait_dma();
     __syncthreads();
   }
 #pragma unroll
