@@ -6,10 +6,12 @@
 // from. The kernel reads raw K, rotates every (x_a, x_b) pair by the angle
 // p * theta_t with cos/sin from a precomputed fp32 table (angles formed in
 // float64 on the host), and writes bf16/fp32 K (one round-to-nearest-even)
-// into the page's K view; for device-resident sources it also writes the raw
-// K shadow and copies V verbatim. Pages are contiguous [L][Hkv][B][d] spans, so
-// every job is a long coalesced stream: HBM-bound, 2 x page bytes per rotated
-// block (plus 3 x page bytes when V and the shadow are written too).
+// into the page's K view; for device-resident sources it also copies V
+// verbatim. Pages are contiguous [L][Hkv][B][d] spans, so every job is a long
+// coalesced stream: HBM-bound, 2 x page bytes per rotated block (plus 2 x page
+// bytes when V is copied). Raw K is read where it already sits in HBM: the
+// page's shadow (filled by DMA, gather or registration) or the block's
+// device-resident lower-tier copy.
 //
 // Host side: the planner turns a selection into hits, misses and evictions
 // over the bounded page pool (LRU among pages outside the new view), stages
@@ -39,7 +41,7 @@ struct RematJob {
   int32_t flags;
   int32_t pad;
 };
-enum { JOB_WRITE_SHADOW = 1, JOB_COPY_V = 2 };
+enum { JOB_COPY_V = 2 };
 
 // (l, g) units of 32 token rows handled by one workgroup
 static constexpr int REMAT_UNITS = 4;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int ROWS = REMAT_UNITS * 32;         // rows per workgroup
   constexpr int NR = ROWS / RPI;                 // rows per thread
   constexpr int NJ = RPI >= 32 ? 1 : 32 / RPI;   // distinct token indices per thread
-  constexpr int NC = LAYOUT == 0 ? P : P;        // (cos, sin) pairs per piece pair
+  constexpr int NC = P;                          // (cos, sin) pairs per piece pair
   const int32_t jid = blockIdx.x / a.wg_per_job;
   const int32_t wpart = blockIdx.x % a.wg_per_job;
   if (jid >= a.n_jobs) return;
@@ -132,7 +134,6 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   }
   const int64_t page = (int64_t)job.slot * a.page_bytes;
   const int64_t row0 = (int64_t)wpart * ROWS;
-  const bool wshadow = (job.flags & JOB_WRITE_SHADOW) != 0;
   const bool copyv = (job.flags & JOB_COPY_V) != 0;
   uint4 k0[NR], k1[NR], v0[NR], v1[NR];
 #pragma unroll
@@ -147,7 +148,6 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
     }
   }
   char* kv = a.k_view + page;
-  char* sh = a.k_shadow + page;
   char* vv = a.v_view + page;
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
@@ -177,10 +177,6 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
     }
     st_plain(kv + b0, pack<T>(y0));
     st_plain(kv + b1, pack<T>(y1));
-    if (wshadow) {
-      st_plain(sh + b0, k0[u]);
-      st_plain(sh + b1, k1[u]);
-    }
     if (copyv) {
       st_plain(vv + b0, v0[u]);
       st_plain(vv + b1, v1[u]);
@@ -216,6 +212,7 @@ struct BlockRec {
   int32_t gather = -1;       // index into ctx->gathers for gathered sources
   const char* src_k = nullptr;
   const char* src_v = nullptr;
+  bool raw_in_shadow = false;  // the page's shadow holds the raw K (else the device source)
 };
 
 struct Gather {
@@ -346,10 +343,21 @@ static int32_t take_slot(kvm_ctx* c, std::vector<std::pair<int64_t, int32_t>>& l
     if (r.last_used >= c->step) continue;  // in the new view
     r.slot = -1;
     r.baked = -1;
+    r.raw_in_shadow = false;
     ++*evicted;
     return s;
   }
   return -1;
+}
+
+// A resident page whose re-encode source is the block's device-resident
+// lower-tier copy must not outlive a change of that source: reclaim it.
+static void release_if_unbacked(kvm_ctx* c, BlockRec& r) {
+  if (r.slot < 0 || r.raw_in_shadow) return;
+  c->slot_block[r.slot] = -1;
+  c->free_slots.push_back(r.slot);
+  r.slot = -1;
+  r.baked = -1;
 }
 
 }  // namespace kvm
@@ -448,6 +456,7 @@ extern "C" int kvm_ctx_set_source(kvm_ctx* c, int64_t first_block, int64_t n_blo
   }
   for (int64_t i = 0; i < n_blocks; ++i) {
     BlockRec& r = c->rec[first_block + i];
+    release_if_unbacked(c, r);
     r.src = loc;
     r.gather = -1;
     r.src_k = loc == KVM_SRC_NONE ? nullptr : (const char*)k_base + i * block_stride;
@@ -480,6 +489,7 @@ extern "C" int kvm_ctx_set_gather(kvm_ctx* c, int64_t first_block, int64_t n_blo
   const int32_t gid = (int32_t)c->gathers.size() - 1;
   for (int64_t i = 0; i < n_blocks; ++i) {
     BlockRec& r = c->rec[first_block + i];
+    release_if_unbacked(c, r);
     r.src = KVM_SRC_HOST_PINNED;
     r.gather = gid;
     r.src_k = nullptr;
@@ -527,8 +537,8 @@ extern "C" int kvm_ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_
     }
     r.baked = -1;
     r.last_used = c->step;
-    KVM_HIP(hipMemcpyAsync(c->d.k_shadow ? (char*)c->d.k_shadow + (int64_t)sl * c->page_bytes
-                                         : nullptr,
+    r.raw_in_shadow = true;
+    KVM_HIP(hipMemcpyAsync((char*)c->d.k_shadow + (int64_t)sl * c->page_bytes,
                            (const char*)k_raw + i * block_stride, c->page_bytes,
                            hipMemcpyDeviceToDevice, s));
     KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)sl * c->page_bytes,
@@ -551,6 +561,7 @@ extern "C" int kvm_ctx_evict(kvm_ctx* c, int64_t first_block, int64_t n_blocks) 
     c->free_slots.push_back(r.slot);
     r.slot = -1;
     r.baked = -1;
+    r.raw_in_shadow = false;
   }
   return KVM_OK;
 }
@@ -635,8 +646,12 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       ++st.hits;
       c->h_page[i] = r.slot;
       if (r.baked != pos) {
-        J[nj] = RematJob{(const char*)c->d.k_shadow + (int64_t)r.slot * c->page_bytes, nullptr,
-                         r.slot, pos, 0, 0};
+        // re-encode from the raw K kept in HBM: the page's shadow, or the
+        // block's device-resident lower-tier copy
+        const char* raw = r.raw_in_shadow
+                              ? (const char*)c->d.k_shadow + (int64_t)r.slot * c->page_bytes
+                              : r.src_k;
+        J[nj] = RematJob{raw, nullptr, r.slot, pos, 0, 0};
         hit_jobs.push_back(nj++);
         r.baked = pos;
       }
@@ -653,9 +668,13 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     r.baked = pos;
     c->h_page[i] = sl;
     if (r.src == KVM_SRC_DEVICE) {
-      J[nj] = RematJob{r.src_k, r.src_v, sl, pos, JOB_WRITE_SHADOW | JOB_COPY_V, 0};
+      // the lower-tier copy is already in HBM: rotate from it, copy V, and
+      // keep reading it for later re-encodes (no shadow copy)
+      J[nj] = RematJob{r.src_k, r.src_v, sl, pos, JOB_COPY_V, 0};
+      r.raw_in_shadow = false;
       dev_jobs.push_back(nj++);
     } else {
+      r.raw_in_shadow = true;
       J[nj] = RematJob{(const char*)c->d.k_shadow + (int64_t)sl * c->page_bytes, nullptr, sl,
                        pos, 0, (int32_t)i};
       if (r.gather >= 0) gather_miss.push_back(nj++);
@@ -697,7 +716,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   int rc = launch_range(0, n_first);
   if (rc) return rc;
   st.d2d_bytes += (int64_t)hit_jobs.size() * 2 * c->page_bytes +
-                  (int64_t)dev_jobs.size() * 5 * c->page_bytes;
+                  (int64_t)dev_jobs.size() * 4 * c->page_bytes;
   // 5. Misses from pinned host memory: DMA straight into the pages, batched.
   const int32_t bb = c->d.batch_blocks;
   int32_t cursor = n_first;

@@ -413,7 +413,7 @@ def main():
     flops_pass = 2.0 * L * Hq * T * N * d
     page = wl.block_bytes
     nh, nm = len(ws.hits), len(ws.misses)
-    remat_bytes = nh * 2 * page + nm * 5 * page
+    remat_bytes = nh * 2 * page + nm * 4 * page
     remat = kern.get("remat")
     remat_gbps = remat_bytes / (remat["avg_ms"] * 1e-3) / 1e9 if remat else None
     # dominant kernel of the step

@@ -147,8 +147,10 @@ int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_
  * Pool (caller-owned device memory, n_slots pages each [L][Hkv][B][d] in dtype):
  *   k_view    K encoded at the block's current compact position (what attention reads)
  *   v_view    V, a verbatim copy of the block's raw V
- *   k_shadow  the block's raw pre-RoPE K (the reconstruction source for hits
- *             whose compact position changes)
+ *   k_shadow  the block's raw pre-RoPE K when its lower-tier copy is not in
+ *             device memory (the re-encode source for hits whose compact
+ *             position changes); blocks with a KVM_SRC_DEVICE copy are
+ *             re-encoded from that copy instead
  * The ctx owns only host-side state, a side stream, events, a pinned staging
  * ring, a small device job list and the RoPE cos/sin table (fp64 angles,
  * rounded to fp32; positions [0, max_pos)). */
@@ -193,7 +195,10 @@ void kvm_ctx_destroy(kvm_ctx* ctx);
  * block first_block+i has raw K at (char*)k_base + i*block_stride and raw V at
  * (char*)v_base + i*block_stride, in pinned host memory (KVM_SRC_HOST_PINNED,
  * staged by DMA straight into the destination page) or device memory
- * (KVM_SRC_DEVICE, read by the remat kernel directly). */
+ * (KVM_SRC_DEVICE, read by the remat kernel directly, also for later
+ * re-encodes while the block stays resident: the memory must stay valid until
+ * the block's source is changed or the ctx is destroyed). Changing the source
+ * of a resident block that relies on its device copy reclaims its page. */
 int kvm_ctx_set_source(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks, const void* k_base,
                        const void* v_base, int64_t block_stride, int32_t loc);
 

@@ -284,3 +284,28 @@ def test_end_to_end_step(k, dev, name):
     blocks = range(n) if n <= 64 else sorted(set(np.linspace(0, n - 1, 48).astype(int)))
     gc.check_view(wl, s, pg, pool, blocks=blocks)
     pool.ctx.close()
+
+
+def test_device_backed_page_released_when_source_changes(k, dev):
+    import torch
+    wl = synth.get_workload("tiny")
+    pool, keep = _remat_setup(k, dev, wl, 128, 16)        # device-resident sources
+    sel = torch.tensor(list(range(11)), dtype=torch.int32, device=dev)
+    n_sel = torch.tensor([11], dtype=torch.int32, device=dev)
+    pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    assert pool.ctx.kvm_ctx_block_state(3)[0] >= 0
+    # block 3's page is re-encoded from its device copy; moving the copy reclaims it
+    rk, rv = keep
+    k3, v3 = rk[3].clone(), rv[3].clone()            # same block, new location
+    pool.ctx.kvm_ctx_set_source(3, 1, k3, v3, wl.block_bytes, k.KVM_SRC_DEVICE)
+    assert pool.ctx.kvm_ctx_block_state(3)[0] == -1
+    # a registered (shadow-backed) block keeps its page when its source changes
+    pool.ctx.kvm_ctx_register_resident(50, 1, rk[50], rv[50], wl.block_bytes)
+    pool.ctx.kvm_ctx_set_source(50, 1, rk[50], rv[50], wl.block_bytes, k.KVM_SRC_DEVICE)
+    assert pool.ctx.kvm_ctx_block_state(50)[0] >= 0
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    assert st["misses"] == 1 and st["hits"] == 10
+    gc.check_view(wl, sel.cpu().numpy(), pool.page.cpu().numpy()[:11], pool)
+    pool.ctx.close()
