@@ -44,7 +44,7 @@ struct RematJob {
 enum { JOB_COPY_V = 2 };
 
 // (l, g) units of 32 token rows handled by one workgroup
-static constexpr int REMAT_UNITS = 4;
+static constexpr int REMAT_UNITS = 8;
 
 struct RematArgs {
   const RematJob* jobs;

@@ -17,6 +17,7 @@ import synth  # noqa: E402
 from oracle import pipeline as op  # noqa: E402
 from oracle.scores import block_scores, block_scores_streamed  # noqa: E402
 from oracle.select import select_blocks, cutoff_margin  # noqa: E402
+from oracle.numerics import bf16_bits  # noqa: E402
 
 
 def one_step(wl, index, step, threads):
@@ -48,30 +49,27 @@ def main():
         index = op.index_rows(wl, 0, wl.n_blocks, threads=threads, out_dtype=np.float32)
         print(f"index {time.time() - t0:.0f}s", flush=True)
         R, sel, margin = one_step(wl, index, 0, threads)
-        out.update(R=R, sel=sel, margin=np.float64(margin))
-        # Mean-K of a few sampled blocks, for the full-size build check
+        out.update(R=R, sel=sel.astype(np.int32), margin=np.float64(margin))
+        # Mean-K of a few sampled blocks (bf16 bit patterns), for the full-size build check
         rng = np.random.default_rng(7)
-        blocks = np.sort(rng.choice(wl.n_blocks, 16, replace=False))
-        out.update(sample_blocks=blocks, sample_index=index[:, :, blocks, :])
+        blocks = np.sort(rng.choice(wl.n_blocks, 4, replace=False))
+        out.update(sample_blocks=blocks, sample_index_bits=bf16_bits(index[:, :, blocks, :]))
     elif name.startswith("churn"):
         # every step: append the step's blocks, score with the step's queries
         N_end = wl.final_blocks
         index = op.index_rows(wl, 0, N_end, threads=threads, out_dtype=np.float32)
         print(f"index {time.time() - t0:.0f}s", flush=True)
-        rng = np.random.default_rng(11)
-        sels, margins, samples, sampleR, sums = [], [], [], [], []
+        sels, margins, Rs = [], [], []
         for t in range(wl.steps):
             N = wl.n_blocks + t * wl.append_blocks
             R, sel, margin = one_step(wl, index[:, :, :N, :], t, threads)
-            pick = np.sort(rng.choice(N, 1024, replace=False))
             sels.append(sel.astype(np.int32))
             margins.append(margin)
-            samples.append(pick)
-            sampleR.append(R[pick])
-            sums.append(R.sum())
+            Rs.append(R)
             print(f"step {t}: {time.time() - t0:.0f}s margin {margin:.2e}", flush=True)
-        out.update(sel=np.stack(sels), margin=np.array(margins), sample_blocks=np.stack(samples),
-                   sample_R=np.stack(sampleR), R_sum=np.array(sums))
+        # scores of step t are R_<t> (lengths grow by the appended blocks)
+        out.update(sel=np.stack(sels), margin=np.array(margins),
+                   **{f"R_{t}": r for t, r in enumerate(Rs)})
     print(f"done {time.time() - t0:.0f}s", flush=True)
     np.savez_compressed(os.path.join(HERE, f"{name}_oracle.npz"), **out)
 

@@ -164,3 +164,31 @@ def raw_blocks_to_device(wl, which: str, blocks, dev):
     for i, b in enumerate(blocks):
         synth.kv_blocks(wl, which, int(b), 1, out=view[i:i + 1])
     return h.to(dev)
+
+
+def check_selection(sel: np.ndarray, R_oracle: np.ndarray, n_sink: int, n_recent: int,
+                    budget: int, band: float = 2e-5):
+    """The GPU selection against the oracle's scores, deciding only what the
+    scores decide: forced blocks present, the right count, ascending order,
+    every candidate whose oracle score exceeds the cutoff score by more than
+    `band` (relative) selected and every one below it by more than `band`
+    left out. Candidates inside the band (fp32 vs fp64 rounding can order
+    them either way) may go either way. Returns the number of band blocks."""
+    N = len(R_oracle)
+    sel = np.asarray(sel)
+    assert np.all(np.diff(sel) > 0)
+    if N <= budget:
+        assert np.array_equal(sel, np.arange(N))
+        return 0
+    assert len(sel) == budget
+    s = set(sel.tolist())
+    assert set(range(n_sink)) <= s and set(range(N - n_recent, N)) <= s
+    k = budget - n_sink - n_recent
+    cand = np.arange(n_sink, N - n_recent)
+    Rc = R_oracle[cand]
+    cut = np.sort(Rc)[::-1][k - 1]
+    above = cand[Rc > cut * (1 + band)]
+    below = cand[Rc < cut * (1 - band)]
+    assert set(above.tolist()) <= s, "a block clearly above the cutoff was not selected"
+    assert not (set(below.tolist()) & s), "a block clearly below the cutoff was selected"
+    return int(len(cand) - len(above) - len(below))

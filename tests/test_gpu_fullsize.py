@@ -52,7 +52,7 @@ def test_ws1m_full_step(k, dev):
     index = gc.build_index_streamed(k, wl, dev)
     blocks = g["sample_blocks"]
     got = gc.to_host_bits(index[:, :, torch.as_tensor(blocks, device=dev), :])
-    assert np.array_equal(gc.as_f64(got), g["sample_index"].astype(np.float64))
+    assert np.array_equal(got, g["sample_index_bits"])
     say("ws1m: scoring")
     q = gc.to_dev(synth.query(wl), dev)
     scores = gc.score_dev(k, wl, q, index, N, N, dev)
@@ -64,8 +64,10 @@ def test_ws1m_full_step(k, dev):
     n = int(n_sel.item())
     s = sel.cpu().numpy()[:n]
     assert n == wl.budget_blocks
-    if float(g["margin"]) > 1e-5:
+    if float(g["margin"]) > 2e-5:
         assert np.array_equal(s, g["sel"])
+    nband = gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
+    say("blocks within the cutoff band", nband)
     assert np.array_equal(base.cpu().numpy()[:n], compact_positions(n))
     del index
     say("ws1m: rematerializing (half resident, half from HBM sources)")
@@ -127,5 +129,7 @@ def test_ws10m_scores_resident_and_host_tiled(k, dev):
                                      wl.n_recent, wl.budget_blocks, dev)
     n = int(n_sel.item())
     assert n == wl.budget_blocks
-    if float(g["margin"]) > 1e-5:
-        assert np.array_equal(sel.cpu().numpy()[:n], g["sel"])
+    s = sel.cpu().numpy()[:n]
+    if float(g["margin"]) > 2e-5:
+        assert np.array_equal(s, g["sel"])
+    gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)

@@ -272,8 +272,9 @@ def test_end_to_end_step(k, dev, name):
     sel, n_sel, base = gc.select_dev(k, scores, N, wl.n_sink, wl.n_recent, wl.budget_blocks, dev)
     n = int(n_sel.item())
     say("margin", ref["margin"])
-    if ref["margin"] > 1e-5:
+    if ref["margin"] > 2e-5:
         assert np.array_equal(sel.cpu().numpy()[:n], ref["sel"])
+    gc.check_selection(sel.cpu().numpy()[:n], ref["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
     assert np.array_equal(base.cpu().numpy()[:n], ref["base_pos"])
     pool = gc.Pool(k, wl, wl.budget_blocks + 8, N, wl.budget_blocks * wl.block_tokens, dev)
     pool.ctx.kvm_ctx_set_source(0, N, raw_k, raw_v, wl.block_bytes, k.KVM_SRC_DEVICE)

@@ -89,3 +89,25 @@ def test_cutoff_margin():
     # sink 1, recent 1, budget 4 -> k = 2 among [4, 2, 1, 3]: kept 4, 3; next 2
     assert cutoff_margin(R, 1, 1, 4) == pytest.approx((3.0 - 2.0) / 3.0)
     assert cutoff_margin(R, 1, 1, 6) == float("inf")
+
+
+def test_band_selection_check_accepts_exact_and_rejects_wrong_choices():
+    from tests.gpu_common import check_selection
+    R = synth.scores_f32(77, 3000).astype(np.float64)
+    sel = select_blocks(R, 1, 64, 500)
+    check_selection(sel, R, 1, 64, 500)                     # the oracle's own choice
+    cand = [b for b in range(1, 3000 - 64) if b not in set(sel.tolist())]
+    worst_in = min((b for b in sel if 1 <= b < 3000 - 64), key=lambda b: R[b])
+    best_out = max(cand, key=lambda b: R[b])
+    swapped = np.sort(np.r_[sel[sel != worst_in], best_out])
+    # swapping the boundary pair is allowed only inside the band
+    rel_gap = (R[worst_in] - R[best_out]) / R[worst_in]
+    if rel_gap > 4e-5:
+        with pytest.raises(AssertionError):
+            check_selection(swapped, R, 1, 64, 500)
+    far_out = min(cand, key=lambda b: R[b])
+    bad = np.sort(np.r_[sel[sel != worst_in], far_out])
+    with pytest.raises(AssertionError):
+        check_selection(bad, R, 1, 64, 500)
+    with pytest.raises(AssertionError):
+        check_selection(sel[1:], R, 1, 64, 500)             # missing sink / wrong count
