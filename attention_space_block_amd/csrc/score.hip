@@ -14,9 +14,10 @@
 //           copies (global_load_lds_dwordx4: no staging registers, no LDS
 //           store instructions; 16-byte pieces XOR-swizzled per row so the
 //           operand reads are bank-conflict free); the 32x32 result puts one
-//           query row in each lane (16 blocks per lane), so the running max /
-//           sum-exp is lane-local: a tile max, one rescale exp per tile and
-//           16 exps; tile sums folded in fp32, the running sum kept in fp64.
+//           query row in each lane (16 blocks per lane), so the running
+//           shift / sum-exp is lane-local: 16 exps against the current shift,
+//           the shift refreshed (tile max, one rescale) only when a tile sum
+//           outgrows it; tile sums folded in fp32, the running sum in fp64.
 //   pass 2: blocks stationary (B operand), query tiles and their LSE streamed
 //           through LDS (A operand); now one block per lane, so the column sum
 //           over query rows is lane-local again. Partial R per (l, g) go to a
@@ -123,17 +124,33 @@ __device__ __forceinline__ void mfma_subtile(f32x16 (&acc)[2], const char* arow,
   }
 }
 
-// Online (max, sum-exp) update of one lane's query row with 16 new scores
-// (raw dot products; x = acc * scale). Branch-free: a lane that has seen only
-// -inf keeps m = -inf and s = 0.
+// Online (shift, sum-exp) update of one lane's query row with 16 new scores
+// (raw dot products; x = acc * scale). The shift m_run is a running maximum
+// that is refreshed lazily: the 16 exps are taken against the current shift,
+// and only a lane whose tile sum exceeds 2^32 (a new score more than 32
+// log2-units above the shift), or that has no shift yet (-inf), or that
+// produced inf/NaN, takes the exact path: tile max, new shift, rescale. Any
+// shift gives the same log-sum-exp, and sums stay below 2^32 per term, so the
+// fp64 running sum loses nothing. A lane that has seen only -inf keeps
+// m = -inf and s = 0.
 __device__ __forceinline__ void lse_update(const f32x16& acc, float scale, float& m_run,
                                            double& s_run) {
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m_run));
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int v = 0; v < w; ++v) e[v] += e[v + w];
+  if (e[0] <= 4294967296.0f) {
+    s_run += (double)e[0];
+    return;
+  }
   float mx = acc[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
   const float m_new = fmaxf(m_run, mx * scale);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-  float e[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m_use));
 #pragma unroll
