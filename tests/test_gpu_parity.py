@@ -96,6 +96,33 @@ def test_scores_match_oracle(k, dev, name, N, scale):
     assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
 
 
+def test_scores_steep_ramp_match_oracle(k, dev):
+    """Scores that climb (or fall) by more than 32 log2-units along the block
+    axis: rows facing the ramp must refresh their softmax shift in pass 1, rows
+    facing away see most terms vanish; both must match the float64 softmax."""
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, n_q_tokens=77)
+    N, d = 2048, wl.head_dim
+    import torch
+    noise = op.as_f64(synth.index_direct(wl, 0, N), "bf16")       # [L][Hkv][N][d]
+    ramp = np.linspace(-120.0, 120.0, N)[None, None, :, None] / np.sqrt(d)
+    bits = torch.from_numpy((noise + ramp).astype(np.float32)).to(torch.bfloat16)
+    bits = bits.view(torch.int16).numpy().view(np.uint16)          # the input, as bf16
+    q = synth.query(wl)
+    ref = op.block_scores(op.as_f64(q, "bf16"), op.as_f64(bits, "bf16"))
+    got = gc.score_dev(k, wl, gc.to_dev(q, dev), gc.to_dev(bits, dev), N, N,
+                       dev).cpu().numpy().astype(np.float64)
+    assert abs(got.sum() - wl.n_q_tokens) <= 1e-5 * wl.n_q_tokens
+    # the input does what it is for: a third of the query rows see their scores
+    # span more than 32 log2-units across the blocks (magnitudes stay below 64,
+    # where fp32 exp arguments keep the 1e-5 bound)
+    qf = op.as_f64(q, "bf16").reshape(wl.n_layers, wl.n_kv_heads, -1, d)
+    kf = op.as_f64(bits, "bf16")
+    span = np.stack([np.ptp(qf[l, g] @ kf[l, g].T, axis=1) for l in range(wl.n_layers)
+                     for g in range(wl.n_kv_heads)]) * np.log2(np.e) / np.sqrt(d)
+    assert np.mean(span > 32) > 0.25
+    assert np.all(np.abs(got - ref) <= 1e-5 * ref + 1e-30)
+
+
 def test_host_tiled_scores_equal_resident(k, dev):
     import torch
     wl = synth.get_workload("ws10m").scaled(n_layers=4, n_blocks=1300, tile_blocks=256)
