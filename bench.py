@@ -88,10 +88,10 @@ class Workspace:
                 gen_err.append(e)
 
         t0 = time.time()
-        build_ms, build_launch = 0.0, 0
         th = threading.Thread(target=gen, args=(0,))
         th.start()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # kernel-only durations from the library's own event pairs on its stream
+        k.kvm_profile_enable(True)
         for i, s in enumerate(starts):
             th.join()
             if gen_err:
@@ -102,15 +102,13 @@ class Workspace:
             if i + 1 < len(starts):
                 th = threading.Thread(target=gen, args=(i + 1,))
                 th.start()
-            ev0.record()
             k.kvm_build_index(self.dims, self.dt, dchunk, nbytes, s, n, self.index, N)
-            ev1.record()
-            ev1.synchronize()
-            build_ms += ev0.elapsed_time(ev1)
-            build_launch += 1
+            torch.cuda.current_stream().synchronize()
             if i % 16 == 0:
                 log(f"index build {s + n}/{n_hist} blocks, {time.time() - t0:.1f}s")
-        self.build_stats = {"launches": build_launch, "blocks": n_hist, "ms": build_ms}
+        launches, ms = k.kvm_profile_read().get("build_index", (0, float("nan")))
+        k.kvm_profile_enable(False)
+        self.build_stats = {"launches": launches, "blocks": n_hist, "ms": ms}
         del dchunk, stage
         # this step's freshly prefilled blocks: raw K/V on the device
         self.new_k = self._gen_dev("K", n_hist, self.n_new)
