@@ -20,7 +20,7 @@ Eq. (10) (only the prose survives), and whether the paper's engine used base
 10000 and interleaved RoPE pairs; both readings are fixed here and stated.
 """
 from .numerics import bf16_round, bf16_bits, round_to_dtype  # noqa: F401
-from .meank import mean_k, mean_k_index  # noqa: F401
+from .meank import mean_k, mean_k_index, mean_k_from_rope  # noqa: F401
 from .scores import block_scores, lg_partial_scores  # noqa: F401
 from .select import select_blocks, compact_positions, cutoff_margin  # noqa: F401
 from .rope import rope_frequencies, rope_rotate, rope_matrix  # noqa: F401

@@ -31,7 +31,10 @@ def from_bf16_bits(bits) -> np.ndarray:
 
 
 def round_to_dtype(x, dtype: str) -> np.ndarray:
-    """Store float64 values in the index dtype: bf16 (RNE) or fp32 (RNE)."""
+    """Store float64 values in the index dtype: bf16 (RNE) or fp32 (RNE); "f64"
+    keeps the float64 value (used by pins that check identities exactly)."""
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
     if dtype == "bf16":
         return bf16_round(x)
     if dtype == "f32":
