@@ -153,6 +153,14 @@ class KvmCtx:
                                                   _ptr(v_raw), block_stride, _stream(stream))
         _abi.check(rc, "kvm_ctx_register_resident")
 
+    def kvm_ctx_build_index_rope(self, k_rope, block_stride: int, first_block: int,
+                                 n_blocks: int, pos0: int, index, index_cap_blocks: int,
+                                 stream=None) -> None:
+        rc = _abi.lib().kvm_ctx_build_index_rope(self._h, _ptr(k_rope), block_stride,
+                                                 first_block, n_blocks, pos0, _ptr(index),
+                                                 index_cap_blocks, _stream(stream))
+        _abi.check(rc, "kvm_ctx_build_index_rope")
+
     def kvm_rematerialize(self, sel, n_sel, page_table, stream=None) -> dict:
         st = RematStats()
         rc = _abi.lib().kvm_rematerialize(self._h, _ptr(sel), _ptr(n_sel), _ptr(page_table),

@@ -41,6 +41,13 @@ inline int dtype_bytes(int32_t dtype) { return dtype == KVM_F32 ? 4 : 2; }
 // Validate dims shared by every entry point.
 int check_dims(const kvm_dims* d, int32_t dtype);
 
+// Launcher of the de-RoPE Mean-K kernel (build_index.hip); arguments checked
+// by the caller. table: device [>= pos0 + 32*n_blocks][d/2] (cos, sin).
+int launch_build_rope(int32_t dtype, int32_t d, int32_t layout, const void* k_rope,
+                      int64_t stride, int64_t n_blocks, int32_t nlg, int64_t pos0,
+                      const void* table, int64_t first_block, int64_t cap, void* index,
+                      hipStream_t s);
+
 // ---- device helpers -------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);

@@ -439,6 +439,32 @@ extern "C" void kvm_ctx_destroy(kvm_ctx* ctx) {
   kvm::destroy(ctx);
 }
 
+extern "C" int kvm_ctx_build_index_rope(kvm_ctx* c, const void* k_rope, int64_t block_stride,
+                                        int64_t first_block, int64_t n_blocks, int64_t pos0,
+                                        void* index, int64_t index_cap_blocks, void* stream) {
+  using namespace kvm;
+  clear_error();
+  KVM_CHECK_ARG(c, "ctx is NULL");
+  KVM_CHECK_ARG(n_blocks >= 0 && first_block >= 0, "negative block range");
+  if (n_blocks == 0) return KVM_OK;
+  KVM_CHECK_ARG(k_rope && index, "null pointer");
+  KVM_CHECK_ARG(block_stride >= c->page_bytes, "block_stride %lld < block bytes %lld",
+                (long long)block_stride, (long long)c->page_bytes);
+  KVM_CHECK_ARG(block_stride % 16 == 0 && ((uintptr_t)k_rope % 16) == 0 &&
+                    ((uintptr_t)index % 16) == 0,
+                "k_rope, index and stride must be 16-byte aligned");
+  KVM_CHECK_ARG(first_block + n_blocks <= index_cap_blocks, "rows beyond index capacity");
+  const kvm_dims& dm = c->d.dims;
+  if (pos0 < 0 || pos0 + (int64_t)dm.block_tokens * n_blocks > (int64_t)c->d.max_pos) {
+    set_error("positions [%lld, %lld) outside the RoPE table [0, %d)", (long long)pos0,
+              (long long)(pos0 + (int64_t)dm.block_tokens * n_blocks), c->d.max_pos);
+    return KVM_ERANGE;
+  }
+  return launch_build_rope(c->d.dtype, dm.head_dim, c->d.rope_layout, k_rope, block_stride,
+                           n_blocks, dm.n_layers * dm.n_kv_heads, pos0, c->d_table,
+                           first_block, index_cap_blocks, index, as_stream(stream));
+}
+
 extern "C" int kvm_ctx_set_source(kvm_ctx* c, int64_t first_block, int64_t n_blocks,
                                   const void* k_base, const void* v_base, int64_t block_stride,
                                   int32_t loc) {

@@ -215,6 +215,22 @@ int kvm_ctx_register_resident(kvm_ctx* ctx, int64_t first_block, int64_t n_block
                               const void* k_raw, const void* v_raw, int64_t block_stride,
                               void* stream);
 
+/* Mean-K index rows from K that already carries RoPE (KVMem Sec. 5: during
+ * prefill RoPE is removed from the K of completed blocks and their Mean-K is
+ * formed while that K is still on the GPU). k_rope: device, block-major
+ * [n_blocks][L][Hkv][B][d] in the ctx dtype, consecutive blocks `block_stride`
+ * bytes apart; token j of block i sits at original position
+ * pos0 + B*i + j. Each token is rotated back by R_{-p} with the (cos, sin) of
+ * the ctx's table (fp32 values of the float64 functions at float64 angles,
+ * the same layout and base as re-RoPE), in float64; the block mean is rounded
+ * once (round-to-nearest-even) into index rows [first_block, first_block +
+ * n_blocks) of the index [L][Hkv][index_cap_blocks][d]. Enqueued on `stream`.
+ * Errors: KVM_EINVAL (pointers, alignment, stride, capacity), KVM_ERANGE
+ * (positions beyond the ctx's max_pos or pos0 < 0). */
+int kvm_ctx_build_index_rope(kvm_ctx* ctx, const void* k_rope, int64_t block_stride,
+                             int64_t first_block, int64_t n_blocks, int64_t pos0, void* index,
+                             int64_t index_cap_blocks, void* stream);
+
 /* Make the execution view for a selection (KVMem Sec. 4.4, Sec. 5, Fig. 3):
  * reads n_sel/sel from the device (one small copy, then waits for `stream`),
  * plans hits / misses / evictions against the pool, stages misses H2D on the

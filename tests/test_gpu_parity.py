@@ -9,6 +9,7 @@ import pytest
 
 import synth
 from oracle import select_blocks, compact_positions
+from oracle.numerics import bf16_bits
 from oracle import pipeline as op
 from tests import gpu_common as gc
 
@@ -66,6 +67,56 @@ def test_build_index_append_and_stride(k, dev):
     k.kvm_build_index(dims, dt, dbl, 2 * wl.block_bytes, 0, 100, st, 128)
     assert torch.equal(full, st)
     assert int(full[:, :, 100:].abs().sum()) == 0     # rows past the range untouched
+
+
+# ------------------------------------------- Mean-K from post-RoPE K ----
+
+@pytest.mark.parametrize("name,layout,pos0,N", [
+    ("ctx64k", 0, 0, 70), ("ctx64k", 1, 4096, 37), ("tiny", 0, 96, 9), ("tiny", 1, 0, 5),
+])
+def test_build_index_rope_matches_oracle(k, dev, name, layout, pos0, N):
+    from oracle import mean_k_from_rope
+    wl = synth.get_workload(name).scaled(rope_layout=layout)
+    if name == "ctx64k":
+        wl = wl.scaled(n_layers=2)
+    say("build index rope", name, layout, pos0, N)
+    k_rope = synth.kv_blocks(wl, "K", 0, N)                 # any K values stand for cached K
+    kd = gc.to_dev(k_rope.reshape(N, -1), dev)
+    pool = gc.Pool(k, wl, 4, N, pos0 + 32 * N, dev)
+    import torch
+    index = torch.zeros((wl.n_layers, wl.n_kv_heads, N + 3, wl.head_dim),
+                        dtype=gc.torch_dtype(wl), device=dev)
+    pool.ctx.kvm_ctx_build_index_rope(kd, wl.block_bytes, 0, N, pos0, index, N + 3)
+    got = gc.to_host_bits(index)[:, :, :N]
+    kf = op.as_f64(k_rope, wl.dtype)
+    want = mean_k_from_rope(kf, pos0, wl.dtype, wl.theta, layout)         # [N][L][Hkv][d]
+    want = np.transpose(want, (1, 2, 0, 3))
+    if wl.dtype == "bf16":
+        assert np.array_equal(got, bf16_bits(want))
+        gv = op.as_f64(got, "bf16")
+    else:
+        assert np.array_equal(got, want.astype(np.float32))
+        gv = got.astype(np.float64)
+    exact = np.transpose(mean_k_from_rope(kf, pos0, "f64", wl.theta, layout, table_fp32=False),
+                         (1, 2, 0, 3))
+    # against the exact float64 rotation: half an ulp of rounding plus the fp32
+    # table's error, at most (|a| + |b|) * 2^-24 per pair of a token
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - (7 if wl.dtype == "bf16" else 23))
+    table_err = 2.0 * np.abs(kf).max() * 2.0 ** -24
+    assert np.all(np.abs(gv - exact) <= 0.5 * ulp + table_err)
+    assert int(index[:, :, N:].abs().sum()) == 0
+    # appending in two calls (positions continue) gives the same rows
+    part = torch.zeros_like(index)
+    n1 = N // 2
+    pool.ctx.kvm_ctx_build_index_rope(kd, wl.block_bytes, 0, n1, pos0, part, N + 3)
+    pool.ctx.kvm_ctx_build_index_rope(kd[n1:], wl.block_bytes, n1, N - n1, pos0 + 32 * n1,
+                                      part, N + 3)
+    assert torch.equal(part, index)
+    # positions past the ctx's table are refused
+    with pytest.raises(k.KvmError) as e:
+        pool.ctx.kvm_ctx_build_index_rope(kd, wl.block_bytes, 0, N, pos0 + 32, index, N + 3)
+    assert e.value.code == k.api._abi.KVM_ERANGE
+    pool.ctx.close()
 
 
 # ---------------------------------------------------------------- scores ----
