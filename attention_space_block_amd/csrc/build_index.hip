@@ -130,100 +130,89 @@ static void launch_build(const void* k_raw, int64_t stride, int64_t n, int32_t n
 // is still on the GPU). Token j of block i sits at original position
 // pos0 + 32*i + j; every (a, b) pair is turned back by that position's angle
 // with the (cos, sin) of the context's fp32 table, in float64, and the block
-// mean is rounded once. A wave takes `upw` (l, g) units of one block: its rows
-// keep the same token indices across units, so their (cos, sin) pairs are
-// loaded once per wave. Each lane owns two 16-byte pieces of a row (the two
-// halves of its rotation pairs: adjacent pieces for interleaved pairs, pieces
-// d/2 apart for the half-split layout).
+// mean is rounded once.
+// A workgroup covers 4*UPW (l, g) units of one block and first widens the
+// block's 32 rows of (cos, sin) into LDS; a wave covers UPW units; within a unit,
+// lane c owns the 16-byte pieces at elements c*P and d/2 + c*P of every row
+// (so each load instruction reads contiguous runs) and walks all 32 rows
+// itself, so the block sum needs no cross-lane reduction; the units of a wave
+// share each row's (cos, sin). Half-split pairs (t, t + d/2) span the two
+// pieces; interleaved pairs (2t, 2t+1) lie inside each piece.
 template <typename T, int D, int LAYOUT>
 __global__ __launch_bounds__(256) void build_index_rope_kernel(
     const char* __restrict__ k_rope, int64_t block_stride, int64_t n_blocks, int32_t nlg,
-    int32_t upw, int64_t pos0, const float2* __restrict__ table, int64_t first_block,
+    int32_t wg_per_block, int64_t pos0, const float2* __restrict__ table, int64_t first_block,
     int64_t cap, T* __restrict__ index) {
   constexpr int P = 16 / sizeof(T);           // elements per piece
-  constexpr int TPR = D / (2 * P);            // lanes per row
-  constexpr int RPI = 64 / TPR;               // rows per wave-wide pass
-  constexpr int ITERS = 32 / RPI;             // rows per lane
+  constexpr int TPU = D / (2 * P);            // lanes per unit
+  constexpr int UPW = 64 / TPU;               // units per wave
   constexpr int HALF = D / 2;
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t waves_per_block = nlg / upw;
-  const int64_t i = wave / waves_per_block;
-  if (i >= n_blocks) return;
-  const int32_t lg0 = (int32_t)(wave % waves_per_block) * upw;
-  const int trow = lane / TPR, tcol = lane % TPR;
-  const int t0 = LAYOUT == 0 ? tcol * 2 * P : tcol * P;      // first element of piece 0
-  const int off1 = LAYOUT == 0 ? P : HALF;                     // piece 1 offset
-  const int tp = LAYOUT == 0 ? t0 / 2 : t0;                    // first pair index
-  // (cos, sin) of the lane's P pairs for each of its ITERS rows
-  float2 cs[ITERS][P];
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const float2* row = table + (pos0 + 32 * i + trow + it * RPI) * HALF + tp;
-#pragma unroll
-    for (int q = 0; q < P; ++q) cs[it][q] = row[q];
+  constexpr int PAD = HALF + HALF / P;        // one spare entry every P pairs (banks)
+  constexpr int RB = 8;                       // rows whose loads are in flight together
+  // (cos, sin) of the block's 32 positions, widened to float64 once per workgroup
+  __shared__ double2 tab[32 * PAD];
+  const int64_t i = blockIdx.x / wg_per_block;
+  if (i >= n_blocks) return;                  // uniform over the workgroup
+  const float2* tsrc = table + (pos0 + 32 * i) * HALF;
+  for (int e = threadIdx.x; e < 32 * HALF; e += 256) {
+    const int r = e / HALF, t = e % HALF;
+    const float2 v = tsrc[e];
+    tab[r * PAD + t + t / P] = make_double2((double)v.x, (double)v.y);
   }
-  const char* blk = k_rope + i * block_stride;
-  for (int32_t u = 0; u < upw; ++u) {
-    const int32_t lg = lg0 + u;
-    const char* src = blk + (int64_t)lg * 32 * D * sizeof(T);
-    uint4 v0[ITERS], v1[ITERS];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int32_t lg = (int32_t)(blockIdx.x % wg_per_block) * 4 * UPW +
+                     (threadIdx.x >> 6) * UPW + lane / TPU;
+  const bool active = lg < nlg;
+  const int tcol = lane % TPU;
+  const int t0 = tcol * P;                                     // first element of piece 0
+  const int off1 = HALF;                                       // piece 1 offset
+  const char* src = k_rope + i * block_stride +
+                    ((int64_t)(active ? lg : 0) * 32 * D + t0) * sizeof(T);
+  double acc0[P], acc1[P];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const char* r = src + ((int64_t)(trow + it * RPI) * D + t0) * sizeof(T);
-      v0[it] = ld_nt(r);
-      v1[it] = ld_nt(r + off1 * sizeof(T));
+  for (int e = 0; e < P; ++e) acc0[e] = acc1[e] = 0.0;
+#pragma unroll 1
+  for (int r0 = 0; r0 < 32; r0 += RB) {
+    uint4 v0[RB], v1[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const char* rp = src + (int64_t)(r0 + r) * D * sizeof(T);
+      v0[r] = ld_nt(rp);
+      v1[r] = ld_nt(rp + off1 * sizeof(T));
     }
-    double acc0[P], acc1[P];
 #pragma unroll
-    for (int e = 0; e < P; ++e) acc0[e] = acc1[e] = 0.0;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
+    for (int r = 0; r < RB; ++r) {
+      const double2* cs = tab + (r0 + r) * PAD;
       double x0[P], x1[P];
-      widen<T>(v0[it], x0);
-      widen<T>(v1[it], x1);
+      widen<T>(v0[r], x0);
+      widen<T>(v1[r], x1);
 #pragma unroll
       for (int q = 0; q < P; ++q) {
-        // pair q of the lane: interleaved (x0[2q], x0[2q+1]) for q < P/2, then
-        // (x1[2(q-P/2)], ...); half-split (x0[q], x1[q])
-        double a, b;
+        // pair q: interleaved (x0[2q], x0[2q+1]) = pair t0/2 + q for q < P/2,
+        // then the same in x1 = pair (t0 + d/2)/2 + q - P/2; half-split
+        // (x0[q], x1[q]) = pair t0 + q. R_{-p}: (a c + b s, b c - a s).
+        const int t = LAYOUT == 0 ? (q < P / 2 ? t0 / 2 + q : HALF / 2 + t0 / 2 + q - P / 2)
+                                  : t0 + q;
+        const double2 w = cs[t + t / P];
+        const double c = w.x, sn = w.y;
         if (LAYOUT == 0) {
-          a = q < P / 2 ? x0[2 * q] : x1[2 * (q - P / 2)];
-          b = q < P / 2 ? x0[2 * q + 1] : x1[2 * (q - P / 2) + 1];
+          double* acc = q < P / 2 ? acc0 : acc1;
+          const double* x = q < P / 2 ? x0 : x1;
+          const int e = 2 * (q % (P / 2));
+          acc[e] = fma(x[e + 1], sn, fma(x[e], c, acc[e]));
+          acc[e + 1] = fma(-x[e], sn, fma(x[e + 1], c, acc[e + 1]));
         } else {
-          a = x0[q];
-          b = x1[q];
-        }
-        const double c = (double)cs[it][q].x, sn = (double)cs[it][q].y;
-        const double ra = a * c + b * sn;      // R_{-p}
-        const double rb = b * c - a * sn;
-        if (LAYOUT == 0) {
-          if (q < P / 2) {
-            acc0[2 * q] += ra;
-            acc0[2 * q + 1] += rb;
-          } else {
-            acc1[2 * (q - P / 2)] += ra;
-            acc1[2 * (q - P / 2) + 1] += rb;
-          }
-        } else {
-          acc0[q] += ra;
-          acc1[q] += rb;
+          acc0[q] = fma(x1[q], sn, fma(x0[q], c, acc0[q]));
+          acc1[q] = fma(-x0[q], sn, fma(x1[q], c, acc1[q]));
         }
       }
     }
-#pragma unroll
-    for (int off = TPR; off < 64; off <<= 1) {
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        acc0[e] += __shfl_xor(acc0[e], off);
-        acc1[e] += __shfl_xor(acc1[e], off);
-      }
-    }
-    if (trow == 0) {
-      T* dst = index + ((int64_t)lg * cap + first_block + i) * D;
-      *reinterpret_cast<uint4*>(dst + t0) = store_mean<T>(acc0);
-      *reinterpret_cast<uint4*>(dst + t0 + off1) = store_mean<T>(acc1);
-    }
+  }
+  if (active) {
+    T* dst = index + ((int64_t)lg * cap + first_block + i) * D;
+    *reinterpret_cast<uint4*>(dst + t0) = store_mean<T>(acc0);
+    *reinterpret_cast<uint4*>(dst + t0 + off1) = store_mean<T>(acc1);
   }
 }
 
@@ -231,10 +220,11 @@ int launch_build_rope(int32_t dtype, int32_t d, int32_t layout, const void* k_ro
                       int64_t stride, int64_t n_blocks, int32_t nlg, int64_t pos0,
                       const void* table, int64_t first_block, int64_t cap, void* index,
                       hipStream_t s) {
-  int32_t upw = 1;
-  while (upw < 8 && nlg % (upw * 2) == 0) upw *= 2;
-  const int64_t waves = n_blocks * (nlg / upw);
-  const int64_t grid = (waves + 3) / 4;
+  // units per wave: 64 / (lanes per unit), lanes per unit = d / (2 * elements per piece);
+  // a workgroup (4 waves) covers 4 * upw units of one block
+  const int32_t upw = 64 / (d / (2 * (16 / dtype_bytes(dtype))));
+  const int32_t wg_per_block = (nlg + 4 * upw - 1) / (4 * upw);
+  const int64_t grid = n_blocks * wg_per_block;
   if (grid >= 0x7fffffffLL) {
     set_error("grid too large");
     return KVM_EINVAL;
@@ -244,7 +234,8 @@ int launch_build_rope(int32_t dtype, int32_t d, int32_t layout, const void* k_ro
   KernelTimer tm("build_index_rope", s);
 #define KVM_BR(T, D, LAY)                                                                   \
   build_index_rope_kernel<T, D, LAY><<<dim3((uint32_t)grid), dim3(256), 0, s>>>(            \
-      src, stride, n_blocks, nlg, upw, pos0, tb, first_block, cap, reinterpret_cast<T*>(index))
+      src, stride, n_blocks, nlg, wg_per_block, pos0, tb, first_block, cap,                \
+      reinterpret_cast<T*>(index))
   if (dtype == KVM_BF16) {
     if (d == 128) { if (layout == 0) KVM_BR(uint16_t, 128, 0); else KVM_BR(uint16_t, 128, 1); }
     else { if (layout == 0) KVM_BR(uint16_t, 64, 0); else KVM_BR(uint16_t, 64, 1); }

@@ -460,6 +460,21 @@ def main():
     bst = ws.build_stats
     build_bytes = bst["blocks"] * (page + L * wl.n_kv_heads * d * 2)
     build_gbps = build_bytes / (bst["ms"] * 1e-3) / 1e9
+    # Mean-K from K that carries RoPE (the prefill-time form), over 1024 blocks of
+    # HBM-resident K (the staged half's copies stand in for cached K)
+    nr = min(1024, nm)
+    ridx = torch.empty((L, wl.n_kv_heads, nr, d), dtype=torch.int16, device=dev)
+    ws.ctx.kvm_ctx_build_index_rope(ws.miss_k_d, page, 0, nr, 0, ridx, nr)
+    torch.cuda.synchronize()
+    k.kvm_profile_enable(True)
+    for _ in range(3):
+        ws.ctx.kvm_ctx_build_index_rope(ws.miss_k_d, page, 0, nr, 0, ridx, nr)
+    torch.cuda.synchronize()
+    rc_, rt_ = k.kvm_profile_read().get("build_index_rope", (0, float("nan")))
+    k.kvm_profile_enable(False)
+    del ridx
+    rope_ms = rt_ / max(rc_, 1)
+    rope_gbps = nr * (page + L * wl.n_kv_heads * d * 2) / (rope_ms * 1e-3) / 1e9
     # PCIe leg: misses from pinned host memory
     pcie = None
     if args.pcie_steps > 0:
@@ -503,6 +518,8 @@ def main():
                   "blocks_per_s": None, "tflops_per_pass": flops_pass / 1e12},
         "build": {"blocks": bst["blocks"], "GBps": build_gbps,
                   "hbm_frac": build_gbps / HBM_PEAK_GBPS},
+        "build_rope": {"blocks": nr, "avg_ms": rope_ms, "GBps": rope_gbps,
+                       "hbm_frac": rope_gbps / HBM_PEAK_GBPS},
         "pcie_leg": pcie,
         "kernels": kern,
     }
