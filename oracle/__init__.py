@@ -23,6 +23,6 @@ from .numerics import bf16_round, bf16_bits, round_to_dtype  # noqa: F401
 from .meank import mean_k, mean_k_index, mean_k_from_rope  # noqa: F401
 from .scores import block_scores, lg_partial_scores  # noqa: F401
 from .select import select_blocks, compact_positions, cutoff_margin  # noqa: F401
-from .rope import rope_frequencies, rope_rotate, rope_matrix  # noqa: F401
+from .rope import rope_frequencies, rope_rotate, rope_matrix, bounded_delta_rope  # noqa: F401
 from .plan import working_set_delta  # noqa: F401
 from .accounting import kv_bytes, index_bytes  # noqa: F401

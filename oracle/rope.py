@@ -62,3 +62,45 @@ def rope_matrix(p: float, d: int, base: float = 10000.0, layout: int = 0) -> np.
         c, s = np.cos(p * th[t]), np.sin(p * th[t])
         M[i, i], M[i, j], M[j, i], M[j, j] = c, -s, s, c
     return M
+
+
+def bounded_delta_rope(k_raw: np.ndarray, base_positions, limit: int, dtype: str,
+                       base: float = 10000.0, layout: int = 0):
+    """Stored K of one block over a sequence of compact placements, with
+    bounded delta re-RoPE (KVMem Sec. 4.4).
+
+    k_raw [..., B, d]: the block's raw (pre-RoPE) K; token j of placement i sits
+    at base_positions[i] + j. Placement 0 encodes from raw K. Later, when the
+    position changes, the stored low-precision K is rotated in place by the
+    shift delta = P_i - P_{i-1} (the same for every token) and rounded again,
+    at most `limit` times in a row; the change after that reconstructs from raw
+    K at the new position and resets the counter. An unchanged position leaves
+    K (and the counter) as it is. Rotations are float64, each store is one
+    round-to-nearest-even into dtype ("f64": no rounding).
+
+    Returns (stored K per placement, kind per placement: "full", "delta" or
+    "same", delta count after each placement)."""
+    k = np.asarray(k_raw, dtype=np.float64)
+    B = k.shape[-2]
+    j = np.arange(B)
+    out, kinds, counts = [], [], []
+    x, prev, n = None, None, 0
+    for i, p in enumerate(base_positions):
+        if i == 0 or (p != prev and n >= limit):
+            x = round_store(rope_rotate(k, p + j, base, layout), dtype)
+            kind, n = "full", 0
+        elif p == prev:
+            kind = "same"
+        else:
+            x = round_store(rope_rotate(x, np.full(B, p - prev), base, layout), dtype)
+            kind, n = "delta", n + 1
+        out.append(x)
+        kinds.append(kind)
+        counts.append(n)
+        prev = p
+    return out, kinds, counts
+
+
+def round_store(x: np.ndarray, dtype: str) -> np.ndarray:
+    from .numerics import round_to_dtype
+    return round_to_dtype(x, dtype)

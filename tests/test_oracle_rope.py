@@ -70,3 +70,75 @@ def test_layouts_differ_by_a_fixed_permutation():
     a = rope_rotate(x, pos, layout=0)[:, perm]
     b = rope_rotate(x[:, perm], pos, layout=1)
     assert np.allclose(a, b, rtol=0, atol=1e-13)
+
+
+# ---- bounded delta re-RoPE (KVMem Sec. 4.4) ----
+
+def _bf16_block(seed, shape=(2, 32, 16)):
+    from oracle.numerics import bf16_round
+    return bf16_round(np.random.default_rng(seed).standard_normal(shape))
+
+
+def _ulp_bf16(x):
+    return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -100))) - 7)
+
+
+def test_delta_limit_zero_is_reencoding_from_raw_every_time():
+    from oracle import bounded_delta_rope
+    from oracle.numerics import bf16_round
+    k = _bf16_block(21)
+    P = [64, 96, 0, 320, 320, 32]
+    xs, kinds, counts = bounded_delta_rope(k, P, 0, "bf16")
+    assert kinds == ["full", "full", "full", "full", "same", "full"]
+    assert counts == [0] * 6
+    for x, p in zip(xs, P):
+        assert np.array_equal(x, bf16_round(rope_rotate(k, p + np.arange(32))))
+
+
+def test_delta_steps_compose_exactly_without_rounding():
+    """R_a R_b = R_{a+b}: unrounded delta steps land on the direct rotation."""
+    from oracle import bounded_delta_rope
+    k = np.random.default_rng(22).standard_normal((2, 32, 16))
+    P = [0, 4096, 33, 100000, 7]
+    for layout in (0, 1):
+        xs, kinds, _ = bounded_delta_rope(k, P, 10, "f64", layout=layout)
+        assert kinds == ["full"] + ["delta"] * 4
+        for x, p in zip(xs, P):
+            assert np.max(np.abs(x - rope_rotate(k, p + np.arange(32), layout=layout))) <= 1e-11
+
+
+def test_counter_resets_after_the_limit():
+    from oracle import bounded_delta_rope
+    from oracle.numerics import bf16_round
+    k = _bf16_block(23)
+    P = [0, 32, 64, 96, 128, 160, 160, 192, 224]
+    xs, kinds, counts = bounded_delta_rope(k, P, 2, "bf16")
+    assert kinds == ["full", "delta", "delta", "full", "delta", "delta", "same", "full", "delta"]
+    assert counts == [0, 1, 2, 0, 1, 2, 2, 0, 1]
+    for x, p, kind in zip(xs, P, kinds):
+        if kind == "full":
+            assert np.array_equal(x, bf16_round(rope_rotate(k, p + np.arange(32))))
+
+
+def test_delta_error_grows_at_most_half_ulp_per_pair_per_store():
+    """Each store rounds both components of a pair by at most half an ulp, and
+    a rotation keeps earlier error's length, so after n deltas the pair error
+    is at most (n + 1) * sqrt(2)/2 ulp of the pair's length (bf16)."""
+    from oracle import bounded_delta_rope
+    k = _bf16_block(24, (4, 32, 64))
+    P = [0, 3000, 17, 9000, 450, 120000, 64, 5000, 99]
+    for layout in (0, 1):
+        xs, _, counts = bounded_delta_rope(k, P, 8, "bf16", layout=layout)
+        worst = []
+        for n, (x, p) in enumerate(zip(xs, P)):
+            exact = rope_rotate(k, p + np.arange(32), layout=layout)
+            if layout == 0:
+                ea, eb, na, nb = (x - exact)[..., 0::2], (x - exact)[..., 1::2], exact[..., 0::2], exact[..., 1::2]
+            else:
+                ea, eb, na, nb = (x - exact)[..., :32], (x - exact)[..., 32:], exact[..., :32], exact[..., 32:]
+            err = np.hypot(ea, eb)
+            norm = np.hypot(na, nb)
+            bound = (counts[n] + 1) * (np.sqrt(2) / 2) * _ulp_bf16(1.1 * norm)
+            assert np.all(err <= bound)
+            worst.append(float(np.max(err / _ulp_bf16(norm))))
+        assert worst[-1] > worst[0]          # the error does grow with the deltas
