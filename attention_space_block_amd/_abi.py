@@ -21,8 +21,8 @@ EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
     "kvm_select_ws_bytes", "kvm_select", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
-    "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state", "kvm_ctx_evict",
-    "kvm_profile_enable", "kvm_profile_read",
+    "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
+    "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_profile_enable", "kvm_profile_read",
 ]
 
 
@@ -44,14 +44,15 @@ class CtxDesc(ctypes.Structure):
                 ("n_slots", ctypes.c_int32), ("k_view", ctypes.c_void_p),
                 ("v_view", ctypes.c_void_p), ("k_shadow", ctypes.c_void_p),
                 ("max_blocks", ctypes.c_int64), ("batch_blocks", ctypes.c_int32),
-                ("staging_blocks", ctypes.c_int32)]
+                ("staging_blocks", ctypes.c_int32), ("delta_limit", ctypes.c_int32)]
 
 
 class RematStats(ctypes.Structure):
     _fields_ = [("n_sel", ctypes.c_int32), ("hits", ctypes.c_int32), ("misses", ctypes.c_int32),
                 ("rotated", ctypes.c_int32), ("evicted", ctypes.c_int32),
                 ("batches", ctypes.c_int32), ("h2d_bytes", ctypes.c_int64),
-                ("d2d_bytes", ctypes.c_int64)]
+                ("d2d_bytes", ctypes.c_int64), ("deltas", ctypes.c_int32),
+                ("rebuilds", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -97,6 +98,7 @@ def lib():
             "kvm_ctx_sync": (ctypes.c_int, [vp]),
             "kvm_ctx_block_state": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32),
                                                    ctypes.POINTER(i32)]),
+            "kvm_ctx_block_deltas": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32)]),
             "kvm_ctx_evict": (ctypes.c_int, [vp, i64, i64]),
             "kvm_profile_enable": (ctypes.c_int, [i32]),
             "kvm_profile_read": (ctypes.c_int, [ctypes.POINTER(KernelStat), i32,

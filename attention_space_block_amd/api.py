@@ -94,7 +94,8 @@ class KvmCtx:
 
     def __init__(self, dims: Dims, dtype: int, k_view, v_view, k_shadow, n_slots: int,
                  max_blocks: int, max_pos: int, rope_theta: float = 10000.0,
-                 rope_layout: int = 0, batch_blocks: int = 64, staging_blocks: int = 0):
+                 rope_layout: int = 0, batch_blocks: int = 64, staging_blocks: int = 0,
+                 delta_limit: int = 0):
         d = _abi.CtxDesc()
         d.dims = dims
         d.dtype = dtype
@@ -108,6 +109,7 @@ class KvmCtx:
         d.max_blocks = max_blocks
         d.batch_blocks = batch_blocks
         d.staging_blocks = staging_blocks
+        d.delta_limit = delta_limit
         h = ctypes.c_void_p()
         _abi.check(_abi.lib().kvm_ctx_create(ctypes.byref(d), ctypes.byref(h)), "kvm_ctx_create")
         self._h = h
@@ -167,6 +169,12 @@ class KvmCtx:
                                           ctypes.byref(st), _stream(stream))
         _abi.check(rc, "kvm_rematerialize")
         return st.as_dict()
+
+    def kvm_ctx_block_deltas(self, block: int) -> int:
+        n = ctypes.c_int32()
+        _abi.check(_abi.lib().kvm_ctx_block_deltas(self._h, block, ctypes.byref(n)),
+                   "kvm_ctx_block_deltas")
+        return int(n.value)
 
     def kvm_ctx_evict(self, first_block: int, n_blocks: int) -> None:
         _abi.check(_abi.lib().kvm_ctx_evict(self._h, first_block, n_blocks), "kvm_ctx_evict")

@@ -41,7 +41,10 @@ struct RematJob {
   int32_t flags;
   int32_t pad;
 };
-enum { JOB_COPY_V = 2 };
+// JOB_DELTA: rotate every token by the same signed shift `pos` (an in-place
+// delta re-RoPE) instead of by its absolute position pos + j. JOB_K_ONLY is
+// host-side only: a staged rebuild that moves raw K but keeps the V page.
+enum { JOB_COPY_V = 2, JOB_DELTA = 4, JOB_K_ONLY = 8 };
 
 // (l, g) units of 32 token rows handled by one workgroup
 static constexpr int REMAT_UNITS = 8;
@@ -122,15 +125,20 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   const int tcol = threadIdx.x % TPR;
   const int t0 = LAYOUT == 0 ? tcol * 2 * P : tcol * P;            // first element
   const int off1 = LAYOUT == 0 ? P : D / 2;                         // second piece offset
-  // (cos, sin) of the pairs this thread rotates, for each of its token indices
+  // (cos, sin) of the pairs this thread rotates, for each of its token indices;
+  // a delta job turns every token by the same shift (sin negated when < 0)
+  const bool delta = (job.flags & JOB_DELTA) != 0;
+  const int32_t shift = job.pos < 0 ? -job.pos : job.pos;
   float2 cs[NJ][NC];
 #pragma unroll
   for (int s = 0; s < NJ; ++s) {
     const int j = (trow + s * RPI) & 31;
-    const float2* row = a.table + (int64_t)(job.pos + j) * HALF;
+    const float2* row = a.table + (int64_t)(delta ? shift : job.pos + j) * HALF;
 #pragma unroll
-    for (int q = 0; q < NC; ++q)
+    for (int q = 0; q < NC; ++q) {
       cs[s][q] = LAYOUT == 0 ? row[t0 / 2 + q] : row[t0 + q];
+      if (delta && job.pos < 0) cs[s][q].y = -cs[s][q].y;
+    }
   }
   const int64_t page = (int64_t)job.slot * a.page_bytes;
   const int64_t row0 = (int64_t)wpart * ROWS;
@@ -213,6 +221,8 @@ struct BlockRec {
   const char* src_k = nullptr;
   const char* src_v = nullptr;
   bool raw_in_shadow = false;  // the page's shadow holds the raw K (else the device source)
+  bool page_raw = false;       // delta mode: the K page holds raw K, not yet rotated
+  int32_t n_delta = 0;         // delta mode: in-place shifts since the last encode from raw K
 };
 
 struct Gather {
@@ -344,6 +354,8 @@ static int32_t take_slot(kvm_ctx* c, std::vector<std::pair<int64_t, int32_t>>& l
     r.slot = -1;
     r.baked = -1;
     r.raw_in_shadow = false;
+    r.page_raw = false;
+    r.n_delta = 0;
     ++*evicted;
     return s;
   }
@@ -353,7 +365,8 @@ static int32_t take_slot(kvm_ctx* c, std::vector<std::pair<int64_t, int32_t>>& l
 // A resident page whose re-encode source is the block's device-resident
 // lower-tier copy must not outlive a change of that source: reclaim it.
 static void release_if_unbacked(kvm_ctx* c, BlockRec& r) {
-  if (r.slot < 0 || r.raw_in_shadow) return;
+  // in delta mode a page's K is self-contained; only rebuilds read the source
+  if (r.slot < 0 || r.raw_in_shadow || c->d.delta_limit > 0) return;
   c->slot_block[r.slot] = -1;
   c->free_slots.push_back(r.slot);
   r.slot = -1;
@@ -368,7 +381,9 @@ extern "C" int kvm_ctx_create(const kvm_ctx_desc* desc, kvm_ctx** out) {
   KVM_CHECK_ARG(desc && out, "null pointer");
   int rc = check_dims(&desc->dims, desc->dtype);
   if (rc) return rc;
-  KVM_CHECK_ARG(desc->n_slots > 0 && desc->k_view && desc->v_view && desc->k_shadow,
+  KVM_CHECK_ARG(desc->delta_limit >= 0, "delta_limit");
+  KVM_CHECK_ARG(desc->n_slots > 0 && desc->k_view && desc->v_view &&
+                    (desc->k_shadow || desc->delta_limit > 0),
                 "pool pointers / n_slots");
   KVM_CHECK_ARG(desc->max_blocks > 0 && desc->max_pos > 0, "max_blocks / max_pos");
   KVM_CHECK_ARG(desc->rope_layout == 0 || desc->rope_layout == 1, "rope_layout");
@@ -563,9 +578,12 @@ extern "C" int kvm_ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_
     }
     r.baked = -1;
     r.last_used = c->step;
-    r.raw_in_shadow = true;
-    KVM_HIP(hipMemcpyAsync((char*)c->d.k_shadow + (int64_t)sl * c->page_bytes,
-                           (const char*)k_raw + i * block_stride, c->page_bytes,
+    r.n_delta = 0;
+    const bool delta = c->d.delta_limit > 0;
+    r.raw_in_shadow = !delta;
+    r.page_raw = delta;
+    char* kdst = (char*)(delta ? c->d.k_view : c->d.k_shadow) + (int64_t)sl * c->page_bytes;
+    KVM_HIP(hipMemcpyAsync(kdst, (const char*)k_raw + i * block_stride, c->page_bytes,
                            hipMemcpyDeviceToDevice, s));
     KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)sl * c->page_bytes,
                            (const char*)v_raw + i * block_stride, c->page_bytes,
@@ -588,7 +606,16 @@ extern "C" int kvm_ctx_evict(kvm_ctx* c, int64_t first_block, int64_t n_blocks) 
     r.slot = -1;
     r.baked = -1;
     r.raw_in_shadow = false;
+    r.page_raw = false;
+    r.n_delta = 0;
   }
+  return KVM_OK;
+}
+
+extern "C" int kvm_ctx_block_deltas(kvm_ctx* c, int64_t block, int32_t* n_delta) {
+  using namespace kvm;
+  KVM_CHECK_ARG(c && n_delta && block >= 0 && block < c->d.max_blocks, "block out of range");
+  *n_delta = c->rec[block].slot >= 0 ? c->rec[block].n_delta : 0;
   return KVM_OK;
 }
 
@@ -632,6 +659,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     return KVM_ERANGE;
   }
   int32_t* sel = c->h_sel + 1;
+  const bool delta_mode = c->d.delta_limit > 0;
   if (n > 0) {
     KVM_HIP(hipMemcpyAsync(sel, sel_dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     KVM_HIP(hipStreamSynchronize(s));
@@ -646,6 +674,13 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     const BlockRec& r = c->rec[b];
     if (r.slot < 0 && r.src == KVM_SRC_NONE) {
       set_error("block %lld is neither resident nor backed by a source", (long long)b);
+      return KVM_ERANGE;
+    }
+    // delta mode: a hit past its delta limit is rebuilt from its raw K
+    if (delta_mode && r.slot >= 0 && !r.page_raw && r.baked != i * B &&
+        (r.baked < 0 || r.n_delta >= c->d.delta_limit) && r.src == KVM_SRC_NONE) {
+      set_error("block %lld needs a rebuild from raw K but has no lower-tier copy",
+                (long long)b);
       return KVM_ERANGE;
     }
   }
@@ -664,6 +699,18 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   std::vector<int32_t> hit_jobs, dev_jobs, dma_miss, gather_miss;
   RematJob* J = c->h_jobs;
   int32_t nj = 0;
+  // Where staged raw K lands and is read by the kernel: the page's shadow, or
+  // (delta mode) the K page itself, rotated in place.
+  auto stage_k = [&](int32_t sl) {
+    return (const char*)(delta_mode ? c->d.k_view : c->d.k_shadow) + (int64_t)sl * c->page_bytes;
+  };
+  auto kpage = [&](int32_t sl) { return (const char*)c->d.k_view + (int64_t)sl * c->page_bytes; };
+  // A job whose raw K (and V unless JOB_K_ONLY) comes from host memory.
+  auto staged_job = [&](BlockRec& r, int32_t sl, int32_t pos, int32_t flags, int32_t i) {
+    J[nj] = RematJob{stage_k(sl), nullptr, sl, pos, flags, i};
+    if (r.gather >= 0) gather_miss.push_back(nj++);
+    else dma_miss.push_back(nj++);
+  };
   for (int32_t i = 0; i < n; ++i) {
     const int64_t b = sel[i];
     BlockRec& r = c->rec[b];
@@ -671,7 +718,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     if (r.slot >= 0) {
       ++st.hits;
       c->h_page[i] = r.slot;
-      if (r.baked != pos) {
+      if (r.baked == pos && !r.page_raw) continue;
+      if (!delta_mode) {
         // re-encode from the raw K kept in HBM: the page's shadow, or the
         // block's device-resident lower-tier copy
         const char* raw = r.raw_in_shadow
@@ -679,8 +727,30 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
                               : r.src_k;
         J[nj] = RematJob{raw, nullptr, r.slot, pos, 0, 0};
         hit_jobs.push_back(nj++);
-        r.baked = pos;
+      } else if (r.page_raw) {
+        // freshly registered: raw K sits in the K page, rotate it there
+        J[nj] = RematJob{kpage(r.slot), nullptr, r.slot, pos, 0, 0};
+        hit_jobs.push_back(nj++);
+        r.page_raw = false;
+        r.n_delta = 0;
+      } else if (r.baked >= 0 && r.n_delta < c->d.delta_limit) {
+        // bounded delta re-RoPE: rotate the stored K by the position shift
+        J[nj] = RematJob{kpage(r.slot), nullptr, r.slot, pos - r.baked, JOB_DELTA, 0};
+        hit_jobs.push_back(nj++);
+        r.n_delta += 1;
+        ++st.deltas;
+      } else {
+        // limit reached: rebuild from raw K at the new position, reset the count
+        ++st.rebuilds;
+        r.n_delta = 0;
+        if (r.src == KVM_SRC_DEVICE) {
+          J[nj] = RematJob{r.src_k, nullptr, r.slot, pos, 0, 0};
+          hit_jobs.push_back(nj++);
+        } else {
+          staged_job(r, r.slot, pos, JOB_K_ONLY, i);
+        }
       }
+      r.baked = pos;
       continue;
     }
     ++st.misses;
@@ -692,6 +762,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
     c->slot_block[sl] = b;
     r.slot = sl;
     r.baked = pos;
+    r.page_raw = false;
+    r.n_delta = 0;
     c->h_page[i] = sl;
     if (r.src == KVM_SRC_DEVICE) {
       // the lower-tier copy is already in HBM: rotate from it, copy V, and
@@ -700,11 +772,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       r.raw_in_shadow = false;
       dev_jobs.push_back(nj++);
     } else {
-      r.raw_in_shadow = true;
-      J[nj] = RematJob{(const char*)c->d.k_shadow + (int64_t)sl * c->page_bytes, nullptr, sl,
-                       pos, 0, (int32_t)i};
-      if (r.gather >= 0) gather_miss.push_back(nj++);
-      else dma_miss.push_back(nj++);
+      r.raw_in_shadow = !delta_mode;
+      staged_job(r, sl, pos, 0, i);
     }
   }
   // Jobs are grouped: [hits + device misses][DMA misses][gathered misses].
@@ -760,20 +829,25 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   for (int32_t bi = 0; bi < n_dma_batches; ++bi) {
     const int32_t first = cursor + bi * bb;
     const int32_t cnt = std::min(bb, n_first + n_dma - first);
+    int32_t pages_in = 0;
     for (int32_t q = 0; q < cnt; ++q) {
       const RematJob& jb = J[first + q];
       const BlockRec& r = c->rec[sel[jb.pad]];
-      char* pg = (char*)c->d.k_shadow + (int64_t)jb.slot * c->page_bytes;
-      KVM_HIP(hipMemcpyAsync(pg, r.src_k, c->page_bytes, hipMemcpyHostToDevice, c->side));
-      KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)jb.slot * c->page_bytes, r.src_v,
-                             c->page_bytes, hipMemcpyHostToDevice, c->side));
+      KVM_HIP(hipMemcpyAsync((char*)jb.src_k, r.src_k, c->page_bytes, hipMemcpyHostToDevice,
+                             c->side));
+      ++pages_in;
+      if (!(jb.flags & JOB_K_ONLY)) {
+        KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)jb.slot * c->page_bytes, r.src_v,
+                               c->page_bytes, hipMemcpyHostToDevice, c->side));
+        ++pages_in;
+      }
     }
     hipEvent_t ev = c->batch_ev[ev_used++];
     KVM_HIP(hipEventRecord(ev, c->side));
     KVM_HIP(hipStreamWaitEvent(s, ev, 0));
     rc = launch_range(first, cnt);
     if (rc) return rc;
-    st.h2d_bytes += (int64_t)cnt * 2 * c->page_bytes;
+    st.h2d_bytes += (int64_t)pages_in * c->page_bytes;
     st.d2d_bytes += (int64_t)cnt * 2 * c->page_bytes;
     ++st.batches;
   }
@@ -799,6 +873,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       char* base = c->ring + (size_t)h * half_blocks * 2 * c->page_bytes;
       c->pool->run(cnt * 2, [&](int t) {
         const RematJob& jb = J[first + t / 2];
+        if ((t & 1) && (jb.flags & JOB_K_ONLY)) return;   // rebuild: V page is intact
         const int64_t blk = sel[jb.pad];
         const Gather& g = c->gathers[c->rec[blk].gather];
         char* dst = base + ((size_t)(t / 2) * 2 + (t & 1)) * c->page_bytes;
@@ -809,14 +884,19 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
         KVM_HIP(hipStreamSynchronize(c->side));
         return KVM_ERANGE;
       }
+      int32_t pages_in = 0;
       for (int32_t q = 0; q < cnt; ++q) {
         const RematJob& jb = J[first + q];
         const char* src = base + (size_t)q * 2 * c->page_bytes;
-        KVM_HIP(hipMemcpyAsync((char*)c->d.k_shadow + (int64_t)jb.slot * c->page_bytes, src,
-                               c->page_bytes, hipMemcpyHostToDevice, c->side));
-        KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)jb.slot * c->page_bytes,
-                               src + c->page_bytes, c->page_bytes, hipMemcpyHostToDevice,
+        KVM_HIP(hipMemcpyAsync((char*)jb.src_k, src, c->page_bytes, hipMemcpyHostToDevice,
                                c->side));
+        ++pages_in;
+        if (!(jb.flags & JOB_K_ONLY)) {
+          KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)jb.slot * c->page_bytes,
+                                 src + c->page_bytes, c->page_bytes, hipMemcpyHostToDevice,
+                                 c->side));
+          ++pages_in;
+        }
       }
       KVM_HIP(hipEventRecord(c->ring_ev[h], c->side));
       half_busy[h] = true;
@@ -825,7 +905,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       KVM_HIP(hipStreamWaitEvent(s, ev, 0));
       rc = launch_range(first, cnt);
       if (rc) return rc;
-      st.h2d_bytes += (int64_t)cnt * 2 * c->page_bytes;
+      st.h2d_bytes += (int64_t)pages_in * c->page_bytes;
       st.d2d_bytes += (int64_t)cnt * 2 * c->page_bytes;
       ++st.batches;
     }

@@ -19,7 +19,7 @@ class WorkingSetUpdater:
     def __init__(self, dims: api.Dims, dtype: int, index_cap: int, budget_blocks: int,
                  n_sink: int, n_recent: int, n_slots: int, max_pos: int, device,
                  rope_theta: float = 10000.0, rope_layout: int = 0, batch_blocks: int = 64,
-                 staging_blocks: int = 0):
+                 staging_blocks: int = 0, delta_limit: int = 0):
         import torch
         self.dims, self.dtype = dims, dtype
         self.cap, self.budget = index_cap, budget_blocks
@@ -33,10 +33,12 @@ class WorkingSetUpdater:
                                  dtype=tdt, device=device)
         self.k_view = torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device)
         self.v_view = torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device)
-        self.k_shadow = torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device)
+        # bounded delta re-RoPE (delta_limit > 0) keeps no raw-K shadow pages
+        self.k_shadow = (None if delta_limit > 0 else
+                         torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device))
         self.ctx = api.KvmCtx(dims, dtype, self.k_view, self.v_view, self.k_shadow, n_slots,
                               index_cap, max_pos, rope_theta, rope_layout, batch_blocks,
-                              staging_blocks)
+                              staging_blocks, delta_limit)
         self.sel = torch.empty(budget_blocks, dtype=torch.int32, device=device)
         self.n_sel = torch.empty(1, dtype=torch.int32, device=device)
         self.base_pos = torch.empty(budget_blocks, dtype=torch.int32, device=device)

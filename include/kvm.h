@@ -150,7 +150,7 @@ int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_
  *   k_shadow  the block's raw pre-RoPE K when its lower-tier copy is not in
  *             device memory (the re-encode source for hits whose compact
  *             position changes); blocks with a KVM_SRC_DEVICE copy are
- *             re-encoded from that copy instead
+ *             re-encoded from that copy instead. Unused with delta_limit > 0.
  * The ctx owns only host-side state, a side stream, events, a pinned staging
  * ring, a small device job list and the RoPE cos/sin table (fp64 angles,
  * rounded to fp32; positions [0, max_pos)). */
@@ -167,6 +167,14 @@ typedef struct {
   int64_t max_blocks;     /* block-record capacity (block ids < max_blocks) */
   int32_t batch_blocks;   /* misses per H2D batch / event (default 64 if <= 0) */
   int32_t staging_blocks; /* pinned ring capacity in blocks for gathered sources (>= 2*batch) */
+  int32_t delta_limit;    /* 0: every re-encode reads raw K (k_shadow required).
+                             n > 0: bounded delta re-RoPE (KVMem Sec. 4.4): a resident
+                             block whose compact position changes has its K page
+                             rotated in place by the shift, at most n times in a row;
+                             the next change rebuilds K from the block's raw K (its
+                             lower-tier copy, which must then exist) and resets the
+                             count. k_shadow is unused and may be NULL; staged raw K
+                             lands in the K page and is rotated there. */
 } kvm_ctx_desc;
 
 typedef struct kvm_ctx kvm_ctx;
@@ -180,6 +188,8 @@ typedef struct {
   int32_t batches;      /* H2D batches (events) issued */
   int64_t h2d_bytes;    /* bytes copied host -> device */
   int64_t d2d_bytes;    /* bytes read + written by the remat kernels */
+  int32_t deltas;       /* delta-mode rotations in place by a position shift */
+  int32_t rebuilds;     /* delta-mode re-encodes from raw K after the limit */
 } kvm_remat_stats;
 
 /* Host-gather callback for lower tiers that are not pinned (pageable or
@@ -252,6 +262,10 @@ int kvm_ctx_sync(kvm_ctx* ctx);
 /* Inspection: pool page of `block` (or -1) and its baked compact position
  * (-1 = K page stale). */
 int kvm_ctx_block_state(kvm_ctx* ctx, int64_t block, int32_t* slot, int32_t* baked_pos);
+
+/* Inspection (delta mode): delta rotations applied to `block`'s K page since
+ * it was last encoded from raw K (0 when not resident). */
+int kvm_ctx_block_deltas(kvm_ctx* ctx, int64_t block, int32_t* n_delta);
 
 /* Reclaim the pool pages of resident blocks [first_block, first_block + n_blocks)
  * (KVMem Sec. 4.4: a page can be reclaimed at once because the block keeps a

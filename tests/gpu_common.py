@@ -83,15 +83,17 @@ class Pool:
     """A page pool plus its context."""
 
     def __init__(self, k, wl, n_slots: int, max_blocks: int, max_pos: int, dev,
-                 batch_blocks: int = 64, staging_blocks: int = 0):
+                 batch_blocks: int = 64, staging_blocks: int = 0, delta_limit: int = 0):
         import torch
         dt = torch_dtype(wl)
         self.k_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
         self.v_view = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
-        self.k_shadow = torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev)
+        # bounded delta re-RoPE keeps no raw-K shadow pages
+        self.k_shadow = (None if delta_limit > 0 else
+                         torch.zeros((n_slots, wl.block_elems), dtype=dt, device=dev))
         self.ctx = k.KvmCtx(k.dims_for(wl), k.dtype_code(wl.dtype), self.k_view, self.v_view,
                             self.k_shadow, n_slots, max_blocks, max_pos, wl.theta,
-                            wl.rope_layout, batch_blocks, staging_blocks)
+                            wl.rope_layout, batch_blocks, staging_blocks, delta_limit)
         self.page = torch.full((n_slots,), -1, dtype=torch.int32, device=dev)
 
 

@@ -230,9 +230,11 @@ def test_select_error_paths(k, dev):
 
 # ------------------------------------------------------ rematerialization ----
 
-def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0):
+def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0, delta_limit=0,
+                 max_pos=None):
     import torch
-    pool = gc.Pool(k, wl, n_slots, N, wl.budget_blocks * wl.block_tokens, dev, batch, staging)
+    pool = gc.Pool(k, wl, n_slots, N, max_pos or wl.budget_blocks * wl.block_tokens, dev, batch,
+                   staging, delta_limit)
     keep = []
     if src == "device":
         rk = gc.raw_to_device(wl, "K", 0, N, dev)
@@ -295,6 +297,103 @@ def test_remat_view_matches_oracle(k, dev, src):
             assert p == old[b]               # GPU hits reuse their page in place
     assert len(set(pg2.tolist())) == n
     gc.check_view(wl, s2, pg2, pool)
+    pool.ctx.close()
+
+
+def _pair_error_in_bound(got, exact, n_delta, layout):
+    """Per (a, b) pair: |stored - exact| <= (n + 1) * sqrt(2)/2 ulp_bf16 of the
+    pair's length (each store rounds, rotations keep earlier error's length),
+    plus the fp32 rotation's own error. Returns the worst error in ulps."""
+    if layout == 0:
+        ea, eb = got[..., 0::2] - exact[..., 0::2], got[..., 1::2] - exact[..., 1::2]
+        na, nb = exact[..., 0::2], exact[..., 1::2]
+    else:
+        h = got.shape[-1] // 2
+        ea, eb = got[..., :h] - exact[..., :h], got[..., h:] - exact[..., h:]
+        na, nb = exact[..., :h], exact[..., h:]
+    err, norm = np.hypot(ea, eb), np.hypot(na, nb)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(1.1 * norm, 2.0 ** -100))) - 7)
+    bound = (n_delta + 1) * (np.sqrt(2) / 2 * ulp + 1e-6 * norm)
+    assert np.all(err <= bound)
+    return float(np.max(err / (2.0 ** (np.floor(np.log2(np.maximum(norm, 2.0 ** -100))) - 7))))
+
+
+@pytest.mark.parametrize("src", ["device", "pinned", "gather"])
+def test_delta_rerope_bounded_and_rebuilt(k, dev, src):
+    """Bounded delta re-RoPE (limit 2): three tracked blocks keep being selected
+    while the number of earlier blocks in the view changes, so their compact
+    positions shift; every third change rebuilds K from raw K."""
+    import torch
+    from oracle import bounded_delta_rope, rope_rotate
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    N, B, limit = 64, wl.block_tokens, 2
+    pool, keep = _remat_setup(k, dev, wl, N, 40, src, batch=4, staging=8, delta_limit=limit,
+                              max_pos=N * B)
+    assert pool.k_shadow is None
+    tracked = [30, 31, 45]
+    prefix = [5, 9, 2, 12, 12, 7, 3, 10]
+    placements = {}                                   # block -> base positions when selected
+    raw_k = {b: op.as_f64(synth.kv_blocks(wl, "K", b, 1)[0], "bf16") for b in range(N)}
+    for t, a in enumerate(prefix):
+        sel_list = list(range(a)) + tracked
+        for i, b in enumerate(sel_list):
+            placements.setdefault(b, []).append(i * B)
+        sel = torch.tensor(sel_list, dtype=torch.int32, device=dev)
+        n_sel = torch.tensor([len(sel_list)], dtype=torch.int32, device=dev)
+        st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+        torch.cuda.synchronize()
+        pg = pool.page.cpu().numpy()[:len(sel_list)]
+        kinds_now, worst = {}, 0.0
+        for i, b in enumerate(sel_list):
+            xs, kinds, counts = bounded_delta_rope(raw_k[b], placements[b], limit, "bf16")
+            kinds_now[b] = kinds[-1]
+            assert pool.ctx.kvm_ctx_block_deltas(b) == counts[-1]
+            got = op.as_f64(gc.to_host_bits(pool.k_view[int(pg[i])]).reshape(raw_k[b].shape),
+                            "bf16")
+            exact = rope_rotate(raw_k[b], i * B + np.arange(B))
+            worst = max(worst, _pair_error_in_bound(got, exact, counts[-1], wl.rope_layout))
+            if kinds[-1] == "full":
+                assert np.max(np.abs(got - exact)) <= 2e-2
+            v = gc.to_host_bits(pool.v_view[int(pg[i])])
+            assert np.array_equal(v, synth.kv_blocks(wl, "V", b, 1).reshape(-1))
+        want = {kd: sum(1 for x in kinds_now.values() if x == kd) for kd in ("delta", "full")}
+        misses = sum(1 for b in sel_list if len(placements[b]) == 1)
+        assert st["misses"] == misses and st["deltas"] == want["delta"]
+        assert st["rebuilds"] == want["full"] - misses
+        say(f"step {t}: prefix {a}, deltas {st['deltas']}, rebuilds {st['rebuilds']}, "
+            f"misses {st['misses']}, worst pair error {worst:.2f} ulp")
+    kinds_30 = bounded_delta_rope(raw_k[30], placements[30], limit, "bf16")[1]
+    assert kinds_30 == ["full", "delta", "delta", "full", "same", "delta", "delta", "full"]
+    pool.ctx.close()
+
+
+def test_delta_rerope_error_growth(k, dev):
+    """One block shifted 12 times with a limit of 12: the K error after n
+    deltas stays within (n + 1) * sqrt(2)/2 ulp per pair; the printed worst
+    errors show how it grows with the count."""
+    import torch
+    from oracle import rope_rotate
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    N, B = 40, wl.block_tokens
+    pool, keep = _remat_setup(k, dev, wl, N, 48, "device", delta_limit=12, max_pos=N * B)
+    raw = op.as_f64(synth.kv_blocks(wl, "K", 39, 1)[0], "bf16")
+    growth = []
+    for t, a in enumerate([0, 17, 3, 29, 8, 22, 1, 33, 12, 27, 5, 38, 14]):
+        sel_list = list(range(a)) + [39]
+        sel = torch.tensor(sel_list, dtype=torch.int32, device=dev)
+        n_sel = torch.tensor([len(sel_list)], dtype=torch.int32, device=dev)
+        pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+        torch.cuda.synchronize()
+        slot = int(pool.page.cpu().numpy()[len(sel_list) - 1])
+        got = op.as_f64(gc.to_host_bits(pool.k_view[slot]).reshape(raw.shape), "bf16")
+        exact = rope_rotate(raw, a * B + np.arange(B))
+        n = pool.ctx.kvm_ctx_block_deltas(39)
+        assert n == t
+        growth.append((n, _pair_error_in_bound(got, exact, n, wl.rope_layout),
+                       float(np.max(np.abs(got - exact)))))
+    say("delta count, worst pair error (ulp of the pair length), worst abs error:")
+    for n, e_ulp, e_abs in growth:
+        say(f"  {n:2d}  {e_ulp:5.2f}  {e_abs:.4f}")
     pool.ctx.close()
 
 
