@@ -106,7 +106,7 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
 // LAYOUT 1 (pairs (t, t+d/2)): pieces [t0, t0+P) and [t0+d/2, t0+d/2+P).
 // All loads of a workgroup's rows are issued before the first store; loads and
 // stores are plain (cached) ones, faster here than the non-temporal forms.
-template <typename T, int D, int LAYOUT>
+template <typename T, int D, int LAYOUT, bool DELTA>
 __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
   constexpr int TPR = D / (2 * P);               // threads per row
@@ -126,18 +126,19 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   const int t0 = LAYOUT == 0 ? tcol * 2 * P : tcol * P;            // first element
   const int off1 = LAYOUT == 0 ? P : D / 2;                         // second piece offset
   // (cos, sin) of the pairs this thread rotates, for each of its token indices;
-  // a delta job turns every token by the same shift (sin negated when < 0)
-  const bool delta = (job.flags & JOB_DELTA) != 0;
+  // launches of delta jobs turn every token by the job's signed shift instead
+  // (table entry |shift|, sin negated for a negative shift)
   const int32_t shift = job.pos < 0 ? -job.pos : job.pos;
+  const float ssign = DELTA && job.pos < 0 ? -1.0f : 1.0f;
   float2 cs[NJ][NC];
 #pragma unroll
   for (int s = 0; s < NJ; ++s) {
     const int j = (trow + s * RPI) & 31;
-    const float2* row = a.table + (int64_t)(delta ? shift : job.pos + j) * HALF;
+    const float2* row = a.table + (int64_t)(DELTA ? shift : job.pos + j) * HALF;
 #pragma unroll
     for (int q = 0; q < NC; ++q) {
       cs[s][q] = LAYOUT == 0 ? row[t0 / 2 + q] : row[t0 + q];
-      if (delta && job.pos < 0) cs[s][q].y = -cs[s][q].y;
+      if (DELTA) cs[s][q].y *= ssign;
     }
   }
   const int64_t page = (int64_t)job.slot * a.page_bytes;
@@ -192,13 +193,17 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   }
 }
 
-static void launch_remat(int32_t dtype, int32_t d, int32_t layout, const RematArgs& a,
-                         hipStream_t s) {
+static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta,
+                         const RematArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_jobs * a.wg_per_job;
   if (grid <= 0) return;
   dim3 g((uint32_t)grid), b(256);
   KernelTimer tm("remat", s);
-#define KVM_REMAT(T, D, LAY) remat_kernel<T, D, LAY><<<g, b, 0, s>>>(a)
+#define KVM_REMAT(T, D, LAY)                                                 \
+  do {                                                                       \
+    if (delta) remat_kernel<T, D, LAY, true><<<g, b, 0, s>>>(a);             \
+    else remat_kernel<T, D, LAY, false><<<g, b, 0, s>>>(a);                  \
+  } while (0)
   if (dtype == KVM_BF16) {
     if (d == 128) { if (layout == 0) KVM_REMAT(uint16_t, 128, 0); else KVM_REMAT(uint16_t, 128, 1); }
     else { if (layout == 0) KVM_REMAT(uint16_t, 64, 0); else KVM_REMAT(uint16_t, 64, 1); }
@@ -696,7 +701,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   size_t lru_pos = 0;
   kvm_remat_stats st{};
   st.n_sel = n;
-  std::vector<int32_t> hit_jobs, dev_jobs, dma_miss, gather_miss;
+  std::vector<int32_t> hit_jobs, delta_jobs, dev_jobs, dma_miss, gather_miss;
   RematJob* J = c->h_jobs;
   int32_t nj = 0;
   // Where staged raw K lands and is read by the kernel: the page's shadow, or
@@ -736,7 +741,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       } else if (r.baked >= 0 && r.n_delta < c->d.delta_limit) {
         // bounded delta re-RoPE: rotate the stored K by the position shift
         J[nj] = RematJob{kpage(r.slot), nullptr, r.slot, pos - r.baked, JOB_DELTA, 0};
-        hit_jobs.push_back(nj++);
+        delta_jobs.push_back(nj++);
         r.n_delta += 1;
         ++st.deltas;
       } else {
@@ -776,11 +781,13 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       staged_job(r, sl, pos, 0, i);
     }
   }
-  // Jobs are grouped: [hits + device misses][DMA misses][gathered misses].
+  // Jobs are grouped: [hits + device misses][delta shifts][DMA misses][gathered misses].
   std::vector<RematJob> ordered;
   ordered.reserve(nj);
   for (int32_t j : hit_jobs) ordered.push_back(J[j]);
   for (int32_t j : dev_jobs) ordered.push_back(J[j]);
+  const int32_t n_full = (int32_t)ordered.size();
+  for (int32_t j : delta_jobs) ordered.push_back(J[j]);
   const int32_t n_first = (int32_t)ordered.size();
   for (int32_t j : dma_miss) ordered.push_back(J[j]);
   for (int32_t j : gather_miss) ordered.push_back(J[j]);
@@ -800,17 +807,19 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   a.v_view = (char*)c->d.v_view;
   a.k_shadow = (char*)c->d.k_shadow;
   a.table = c->d_table;
-  auto launch_range = [&](int32_t first, int32_t count) -> int {
+  auto launch_range = [&](int32_t first, int32_t count, bool delta = false) -> int {
     if (count <= 0) return KVM_OK;
     a.jobs = c->d_jobs + first;
     a.n_jobs = count;
-    launch_remat(c->d.dtype, dm.head_dim, c->d.rope_layout, a, s);
+    launch_remat(c->d.dtype, dm.head_dim, c->d.rope_layout, delta, a, s);
     KVM_HIP(hipGetLastError());
     return KVM_OK;
   };
-  int rc = launch_range(0, n_first);
+  int rc = launch_range(0, n_full);
   if (rc) return rc;
-  st.d2d_bytes += (int64_t)hit_jobs.size() * 2 * c->page_bytes +
+  rc = launch_range(n_full, n_first - n_full, true);
+  if (rc) return rc;
+  st.d2d_bytes += (int64_t)(hit_jobs.size() + delta_jobs.size()) * 2 * c->page_bytes +
                   (int64_t)dev_jobs.size() * 4 * c->page_bytes;
   // 5. Misses from pinned host memory: DMA straight into the pages, batched.
   const int32_t bb = c->d.batch_blocks;

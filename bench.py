@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--pcie-steps", type=int, default=2,
                     help="steps of the pinned-host leg (0 to skip)")
+    ap.add_argument("--delta-steps", type=int, default=4,
+                    help="rematerializations timed in bounded delta re-RoPE mode (0: skip)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle sample")
     ap.add_argument("--cpu-pairs", type=int, default=6,
                     help="(layer, KV head) pairs in the CPU oracle sample")
@@ -475,6 +477,42 @@ def main():
     del ridx
     rope_ms = rt_ / max(rc_, 1)
     rope_gbps = nr * (page + L * wl.n_kv_heads * d * 2) / (rope_ms * 1e-3) / 1e9
+    # Delta re-RoPE leg: a second context in delta mode over the same pages; the
+    # view alternates between the selection and the selection without its first
+    # block, so every resident block is rotated in place by +-32 positions
+    delta = None
+    if args.delta_steps > 0:
+        ws.ctx.kvm_ctx_evict(0, wl.final_blocks)
+        dctx = k.KvmCtx(ws.dims, ws.dt, ws.k_view, ws.v_view, None, ws.k_view.shape[0],
+                        wl.final_blocks, (wl.budget_blocks + wl.reserve_blocks) * wl.block_tokens,
+                        wl.theta, wl.rope_layout, 64, 0, 1 << 20)
+        for i, b in enumerate(ws.hits):
+            dctx.kvm_ctx_set_source(int(b), 1, ws.hit_k[i], ws.hit_v[i], page, k.KVM_SRC_DEVICE)
+        for i, b in enumerate(ws.misses):
+            dctx.kvm_ctx_set_source(int(b), 1, ws.miss_k_d[i], ws.miss_v_d[i], page,
+                                    k.KVM_SRC_DEVICE)
+        sel_a = ws.sel[:n].clone()
+        sel_b = ws.sel[1:n].clone()
+        n_a = torch.tensor([n], dtype=torch.int32, device=dev)
+        n_b = torch.tensor([n - 1], dtype=torch.int32, device=dev)
+        dctx.kvm_rematerialize(sel_a, n_a, ws.page)
+        torch.cuda.synchronize()
+        k.kvm_profile_enable(True)
+        dst = None
+        for t in range(args.delta_steps):
+            dst = dctx.kvm_rematerialize(sel_b if t % 2 == 0 else sel_a,
+                                         n_b if t % 2 == 0 else n_a, ws.page)
+        torch.cuda.synchronize()
+        dc, dt_ = k.kvm_profile_read().get("remat", (0, float("nan")))
+        k.kvm_profile_enable(False)
+        dctx.close()
+        d_ms = dt_ / max(dc, 1)
+        d_bytes = dst["deltas"] * 2 * page
+        delta = {"avg_ms": d_ms, "deltas_per_call": dst["deltas"], "bytes": d_bytes,
+                 "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
+                 "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
+        ws.reset_pool()
     # PCIe leg: misses from pinned host memory
     pcie = None
     if args.pcie_steps > 0:
@@ -520,6 +558,7 @@ def main():
                   "hbm_frac": build_gbps / HBM_PEAK_GBPS},
         "build_rope": {"blocks": nr, "avg_ms": rope_ms, "GBps": rope_gbps,
                        "hbm_frac": rope_gbps / HBM_PEAK_GBPS},
+        "delta_rerope": delta,
         "pcie_leg": pcie,
         "kernels": kern,
     }
