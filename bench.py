@@ -225,9 +225,9 @@ def counter_traffic() -> dict:
     return out
 
 
-def traffic_for(traffic: dict, short: str):
+def traffic_for(traffic: dict, short: str, tail: str | None = None):
     for name, val in traffic.items():
-        if name.split("<")[0].endswith(short):
+        if name.split("<")[0].endswith(short) and (tail is None or name.endswith(tail)):
             return val
     return None
 
@@ -453,7 +453,7 @@ def main():
         if name == "remat":
             return {"kernel": name, "bound": "hbm", "achieved": remat_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS,
-                    "traffic": traffic_for(traffic, "remat_kernel")}
+                    "traffic": traffic_for(traffic, "remat_kernel", "false>")}
         return None
 
     dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
@@ -510,7 +510,8 @@ def main():
         d_bytes = dst["deltas"] * 2 * page
         delta = {"avg_ms": d_ms, "deltas_per_call": dst["deltas"], "bytes": d_bytes,
                  "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
-                 "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                 "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "traffic": traffic_for(counter_traffic(), "remat_kernel", "true>")}
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
     # PCIe leg: misses from pinned host memory
