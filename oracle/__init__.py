@@ -26,3 +26,4 @@ from .select import select_blocks, compact_positions, cutoff_margin  # noqa: F40
 from .rope import rope_frequencies, rope_rotate, rope_matrix, bounded_delta_rope  # noqa: F401
 from .plan import working_set_delta  # noqa: F401
 from .accounting import kv_bytes, index_bytes  # noqa: F401
+from .tier import simulate_host_tier  # noqa: F401
