@@ -16,13 +16,15 @@ KVM_OK, KVM_EINVAL, KVM_ENOMEM, KVM_EHIP, KVM_ERANGE, KVM_ENOTSUP = 0, -1, -2, -
 KVM_F32, KVM_BF16 = 0, 1
 KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED = 0, 1
 KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE = 0, 1, 2
+KVM_TIER_LRU, KVM_TIER_LRFU = 0, 1
 
 EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
     "kvm_select_ws_bytes", "kvm_select", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
     "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
-    "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_profile_enable", "kvm_profile_read",
+    "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_profile_enable",
+    "kvm_profile_read",
 ]
 
 
@@ -56,6 +58,11 @@ class RematStats(ctypes.Structure):
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class TierPolicy(ctypes.Structure):
+    _fields_ = [("policy", ctypes.c_int32), ("host_blocks", ctypes.c_int32),
+                ("lam", ctypes.c_double)]
 
 
 class KernelStat(ctypes.Structure):
@@ -100,6 +107,8 @@ def lib():
                                                    ctypes.POINTER(i32)]),
             "kvm_ctx_block_deltas": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32)]),
             "kvm_ctx_evict": (ctypes.c_int, [vp, i64, i64]),
+            "kvm_tier_simulate": (ctypes.c_int, [ctypes.POINTER(TierPolicy), i32, vp, vp, vp, vp,
+                                                 vp, vp, vp]),
             "kvm_profile_enable": (ctypes.c_int, [i32]),
             "kvm_profile_read": (ctypes.c_int, [ctypes.POINTER(KernelStat), i32,
                                                 ctypes.POINTER(i32)]),

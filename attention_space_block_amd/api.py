@@ -7,6 +7,7 @@ from . import _abi
 from ._abi import (  # noqa: F401
     Dims, KvmError, RematStats, KVM_F32, KVM_BF16, KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED,
     KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
+    KVM_TIER_LRU, KVM_TIER_LRFU,
 )
 
 
@@ -74,6 +75,29 @@ def kvm_select(scores, n_blocks: int, n_sink: int, n_recent: int, budget_blocks:
                                block_tokens, _ptr(sel), _ptr(n_sel), _ptr(base_pos), _ptr(ws),
                                ws_bytes, _stream(stream))
     _abi.check(rc, "kvm_select")
+
+
+def kvm_tier_simulate(policy: int, host_blocks: int, lam: float, steps) -> list:
+    """Host-tier admission over a trace; steps = [(new, sel, miss), ...], each an
+    ascending list of block ids. Returns [(host_hits, nvme_reads, demotions)]."""
+    import numpy as np
+
+    def csr(lists):
+        off = np.zeros(len(lists) + 1, dtype=np.int64)
+        off[1:] = np.cumsum([len(x) for x in lists])
+        blk = np.ascontiguousarray(np.concatenate([np.asarray(x, dtype=np.int32).reshape(-1)
+                                                   for x in lists] + [np.zeros(0, np.int32)]))
+        return off, blk
+    n = len(steps)
+    arrs = [csr([st[i] for st in steps]) for i in range(3)]
+    out = np.zeros((max(n, 1), 3), dtype=np.int32)
+    pol = _abi.TierPolicy(policy, host_blocks, lam)
+    ptr = lambda a: a.ctypes.data if a.size else None
+    rc = _abi.lib().kvm_tier_simulate(ctypes.byref(pol), n, ptr(arrs[0][0]), ptr(arrs[0][1]),
+                                      ptr(arrs[1][0]), ptr(arrs[1][1]), ptr(arrs[2][0]),
+                                      ptr(arrs[2][1]), out.ctypes.data)
+    _abi.check(rc, "kvm_tier_simulate")
+    return [tuple(int(v) for v in row) for row in out[:n]]
 
 
 def kvm_profile_enable(on: bool) -> None:

@@ -7,7 +7,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["api.hip", "profile.hip", "build_index.hip", "score.hip", "select.hip", "remat.hip"]
+SOURCES = ["api.hip", "profile.hip", "build_index.hip", "score.hip", "select.hip", "remat.hip",
+           "tier.cpp"]
 LIB = os.path.join(HERE, "libkvm.so")
 
 FLAGS = [

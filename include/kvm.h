@@ -274,6 +274,37 @@ int kvm_ctx_block_deltas(kvm_ctx* ctx, int64_t block, int32_t* n_delta);
 int kvm_ctx_evict(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks);
 
 /* ------------------------------------------------------------------------ */
+/* Host-tier admission (KVMem Sec. 4.4, hierarchical reuse): replay a trace of
+ * agent steps against a bounded host tier and count where GPU misses come
+ * from. Host memory only, no device work.
+ *
+ * Policies: KVM_TIER_LRU (evict the least recently touched block) and
+ * KVM_TIER_LRFU (recency and cumulative frequency: a block touched at
+ * t_1 < ... < t_k is worth sum_i 2^(-lambda (t - t_i)); evict the least
+ * worth; lambda = 0 is LFU, lambda = 1 orders like LRU). Ties evict the lowest
+ * block id.
+ * Trace (three CSR lists over n_steps steps; offsets int64[n_steps + 1]
+ * starting at 0, each step a strictly ascending list of block ids >= 0):
+ *   new:  blocks prefilled at the step, staged out to the host (admitted);
+ *   sel:  the step's selection (every block touched once per step);
+ *   miss: selected blocks the GPU pool lacked (must be in sel): a host copy
+ *         is a host hit, else an NVMe read that admits the block.
+ * Admission into a full host tier first demotes the block with the lowest
+ * worth to NVMe. out: int32[n_steps][3] = host hits, NVMe reads, demotions.
+ * Errors: KVM_EINVAL (pointers, policy, capacity < 1, lambda < 0, malformed
+ * lists, a miss outside its selection). */
+enum { KVM_TIER_LRU = 0, KVM_TIER_LRFU = 1 };
+typedef struct {
+  int32_t policy;
+  int32_t host_blocks;   /* host-tier capacity in blocks */
+  double lambda;         /* LRFU decay per step */
+} kvm_tier_policy;
+
+int kvm_tier_simulate(const kvm_tier_policy* policy, int32_t n_steps, const int64_t* new_off,
+                      const int32_t* new_blk, const int64_t* sel_off, const int32_t* sel_blk,
+                      const int64_t* miss_off, const int32_t* miss_blk, int32_t* out);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (tracing aid). While enabled, every kernel launch of the
  * library is bracketed by a HIP event pair on its stream. kvm_profile_read
  * waits for the recorded events and returns, per kernel name, the number of

@@ -33,7 +33,7 @@ import math
 def simulate_host_tier(steps, host_blocks: int, policy: str, lam: float = 0.0):
     """steps: list of (new, sel, miss) block lists; policy "lru" or "lrfu"."""
     assert host_blocks >= 1 and policy in ("lru", "lrfu")
-    last, crf = {}, {}
+    last, crf, key = {}, {}, {}
     host = set()
     out = []
 
@@ -44,18 +44,14 @@ def simulate_host_tier(steps, host_blocks: int, policy: str, lam: float = 0.0):
             prev = crf.get(b)
             crf[b] = 1.0 if prev is None else 1.0 + 2.0 ** (-lam * (t - last[b])) * prev
         last[b] = t
-
-    def key(b):
-        if policy == "lru":
-            return last[b]
-        return math.log2(crf[b]) + lam * last[b]
+        key[b] = t if policy == "lru" else math.log2(crf[b]) + lam * t
 
     def admit(b):
         demoted = 0
         if b in host:
             return 0
         if len(host) >= host_blocks:
-            victim = min(host, key=lambda x: (key(x), x))
+            victim = min(host, key=lambda x: (key[x], x))
             host.remove(victim)
             demoted = 1
         host.add(b)
