@@ -332,6 +332,7 @@ def run_churn(args, k, wl, dev):
     new_k = torch.empty((wl.append_blocks, wl.block_elems), dtype=torch.int16, device=dev)
     new_v = torch.empty_like(new_k)
     rows, prev = [], None
+    trace = []                  # (new, selection, GPU misses) per step, for the host-tier replay
     k.kvm_profile_enable(True)
     for t in range(steps):
         q = torch.from_numpy(synth.query(wl, step=t).view(np.int16)).to(dev)
@@ -343,13 +344,24 @@ def run_churn(args, k, wl, dev):
                 np.int16).reshape(wl.append_blocks, -1)))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        new_ids = []
         if t > 0:
+            new_ids = list(range(upd.n_blocks, upd.n_blocks + wl.append_blocks))
             upd.append(new_k, new_v, wl.append_blocks)
-        st = upd.update(q, wl.n_q_tokens)
+        upd.score(q, wl.n_q_tokens)
+        upd.select()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         n = int(upd.n_sel.item())
         sel = upd.sel.cpu().numpy()[:n]
+        # outside the timed region: which selected blocks the GPU pool lacks
+        miss_ids = [int(b) for b in sel if upd.ctx.kvm_ctx_block_state(int(b))[0] < 0]
+        trace.append((new_ids, sel.tolist(), miss_ids))
+        t0 = time.perf_counter()
+        st = upd.rematerialize()
+        torch.cuda.synchronize()
+        dt += time.perf_counter() - t0
+        assert st["misses"] == len(miss_ids)
         cand = set(sel[(sel >= wl.n_sink) & (sel < upd.n_blocks - wl.n_recent)].tolist())
         ov = None if prev is None else len(cand & prev) / max(1, len(cand))
         prev = cand
@@ -359,6 +371,20 @@ def run_churn(args, k, wl, dev):
     prof = k.kvm_profile_read()
     k.kvm_profile_enable(False)
     upd.close()
+    # Host-tier admission on the recorded trace (KVMem Sec. 4.4): NVMe reads of the
+    # GPU misses for host tiers of 1x, 2x and 4x the view, LRU vs LRFU
+    tier = []
+    for cap in (Kb, 2 * Kb, 4 * Kb):
+        for name, code, lam in (("lru", k.KVM_TIER_LRU, 0.0), ("lrfu", k.KVM_TIER_LRFU, 0.02),
+                                ("lrfu", k.KVM_TIER_LRFU, 0.1), ("lrfu", k.KVM_TIER_LRFU, 0.5)):
+            t1 = time.perf_counter()
+            res = k.kvm_tier_simulate(code, cap, lam, trace)
+            sim_ms = (time.perf_counter() - t1) * 1e3
+            tier.append({"host_blocks": cap, "policy": name, "lambda": lam,
+                         "host_hits": sum(r[0] for r in res), "nvme_reads": sum(r[1] for r in res),
+                         "demotions": sum(r[2] for r in res), "sim_ms": sim_ms})
+            log(f"host tier {cap} blocks, {name} {lam}: NVMe reads {tier[-1]['nvme_reads']}, "
+                f"host hits {tier[-1]['host_hits']}")
     later = rows[1:] if len(rows) > 1 else rows
     ms = sum(r["ms"] for r in later) / len(later)
     ovs = [r["overlap"] for r in rows if r["overlap"] is not None]
@@ -373,6 +399,7 @@ def run_churn(args, k, wl, dev):
         "mean_overlap": sum(ovs) / len(ovs) if ovs else None,
         "mean_hits": sum(r["hits"] for r in later) / len(later),
         "mean_misses": sum(r["misses"] for r in later) / len(later),
+        "host_tier": tier,
         "steps_detail": rows,
         "kernels": {n: {"launches": c, "avg_ms": t / c} for n, (c, t) in prof.items()},
     }
