@@ -40,3 +40,41 @@ def round_to_dtype(x, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+# ---- FP8 E4M3 (OCP "E4M3FN"): 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+# no infinities, S.1111.111 is NaN, largest finite 448, subnormals m * 2^-9.
+
+def fp8_decode(bits) -> np.ndarray:
+    """Values of E4M3FN bytes (float64; NaN for 0x7F / 0xFF)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    s = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 0xF) & (m == 0x7), np.nan, val)
+    return s * val
+
+
+def fp8_encode(x) -> np.ndarray:
+    """Nearest E4M3FN byte, ties to even, saturating to +-448 (the largest
+    finite value) beyond the range. Works on the exact float64 input: the
+    finite codes are enumerated and the nearest one chosen, the even mantissa
+    (lower code) on ties."""
+    x = np.asarray(x, dtype=np.float64)
+    codes = np.arange(0x7F, dtype=np.uint8)                 # 0 .. 448, ascending values
+    vals = fp8_decode(codes)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(vals, a, side="left")             # first value >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    exact = vals[hi] == a
+    c = np.where(exact | pick_hi, codes[hi], codes[lo]).astype(np.uint8)
+    return np.where(np.signbit(x), c | 0x80, c).astype(np.uint8)   # sign kept, also on zero
+
+
+def fp8_round(x) -> np.ndarray:
+    """x rounded to the nearest E4M3FN value (ties to even, saturating)."""
+    return fp8_decode(fp8_encode(x))

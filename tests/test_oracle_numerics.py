@@ -55,3 +55,40 @@ def test_bits_roundtrip():
     v = bf16_round(np.array([1.5, -0.75, 3.140625]))
     assert list(bf16_bits(v)) == [0x3FC0, 0xBF40, 0x4049]
     assert np.array_equal(from_bf16_bits(bf16_bits(v)), v)
+
+
+# ---- FP8 E4M3FN ----
+
+def test_fp8_decode_table_landmarks():
+    from oracle.numerics import fp8_decode
+    v = fp8_decode(np.arange(256, dtype=np.uint8))
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0           # largest finite
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9    # smallest normal / subnormal
+    assert v[0x38] == 1.0 and v[0x39] == 1.125 and v[0x40] == 2.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])          # the only NaNs, no infinities
+    fin = v[:0x7F]
+    assert np.all(np.diff(fin) > 0)                          # codes 0..0x7E ascend
+    assert np.array_equal(v[0x80:0xFF], -fin[:0x7F])
+
+
+def test_fp8_encode_exact_nearest_ties_even_saturate():
+    from fractions import Fraction
+    from oracle.numerics import fp8_decode, fp8_encode
+    vals = [Fraction(float(x)) for x in fp8_decode(np.arange(0x7F, dtype=np.uint8))]
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([rng.standard_normal(400) * 3, rng.standard_normal(200) * 0.01,
+                         (np.array(vals[1:], dtype=float) + np.array(vals[:-1], dtype=float)) / 2])
+    for x in xs:
+        a = min(Fraction(abs(float(x))), Fraction(448))
+        d = [abs(a - v) for v in vals]
+        best = min(range(len(vals)), key=lambda i: (d[i], i % 2))   # nearest, even code on ties
+        code = int(fp8_encode(x))
+        assert code & 0x7F == best and (code >> 7) == (1 if np.signbit(x) else 0)
+    assert fp8_encode(1000.0) == 0x7E and fp8_encode(-1e9) == 0xFE
+    assert fp8_encode(-0.0) == 0x80 and fp8_encode(-1e-6) == 0x80
+
+
+def test_fp8_round_trip_of_every_finite_code():
+    from oracle.numerics import fp8_decode, fp8_encode
+    fin = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(fp8_encode(fp8_decode(fin)), fin)
