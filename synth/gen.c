@@ -28,6 +28,7 @@
  */
 #include <stdint.h>
 #include <string.h>
+#include <math.h>
 #include <omp.h>
 
 #define GOLDEN 0x9e3779b97f4a7c15ULL
@@ -100,6 +101,29 @@ static inline uint16_t to_bf16(float x) {
   return (uint16_t)(u >> 16);
 }
 
+/* Nearest FP8 E4M3 (OCP "E4M3FN": bias 7, 3 mantissa bits, largest finite 448,
+ * no infinities) code of x, ties to even, saturating to +-448; the sign is kept
+ * (also on zero). Subnormals step by 2^-9. */
+static inline uint8_t to_e4m3(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  const uint8_t sign = (uint8_t)((u >> 24) & 0x80u);
+  const float a = fabsf(x);
+  if (!(a < 464.0f)) return sign | 0x7Eu;       /* 464 ties down to 448; beyond: saturate */
+  if (a < 0.015625f)                             /* below 2^-6: multiples of 2^-9 */
+    return sign | (uint8_t)(int)nearbyintf(a * 512.0f);
+  int e;
+  frexpf(a, &e);                                 /* a = f * 2^e, f in [0.5, 1) */
+  int E = e - 1;                                 /* a in [2^E, 2^(E+1)) */
+  int q = (int)nearbyintf(ldexpf(a, 3 - E));     /* 8 .. 16, ties to even */
+  if (q == 16) {
+    q = 8;
+    E += 1;
+  }
+  if (E > 8 || (E == 8 && q > 14)) return sign | 0x7Eu;
+  return sign | (uint8_t)(((E + 7) << 3) | (q - 8));
+}
+
 /* out[i] = unit(key, e0 + i), fp32 */
 void synth_unit_f32(uint64_t key, uint64_t e0, int64_t n, float* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = unit_at(key, e0 + (uint64_t)i);
@@ -109,7 +133,7 @@ void synth_unit_f32(uint64_t key, uint64_t e0, int64_t n, float* out) {
  * value(b,l,g,j,t) = unit(key(seed, tensor, b, l*Hkv+g), j*d+t)
  *                  + off_sigma * unit(key(seed, off_tensor, b, l*Hkv+g), t)
  * (the offset term is skipped when off_sigma == 0).
- * dtype 0: fp32 output, 1: bf16 (uint16 bits) output.
+ * dtype 0: fp32 output, 1: bf16 (uint16 bits) output, 2: FP8 E4M3 (bytes).
  * Block b0+i is written at (char*)out + i*block_stride_bytes. */
 void synth_kv_blocks(uint64_t seed, int32_t tensor, int32_t off_tensor, float off_sigma,
                      int64_t b0, int64_t nb, int32_t L, int32_t Hkv, int32_t B,
@@ -138,6 +162,9 @@ void synth_kv_blocks(uint64_t seed, int32_t tensor, int32_t off_tensor, float of
       if (dtype == 0) {
         float* o = (float*)blk + lg * (int64_t)B * d + e;
         for (int64_t i2 = 0; i2 < n; ++i2) o[i2] = use_off ? xs[i2] + off[i2 % d] : xs[i2];
+      } else if (dtype == 2) {
+        uint8_t* o = (uint8_t*)blk + lg * (int64_t)B * d + e;
+        for (int64_t i2 = 0; i2 < n; ++i2) o[i2] = to_e4m3(use_off ? xs[i2] + off[i2 % d] : xs[i2]);
       } else {
         add_row_offset_to_bf16(xs, off, rows_here, d, use_off,
                                (uint16_t*)blk + lg * (int64_t)B * d + e);
@@ -210,7 +237,7 @@ typedef struct {
 
 int synth_gather_kv(void* user, int64_t block, int32_t which, void* dst) {
   const synth_store* s = (const synth_store*)user;
-  const int64_t bytes = (int64_t)s->L * s->Hkv * s->B * s->d * (s->dtype == 0 ? 4 : 2);
+  const int64_t bytes = (int64_t)s->L * s->Hkv * s->B * s->d * (s->dtype == 0 ? 4 : s->dtype == 2 ? 1 : 2);
   synth_kv_blocks(s->seed, which == 0 ? 1 : 2, which == 0 ? 3 : 4, s->off_sigma, block, 1,
                   s->L, s->Hkv, s->B, s->d, s->dtype, dst, bytes, 1);
   return 0;

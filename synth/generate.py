@@ -28,7 +28,7 @@ def build_library(force: bool = False) -> str:
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-shared", "-fPIC", _SRC, "-o", tmp]
+               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -75,11 +75,11 @@ def unit_stream(key: int, e0: int, n: int) -> np.ndarray:
 
 
 def _dtype_code(dtype: str) -> int:
-    return 0 if dtype == "f32" else 1
+    return {"f32": 0, "bf16": 1, "fp8": 2}[dtype]
 
 
 def _np_dtype(dtype: str):
-    return np.float32 if dtype == "f32" else np.uint16
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
 
 
 def kv_blocks(wl: Workload, which: str, b0: int, nb: int, out: np.ndarray | None = None,
@@ -148,13 +148,13 @@ def query(wl: Workload, step: int = 0, shift: np.ndarray | None = None,
         tensor = TENSOR["QSTEP"] + step
         if shift is None:
             shift = churn_shift(wl, step)
-    out = np.empty((L, Hq, T, d), dtype=_np_dtype(wl.dtype))
+    out = np.empty((L, Hq, T, d), dtype=_np_dtype(wl.index_dtype))
     sp = None
     if shift is not None:
         shift = np.ascontiguousarray(shift, dtype=np.float32)
         assert shift.shape == (L, Hq, d)
         sp = _ptr(shift)
-    _load().synth_query(wl.seed, tensor, L, Hq, T, d, sp, _dtype_code(wl.dtype), _ptr(out),
+    _load().synth_query(wl.seed, tensor, L, Hq, T, d, sp, _dtype_code(wl.index_dtype), _ptr(out),
                         nthreads or default_threads())
     return out
 

@@ -42,6 +42,24 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
             ).astype(np.uint16)
 
 
+def to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 (OCP E4M3FN) codes of fp32 values: nearest, ties to even,
+    saturating to +-448, sign kept."""
+    x = np.asarray(x, dtype=np.float32)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.int64)
+    a = np.abs(x).astype(np.float32)
+    sub = np.rint(a * np.float32(512.0)).astype(np.int64)            # below 2^-6
+    f, e = np.frexp(a)                                                # a = f * 2^e
+    E = e.astype(np.int64) - 1
+    q = np.rint(np.ldexp(a, (3 - E).astype(np.int32))).astype(np.int64)
+    E = np.where(q == 16, E + 1, E)
+    q = np.where(q == 16, 8, q)
+    norm = ((E + 7) << 3) | (q - 8)
+    code = np.where(a < np.float32(0.015625), sub, norm)
+    code = np.where((a >= np.float32(464.0)) | (E > 8) | ((E == 8) & (q > 14)), 0x7E, code)
+    return (sign | code).astype(np.uint8)
+
+
 def kv_block(seed, tensor, off_tensor, off_sigma, b, L, Hkv, B, d, dtype):
     out = np.empty((L, Hkv, B, d), dtype=np.float32)
     for l in range(L):
@@ -52,4 +70,6 @@ def kv_block(seed, tensor, off_tensor, off_sigma, b, L, Hkv, B, d, dtype):
                 o = np.float32(off_sigma) * unit(key(seed, off_tensor, b, lg), 0, d)
                 x = (x + o[None, :]).astype(np.float32)
             out[l, g] = x
+    if dtype == "fp8":
+        return to_e4m3_bits(out)
     return out if dtype == "f32" else to_bf16_bits(out)

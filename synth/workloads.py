@@ -34,7 +34,8 @@ class Workload:
     n_kv_heads: int
     n_q_heads: int
     head_dim: int
-    dtype: str            # "f32" or "bf16": the dtype of raw K/V, index and q
+    dtype: str            # "f32", "bf16" or "fp8" (E4M3): the dtype of raw K/V (and of the
+                          # index and q, which are bf16 for fp8 K/V)
     n_blocks: int         # history blocks at the (first) scoring step
     n_q_tokens: int
     n_sink: int
@@ -60,8 +61,13 @@ class Workload:
         return self.n_q_heads // self.n_kv_heads
 
     @property
+    def index_dtype(self) -> str:
+        """dtype of the Mean-K index and the queries: bf16 when K/V are fp8."""
+        return "bf16" if self.dtype == "fp8" else self.dtype
+
+    @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
     @property
     def block_elems(self) -> int:
@@ -74,7 +80,7 @@ class Workload:
 
     @property
     def index_row_bytes(self) -> int:
-        return self.head_dim * self.elem_bytes
+        return self.head_dim * (4 if self.index_dtype == "f32" else 2)
 
     @property
     def final_blocks(self) -> int:
@@ -106,6 +112,10 @@ WORKLOADS = {
 # budget and step structure at 1/16 of the scoring work, so the CPU oracle can
 # produce every step's expected selection.
 WORKLOADS["churn_l4"] = WORKLOADS["churn"].scaled(name="churn_l4", n_layers=4, steps=8)
+# FP8 (E4M3) K/V pages, as the pages' engine runs its KV cache: the same values
+# as the bf16 workspaces, rounded to FP8 instead of bf16; index and q stay bf16.
+WORKLOADS["ctx64k_fp8"] = WORKLOADS["ctx64k"].scaled(name="ctx64k_fp8", dtype="fp8")
+WORKLOADS["ws1m_fp8"] = WORKLOADS["ws1m"].scaled(name="ws1m_fp8", dtype="fp8")
 
 
 def get_workload(name: str) -> Workload:

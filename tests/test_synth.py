@@ -25,6 +25,18 @@ def test_kv_blocks_match_numpy_restatement_bf16_and_f32():
     assert np.array_equal(got[1].view(np.uint32), want.view(np.uint32))
 
 
+def test_kv_blocks_match_numpy_restatement_fp8():
+    wl = synth.get_workload("ctx64k_fp8")
+    got = synth.kv_blocks(wl, "K", 7, 2)
+    want = ref.kv_block(wl.seed, 1, 3, 0.5, 8, wl.n_layers, wl.n_kv_heads, 32, wl.head_dim, "fp8")
+    assert got.dtype == np.uint8 and np.array_equal(got[1], want)
+    # the encoder on its own: ties to even, subnormals, saturation, signed zero
+    x = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -11, 463.9, 464.0, 1e6, -0.0, -1e-7,
+                  -500.0], dtype=np.float32)
+    assert ref.to_e4m3_bits(x).tolist() == [0x38, 0x3A, 0x00, 0x01, 0x7E, 0x7E, 0x7E, 0x80, 0x80,
+                                            0xFE]
+
+
 def test_any_block_regenerates_alone():
     wl = synth.get_workload("ctx64k")
     many = synth.kv_blocks(wl, "K", 100, 8)
