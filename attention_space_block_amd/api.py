@@ -5,7 +5,8 @@ import ctypes
 
 from . import _abi
 from ._abi import (  # noqa: F401
-    Dims, KvmError, RematStats, KVM_F32, KVM_BF16, KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED,
+    Dims, KvmError, RematStats, KVM_F32, KVM_BF16, KVM_FP8_E4M3, KVM_INDEX_DEVICE,
+    KVM_INDEX_HOST_TILED,
     KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
     KVM_TIER_LRU, KVM_TIER_LRFU,
 )
@@ -34,7 +35,7 @@ def dims_for(wl) -> Dims:
 
 
 def dtype_code(dtype: str) -> int:
-    return KVM_F32 if dtype == "f32" else KVM_BF16
+    return {"f32": KVM_F32, "bf16": KVM_BF16, "fp8": KVM_FP8_E4M3}[dtype]
 
 
 def kvm_version() -> int:

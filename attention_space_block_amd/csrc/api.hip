@@ -18,7 +18,8 @@ void clear_error() { g_err[0] = 0; }
 
 int check_dims(const kvm_dims* d, int32_t dtype) {
   KVM_CHECK_ARG(d != nullptr, "dims is NULL");
-  KVM_CHECK_ARG(dtype == KVM_F32 || dtype == KVM_BF16, "dtype %d invalid", dtype);
+  KVM_CHECK_ARG(dtype == KVM_F32 || dtype == KVM_BF16 || dtype == KVM_FP8_E4M3,
+                "dtype %d invalid", dtype);
   KVM_CHECK_ARG(d->n_layers > 0 && d->n_kv_heads > 0 && d->n_q_heads > 0,
                 "layers/heads must be positive");
   KVM_CHECK_ARG(d->n_q_heads % d->n_kv_heads == 0, "n_q_heads %% n_kv_heads != 0");

@@ -35,6 +35,18 @@ __device__ __forceinline__ void widen<uint16_t>(const uint4& v, double* out) {
 }
 
 template <>
+__device__ __forceinline__ void widen<uint8_t>(const uint4& v, double* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float x[4];
+    fp8x4_to_f32(w[i], x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * i + e] = (double)x[e];
+  }
+}
+
+template <>
 __device__ __forceinline__ void widen<float>(const uint4& v, double* out) {
   out[0] = (double)__uint_as_float(v.x);
   out[1] = (double)__uint_as_float(v.y);
@@ -60,6 +72,27 @@ __device__ __forceinline__ uint4 store_mean<float>(const double* acc) {
                     __float_as_uint((float)(acc[1] * (1.0 / 32.0))),
                     __float_as_uint((float)(acc[2] * (1.0 / 32.0))),
                     __float_as_uint((float)(acc[3] * (1.0 / 32.0))));
+}
+
+// Index element type for K of element type T: bf16 for FP8 K.
+template <typename T>
+struct IndexOf {
+  using type = T;
+};
+template <>
+struct IndexOf<uint8_t> {
+  using type = uint16_t;
+};
+
+// Store the P = 16 / sizeof(T) means of a lane's piece as index elements.
+template <typename T>
+__device__ __forceinline__ void store_means(const double* acc, typename IndexOf<T>::type* dst) {
+  constexpr int P = 16 / sizeof(T);
+  using TI = typename IndexOf<T>::type;
+  constexpr int PER = 16 / sizeof(TI);          // index elements per 16-byte store
+#pragma unroll
+  for (int c = 0; c < P / PER; ++c)
+    *reinterpret_cast<uint4*>(dst + c * PER) = store_mean<TI>(acc + c * PER);
 }
 
 template <typename T, int D>
@@ -113,6 +146,76 @@ __global__ __launch_bounds__(256) void build_index_kernel(const char* __restrict
   }
 }
 
+// FP8 E4M3 raw K: every value is a multiple of 2^-9 below 448 in magnitude,
+// so any partial sum of a column's 32 values (|sum| < 2^14) is exact in fp32;
+// the mean (sum / 32, exact) is rounded once to bf16. One wavefront per
+// (block, l, g); lanes decode 16 values per 16-byte load with the hardware
+// conversion and fold across the lanes sharing a column with xor-shuffles.
+template <int D>
+__global__ __launch_bounds__(256) void build_index_fp8_kernel(const char* __restrict__ k_raw,
+                                                              int64_t block_stride,
+                                                              int64_t n_blocks, int32_t nlg,
+                                                              int64_t first_block, int64_t cap,
+                                                              uint16_t* __restrict__ index) {
+  constexpr int VEC = 16;                        // fp8 values per 16-byte load
+  constexpr int LPR = D / VEC;                   // lanes per row
+  constexpr int RPI = 64 / LPR;                  // rows per wave-wide load
+  constexpr int ITERS = 32 / RPI;                // loads per lane (B = 32)
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (i, lg) pair
+  if (row >= n_blocks * nlg) return;
+  const int64_t i = row / nlg;
+  const int32_t lg = (int32_t)(row % nlg);
+  const char* src = k_raw + i * block_stride + (int64_t)lg * 32 * D;
+  const int col = lane % LPR;
+  const int r0 = lane / LPR;
+  uint4 v[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it)
+    v[it] = ld_nt(src + (int64_t)(r0 + it * RPI) * D + col * VEC);
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float x[4];
+      fp8x4_to_f32(w[q], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q + e] += x[e];
+    }
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (r0 == 0) {
+    uint16_t* dst = index + ((int64_t)lg * cap + first_block + i) * D + col * VEC;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        w[p] = (uint32_t)f32_to_bf16(acc[8 * c + 2 * p] * (1.0f / 32.0f)) |
+               ((uint32_t)f32_to_bf16(acc[8 * c + 2 * p + 1] * (1.0f / 32.0f)) << 16);
+      *reinterpret_cast<uint4*>(dst + 8 * c) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int D>
+static void launch_build_fp8(const void* k_raw, int64_t stride, int64_t n, int32_t nlg,
+                             int64_t first, int64_t cap, void* index, hipStream_t s) {
+  const int64_t grid = (n * nlg + 3) / 4;
+  KernelTimer tm("build_index", s);
+  build_index_fp8_kernel<D><<<dim3((uint32_t)grid), dim3(256), 0, s>>>(
+      reinterpret_cast<const char*>(k_raw), stride, n, nlg, first, cap,
+      reinterpret_cast<uint16_t*>(index));
+}
+
 template <typename T, int D>
 static void launch_build(const void* k_raw, int64_t stride, int64_t n, int32_t nlg, int64_t first,
                          int64_t cap, void* index, hipStream_t s) {
@@ -142,7 +245,7 @@ template <typename T, int D, int LAYOUT>
 __global__ __launch_bounds__(256) void build_index_rope_kernel(
     const char* __restrict__ k_rope, int64_t block_stride, int64_t n_blocks, int32_t nlg,
     int32_t wg_per_block, int64_t pos0, const float2* __restrict__ table, int64_t first_block,
-    int64_t cap, T* __restrict__ index) {
+    int64_t cap, typename IndexOf<T>::type* __restrict__ index) {
   constexpr int P = 16 / sizeof(T);           // elements per piece
   constexpr int TPU = D / (2 * P);            // lanes per unit
   constexpr int UPW = 64 / TPU;               // units per wave
@@ -210,9 +313,9 @@ __global__ __launch_bounds__(256) void build_index_rope_kernel(
     }
   }
   if (active) {
-    T* dst = index + ((int64_t)lg * cap + first_block + i) * D;
-    *reinterpret_cast<uint4*>(dst + t0) = store_mean<T>(acc0);
-    *reinterpret_cast<uint4*>(dst + t0 + off1) = store_mean<T>(acc1);
+    typename IndexOf<T>::type* dst = index + ((int64_t)lg * cap + first_block + i) * D;
+    store_means<T>(acc0, dst + t0);
+    store_means<T>(acc1, dst + t0 + off1);
   }
 }
 
@@ -235,8 +338,11 @@ int launch_build_rope(int32_t dtype, int32_t d, int32_t layout, const void* k_ro
 #define KVM_BR(T, D, LAY)                                                                   \
   build_index_rope_kernel<T, D, LAY><<<dim3((uint32_t)grid), dim3(256), 0, s>>>(            \
       src, stride, n_blocks, nlg, wg_per_block, pos0, tb, first_block, cap,                \
-      reinterpret_cast<T*>(index))
-  if (dtype == KVM_BF16) {
+      reinterpret_cast<typename IndexOf<T>::type*>(index))
+  if (dtype == KVM_FP8_E4M3) {
+    if (d == 128) { if (layout == 0) KVM_BR(uint8_t, 128, 0); else KVM_BR(uint8_t, 128, 1); }
+    else { if (layout == 0) KVM_BR(uint8_t, 64, 0); else KVM_BR(uint8_t, 64, 1); }
+  } else if (dtype == KVM_BF16) {
     if (d == 128) { if (layout == 0) KVM_BR(uint16_t, 128, 0); else KVM_BR(uint16_t, 128, 1); }
     else { if (layout == 0) KVM_BR(uint16_t, 64, 0); else KVM_BR(uint16_t, 64, 1); }
   } else {
@@ -272,7 +378,14 @@ extern "C" int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* 
                 "grid too large");
   const int32_t nlg = dims->n_layers * dims->n_kv_heads;
   hipStream_t s = as_stream(stream);
-  if (dtype == KVM_BF16) {
+  if (dtype == KVM_FP8_E4M3) {
+    if (dims->head_dim == 128)
+      launch_build_fp8<128>(k_raw, k_block_stride, n_blocks, nlg, first_block, index_cap_blocks,
+                            index, s);
+    else
+      launch_build_fp8<64>(k_raw, k_block_stride, n_blocks, nlg, first_block, index_cap_blocks,
+                           index, s);
+  } else if (dtype == KVM_BF16) {
     if (dims->head_dim == 128)
       launch_build<uint16_t, 128>(k_raw, k_block_stride, n_blocks, nlg, first_block,
                                   index_cap_blocks, index, s);

@@ -36,7 +36,11 @@ void clear_error();
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-inline int dtype_bytes(int32_t dtype) { return dtype == KVM_F32 ? 4 : 2; }
+inline int dtype_bytes(int32_t dtype) {
+  return dtype == KVM_F32 ? 4 : dtype == KVM_FP8_E4M3 ? 1 : 2;
+}
+// dtype of the Mean-K index rows for K of `dtype` (bf16 for FP8 K)
+inline int32_t index_dtype(int32_t dtype) { return dtype == KVM_FP8_E4M3 ? KVM_BF16 : dtype; }
 
 // Validate dims shared by every entry point.
 int check_dims(const kvm_dims* d, int32_t dtype);
@@ -79,6 +83,28 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
   if (e8 <= 0) return (uint16_t)(sign << 15);    // below bf16 normal range
   if (e8 >= 255) return (uint16_t)((sign << 15) | 0x7f80u);
   return (uint16_t)((sign << 15) | ((uint64_t)e8 << 7) | keep);
+}
+
+// FP8 E4M3 (OCP E4M3FN) <-> fp32 with the gfx950 conversion instructions:
+// decoding is exact; encoding rounds to nearest, ties to even, after a clamp
+// to +-448 (so out-of-range values saturate instead of becoming NaN).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* x) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  x[0] = lo.x;
+  x[1] = lo.y;
+  x[2] = hi.x;
+  x[3] = hi.y;
+}
+__device__ __forceinline__ uint32_t f32x4_to_fp8(const float* x) {
+  const float a0 = __builtin_amdgcn_fmed3f(x[0], -448.0f, 448.0f);
+  const float a1 = __builtin_amdgcn_fmed3f(x[1], -448.0f, 448.0f);
+  const float a2 = __builtin_amdgcn_fmed3f(x[2], -448.0f, 448.0f);
+  const float a3 = __builtin_amdgcn_fmed3f(x[3], -448.0f, 448.0f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, r, true);
+  return (uint32_t)r;
 }
 
 // exp2 as the single hardware instruction (v_exp_f32). Results below the fp32

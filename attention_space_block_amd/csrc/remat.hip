@@ -80,6 +80,14 @@ __device__ __forceinline__ void unpack<float>(const uint4& v, float* x) {
   x[3] = __uint_as_float(v.w);
 }
 
+template <>
+__device__ __forceinline__ void unpack<uint8_t>(const uint4& v, float* x) {
+  fp8x4_to_f32(v.x, x);
+  fp8x4_to_f32(v.y, x + 4);
+  fp8x4_to_f32(v.z, x + 8);
+  fp8x4_to_f32(v.w, x + 12);
+}
+
 template <typename T>
 __device__ __forceinline__ uint4 pack(const float* x);
 template <>
@@ -89,6 +97,11 @@ __device__ __forceinline__ uint4 pack<uint16_t>(const float* x) {
   for (int i = 0; i < 4; ++i)
     w[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ uint4 pack<uint8_t>(const float* x) {
+  return make_uint4(f32x4_to_fp8(x), f32x4_to_fp8(x + 4), f32x4_to_fp8(x + 8),
+                    f32x4_to_fp8(x + 12));
 }
 template <>
 __device__ __forceinline__ uint4 pack<float>(const float* x) {
@@ -204,7 +217,10 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta,
     if (delta) remat_kernel<T, D, LAY, true><<<g, b, 0, s>>>(a);             \
     else remat_kernel<T, D, LAY, false><<<g, b, 0, s>>>(a);                  \
   } while (0)
-  if (dtype == KVM_BF16) {
+  if (dtype == KVM_FP8_E4M3) {
+    if (d == 128) { if (layout == 0) KVM_REMAT(uint8_t, 128, 0); else KVM_REMAT(uint8_t, 128, 1); }
+    else { if (layout == 0) KVM_REMAT(uint8_t, 64, 0); else KVM_REMAT(uint8_t, 64, 1); }
+  } else if (dtype == KVM_BF16) {
     if (d == 128) { if (layout == 0) KVM_REMAT(uint16_t, 128, 0); else KVM_REMAT(uint16_t, 128, 1); }
     else { if (layout == 0) KVM_REMAT(uint16_t, 64, 0); else KVM_REMAT(uint16_t, 64, 1); }
   } else {

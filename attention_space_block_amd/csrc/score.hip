@@ -680,7 +680,8 @@ static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStrea
 extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
                                      int64_t n_blocks, int32_t index_loc, int64_t tile_blocks) {
   using namespace kvm;
-  if (check_dims(dims, dtype) || n_q_tokens < 1 || n_blocks < 1) return 0;
+  if (check_dims(dims, dtype) || dtype == KVM_FP8_E4M3 || n_q_tokens < 1 || n_blocks < 1)
+    return 0;
   return make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks).bytes;
 }
 
@@ -692,6 +693,8 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   clear_error();
   int rc = check_dims(dims, dtype);
   if (rc) return rc;
+  KVM_CHECK_ARG(dtype != KVM_FP8_E4M3, "the index and queries of FP8 K/V are bf16: score with "
+                "KVM_BF16");
   KVM_CHECK_ARG(q && index && scores, "null pointer");
   KVM_CHECK_ARG(n_q_tokens >= 1 && n_blocks >= 1 && n_blocks < (1LL << 30),
                 "n_q_tokens / n_blocks out of range");

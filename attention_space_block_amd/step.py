@@ -25,12 +25,16 @@ class WorkingSetUpdater:
         self.cap, self.budget = index_cap, budget_blocks
         self.n_sink, self.n_recent = n_sink, n_recent
         self.dev = device
-        tdt = torch.float32 if dtype == api.KVM_F32 else torch.int16
+        # page elements in the K/V dtype; the index and queries are bf16 for FP8 K/V
+        tdt = {api.KVM_F32: torch.float32, api.KVM_BF16: torch.int16,
+               api.KVM_FP8_E4M3: torch.uint8}[dtype]
+        self.index_dtype = api.KVM_BF16 if dtype == api.KVM_FP8_E4M3 else dtype
         self.elem_dtype = tdt
         self.block_elems = dims.n_layers * dims.n_kv_heads * dims.block_tokens * dims.head_dim
-        self.block_bytes = self.block_elems * (4 if dtype == api.KVM_F32 else 2)
+        self.block_bytes = self.block_elems * tdt.itemsize
         self.index = torch.zeros((dims.n_layers, dims.n_kv_heads, index_cap, dims.head_dim),
-                                 dtype=tdt, device=device)
+                                 dtype=torch.float32 if dtype == api.KVM_F32 else torch.int16,
+                                 device=device)
         self.k_view = torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device)
         self.v_view = torch.zeros((n_slots, self.block_elems), dtype=tdt, device=device)
         # bounded delta re-RoPE (delta_limit > 0) keeps no raw-K shadow pages
@@ -67,7 +71,7 @@ class WorkingSetUpdater:
         import torch
         key = (n_q_tokens, self.n_blocks)
         if self.ws_key != key:
-            nbytes = api.kvm_score_ws_bytes(self.dims, self.dtype, n_q_tokens, self.n_blocks)
+            nbytes = api.kvm_score_ws_bytes(self.dims, self.index_dtype, n_q_tokens, self.n_blocks)
             if self.ws is None or self.ws.numel() < nbytes:
                 self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.dev)
             self.ws_key = key
@@ -75,7 +79,7 @@ class WorkingSetUpdater:
 
     def score(self, q, n_q_tokens: int):
         ws = self._workspace(n_q_tokens)
-        api.kvm_score_blocks(self.dims, self.dtype, q, n_q_tokens, self.index, self.cap,
+        api.kvm_score_blocks(self.dims, self.index_dtype, q, n_q_tokens, self.index, self.cap,
                              self.n_blocks, KVM_INDEX_DEVICE, 0, self.scores, ws, ws.numel())
 
     def select(self):

@@ -25,8 +25,13 @@
  *    synchronous and leaves outputs untouched. HIP errors return KVM_EHIP;
  *    the text is in kvm_last_error() (thread-local). No C++ exception crosses
  *    this interface.
- *  - Element types: KVM_F32 (IEEE binary32) or KVM_BF16 (bfloat16 bit
- *    patterns). Supported head_dim: 64 and 128; block_tokens: 32.
+ *  - Element types: KVM_F32 (IEEE binary32), KVM_BF16 (bfloat16 bit patterns)
+ *    or KVM_FP8_E4M3 (OCP FP8 E4M3FN bytes: bias 7, 3 mantissa bits, largest
+ *    finite 448, no infinities; the KV-cache format the pages' engine runs).
+ *    With FP8 K/V the Mean-K index and the queries are bf16, so scoring takes
+ *    KVM_BF16; re-RoPE decodes FP8 exactly, rotates in fp32 and re-encodes
+ *    (nearest, ties to even, saturating at +-448); V is copied byte for byte.
+ *    Supported head_dim: 64 and 128; block_tokens: 32.
  */
 #ifndef KVM_H
 #define KVM_H
@@ -48,7 +53,7 @@ typedef enum {
   KVM_ENOTSUP = -5  /* valid but unsupported combination (dtype, head_dim) */
 } kvm_status;
 
-typedef enum { KVM_F32 = 0, KVM_BF16 = 1 } kvm_dtype;
+typedef enum { KVM_F32 = 0, KVM_BF16 = 1, KVM_FP8_E4M3 = 2 } kvm_dtype;
 
 /* Where kvm_score_blocks finds the index. */
 typedef enum { KVM_INDEX_DEVICE = 0, KVM_INDEX_HOST_TILED = 1 } kvm_index_loc;
@@ -78,11 +83,13 @@ const char* kvm_last_error(void);
  *
  * k_raw   device, block-major raw K: block i at (char*)k_raw + i*k_block_stride,
  *         each block [L][Hkv][B][d] contiguous in `dtype`.
- * index   device, [L][Hkv][index_cap_blocks][d] in `dtype`; the call writes rows
- *         [first_block, first_block + n_blocks) of every (l, g) and nothing else.
+ * index   device, [L][Hkv][index_cap_blocks][d] in `dtype` (bf16 for
+ *         KVM_FP8_E4M3 K); the call writes rows [first_block, first_block +
+ *         n_blocks) of every (l, g) and nothing else.
  * Result: index[l][g][first_block+i][t] = round(mean_j k_raw[i][l][g][j][t]),
- *         the sum formed exactly (float64) and rounded once to nearest-even, so
- *         the stored mean is the correctly rounded block mean.
+ *         the sum formed exactly (float64; fp32 for FP8 K, whose 32 values sum
+ *         exactly there) and rounded once to nearest-even, so the stored mean
+ *         is the correctly rounded block mean.
  * Errors: KVM_EINVAL (null pointer, n_blocks < 0, stride smaller than a block,
  *         first_block + n_blocks > index_cap_blocks), KVM_ENOTSUP (head_dim,
  *         block_tokens). n_blocks == 0 is a no-op. */

@@ -14,14 +14,18 @@ import numpy as np
 
 import synth
 from .meank import mean_k
-from .numerics import from_bf16_bits
+from .numerics import from_bf16_bits, fp8_decode
 from .rope import rope_rotate
 from .scores import block_scores
 from .select import select_blocks, compact_positions, cutoff_margin
 
 
 def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    return from_bf16_bits(a) if dtype == "bf16" else np.asarray(a, dtype=np.float64)
+    if dtype == "bf16":
+        return from_bf16_bits(a)
+    if dtype == "fp8":
+        return fp8_decode(a)
+    return np.asarray(a, dtype=np.float64)
 
 
 def raw_blocks(wl, which: str, b0: int, nb: int) -> np.ndarray:
@@ -43,7 +47,7 @@ def index_rows(wl, b0: int, nb: int, chunk: int = 64, threads: int | None = None
 
     def work(s):
         n = min(chunk, nb - s)
-        m = mean_k(raw_blocks(wl, "K", b0 + s, n), wl.dtype)          # [n][L][Hkv][d]
+        m = mean_k(raw_blocks(wl, "K", b0 + s, n), wl.index_dtype)    # [n][L][Hkv][d]
         out[:, :, s:s + n, :] = np.transpose(m, (1, 2, 0, 3))
 
     threads = threads or min(16, os.cpu_count() or 1)
@@ -71,7 +75,7 @@ def query_f64(wl, step: int = 0, index: np.ndarray | None = None) -> np.ndarray:
     shift = None
     if wl.planted_block >= 0:
         shift = planted_shift(wl, index)
-    return as_f64(synth.query(wl, step=step, shift=shift), wl.dtype)
+    return as_f64(synth.query(wl, step=step, shift=shift), wl.index_dtype)
 
 
 def query_stored(wl, step: int = 0, index: np.ndarray | None = None) -> np.ndarray:

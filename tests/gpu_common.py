@@ -12,8 +12,27 @@ import synth
 
 
 def torch_dtype(wl):
+    """torch dtype holding the workspace's raw K/V and page elements."""
     import torch
-    return torch.float32 if wl.dtype == "f32" else torch.int16
+    return {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8}[wl.dtype]
+
+
+def np_elem(wl):
+    """numpy dtype of the generator's raw K/V elements (bit patterns for bf16/fp8)."""
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[wl.dtype]
+
+
+def index_torch_dtype(wl):
+    """torch dtype of the Mean-K index (bf16 bits for bf16 and fp8 K)."""
+    import torch
+    return torch.float32 if wl.index_dtype == "f32" else torch.int16
+
+
+def fp8_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half the spacing of E4M3 values around |x| (subnormal step 2^-9)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 0.5 * 2.0 ** (e - 3)
 
 
 def to_dev(a: np.ndarray, dev):
@@ -31,6 +50,9 @@ def to_host_bits(t) -> np.ndarray:
 def as_f64(a: np.ndarray) -> np.ndarray:
     if a.dtype == np.uint16:
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.uint8:
+        from oracle.numerics import fp8_decode
+        return fp8_decode(a)
     return a.astype(np.float64)
 
 
@@ -49,8 +71,8 @@ def build_index_dev(k, wl, raw_k, dev, cap: int | None = None, first: int = 0):
     import torch
     N = raw_k.shape[0]
     cap = cap or N
-    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim), dtype=torch_dtype(wl),
-                        device=dev)
+    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim),
+                        dtype=index_torch_dtype(wl), device=dev)
     k.kvm_build_index(k.dims_for(wl), k.dtype_code(wl.dtype), raw_k, wl.block_bytes, first, N,
                       index, cap)
     return index
@@ -60,7 +82,7 @@ def score_dev(k, wl, q_dev, index, n_blocks: int, cap: int, dev, loc: int = 0,
               tile_blocks: int = 0, host_index=None):
     import torch
     dims = k.dims_for(wl)
-    dt = k.dtype_code(wl.dtype)
+    dt = k.dtype_code(wl.index_dtype)
     T = q_dev.shape[2]
     ws_b = k.kvm_score_ws_bytes(dims, dt, T, n_blocks, loc, tile_blocks)
     ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
@@ -100,8 +122,9 @@ class Pool:
 def check_view(wl, sel: np.ndarray, page: np.ndarray, pool: Pool, blocks=None, atol=None):
     """Compare the K and V pages of selected blocks with the oracle.
 
-    K: |K_gpu - RoPE(raw K)| within 2e-2 (bf16) or 1e-5*max(1,|K|) (fp32),
-    against the unrounded float64 oracle; V: bit-exact."""
+    K: |K_gpu - RoPE(raw K)| within 2e-2 (bf16), half an E4M3 spacing plus
+    the fp32 rotation's error (fp8) or 1e-5*max(1,|K|) (fp32), against the
+    unrounded float64 oracle; V: bit-exact."""
     from oracle.pipeline import expected_view_k, expected_view_v_bits
     B = wl.block_tokens
     idx = range(len(sel)) if blocks is None else blocks
@@ -114,6 +137,8 @@ def check_view(wl, sel: np.ndarray, page: np.ndarray, pool: Pool, blocks=None, a
         err = np.abs(got - want)
         if wl.dtype == "bf16":
             ok = np.all(err <= (atol if atol is not None else 2e-2))
+        elif wl.dtype == "fp8":
+            ok = np.all(err <= fp8_half_ulp(want * (1 + 1e-6)) + 1e-6 * np.maximum(1.0, np.abs(want)))
         else:
             ok = np.all(err <= 1e-5 * np.maximum(1.0, np.abs(want)))
         worst = max(worst, float(err.max()))
@@ -130,8 +155,8 @@ def build_index_streamed(k, wl, dev, n_blocks=None, chunk: int = 1024, cap=None)
     import torch
     N = n_blocks or wl.n_blocks
     cap = cap or N
-    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim), dtype=torch_dtype(wl),
-                        device=dev)
+    index = torch.zeros((wl.n_layers, wl.n_kv_heads, cap, wl.head_dim),
+                        dtype=index_torch_dtype(wl), device=dev)
     stage = [torch.empty((chunk, wl.block_elems), dtype=torch_dtype(wl)).pin_memory()
              for _ in range(2)]
     dchunk = torch.empty((chunk, wl.block_elems), dtype=torch_dtype(wl), device=dev)

@@ -37,7 +37,8 @@ def say(*a):
 
 # ---------------------------------------------------------------- Mean-K ----
 
-@pytest.mark.parametrize("name,nb,layers", [("tiny", 128, None), ("ctx64k", 300, 2)])
+@pytest.mark.parametrize("name,nb,layers", [("tiny", 128, None), ("ctx64k", 300, 2),
+                                             ("ctx64k_fp8", 300, 2)])
 def test_build_index_bit_exact(k, dev, name, nb, layers):
     wl = synth.get_workload(name)
     if layers:
@@ -73,25 +74,27 @@ def test_build_index_append_and_stride(k, dev):
 
 @pytest.mark.parametrize("name,layout,pos0,N", [
     ("ctx64k", 0, 0, 70), ("ctx64k", 1, 4096, 37), ("tiny", 0, 96, 9), ("tiny", 1, 0, 5),
+    ("ctx64k_fp8", 0, 512, 41), ("ctx64k_fp8", 1, 0, 30),
 ])
 def test_build_index_rope_matches_oracle(k, dev, name, layout, pos0, N):
     from oracle import mean_k_from_rope
     wl = synth.get_workload(name).scaled(rope_layout=layout)
-    if name == "ctx64k":
+    if name.startswith("ctx64k"):
         wl = wl.scaled(n_layers=2)
+    idt = wl.index_dtype                                     # bf16 rows for fp8 K
     say("build index rope", name, layout, pos0, N)
     k_rope = synth.kv_blocks(wl, "K", 0, N)                 # any K values stand for cached K
     kd = gc.to_dev(k_rope.reshape(N, -1), dev)
     pool = gc.Pool(k, wl, 4, N, pos0 + 32 * N, dev)
     import torch
     index = torch.zeros((wl.n_layers, wl.n_kv_heads, N + 3, wl.head_dim),
-                        dtype=gc.torch_dtype(wl), device=dev)
+                        dtype=gc.index_torch_dtype(wl), device=dev)
     pool.ctx.kvm_ctx_build_index_rope(kd, wl.block_bytes, 0, N, pos0, index, N + 3)
     got = gc.to_host_bits(index)[:, :, :N]
     kf = op.as_f64(k_rope, wl.dtype)
-    want = mean_k_from_rope(kf, pos0, wl.dtype, wl.theta, layout)         # [N][L][Hkv][d]
+    want = mean_k_from_rope(kf, pos0, idt, wl.theta, layout)              # [N][L][Hkv][d]
     want = np.transpose(want, (1, 2, 0, 3))
-    if wl.dtype == "bf16":
+    if idt == "bf16":
         assert np.array_equal(got, bf16_bits(want))
         gv = op.as_f64(got, "bf16")
     else:
@@ -101,7 +104,7 @@ def test_build_index_rope_matches_oracle(k, dev, name, layout, pos0, N):
                          (1, 2, 0, 3))
     # against the exact float64 rotation: half an ulp of rounding plus the fp32
     # table's error, at most (|a| + |b|) * 2^-24 per pair of a token
-    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - (7 if wl.dtype == "bf16" else 23))
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - (7 if idt == "bf16" else 23))
     table_err = 2.0 * np.abs(kf).max() * 2.0 ** -24
     assert np.all(np.abs(gv - exact) <= 0.5 * ulp + table_err)
     assert int(index[:, :, N:].abs().sum()) == 0
@@ -124,7 +127,7 @@ def test_build_index_rope_matches_oracle(k, dev, name, layout, pos0, N):
 def _score_case(k, dev, wl, N):
     index = op.index_rows(wl, 0, N)
     q = op.query_stored(wl, 0, index)
-    ref = op.block_scores(op.as_f64(q, wl.dtype), index)
+    ref = op.block_scores(op.as_f64(q, wl.index_dtype), index)
     raw = gc.raw_to_device(wl, "K", 0, N, dev)
     idx_dev = gc.build_index_dev(k, wl, raw, dev)
     got = gc.score_dev(k, wl, gc.to_dev(q, dev), idx_dev, N, N, dev).cpu().numpy()
@@ -244,10 +247,8 @@ def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0, delt
     elif src == "pinned":
         rk = torch.empty((N, wl.block_elems), dtype=gc.torch_dtype(wl)).pin_memory()
         rv = torch.empty((N, wl.block_elems), dtype=gc.torch_dtype(wl)).pin_memory()
-        synth.kv_blocks(wl, "K", 0, N, out=rk.numpy().view(
-            np.float32 if wl.dtype == "f32" else np.uint16))
-        synth.kv_blocks(wl, "V", 0, N, out=rv.numpy().view(
-            np.float32 if wl.dtype == "f32" else np.uint16))
+        synth.kv_blocks(wl, "K", 0, N, out=rk.numpy().view(gc.np_elem(wl)))
+        synth.kv_blocks(wl, "V", 0, N, out=rv.numpy().view(gc.np_elem(wl)))
         pool.ctx.kvm_ctx_set_source(0, N, rk, rv, wl.block_bytes, k.KVM_SRC_HOST_PINNED)
         keep += [rk, rv]
     else:
@@ -255,16 +256,18 @@ def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0, delt
 
         def gather(block, which, dst):
             buf = (ctypes.c_char * wl.block_bytes).from_address(dst)
-            arr = np.frombuffer(buf, dtype=np.float32 if wl.dtype == "f32" else np.uint16)
+            arr = np.frombuffer(buf, dtype=gc.np_elem(wl))
             synth.kv_blocks(wl, "K" if which == 0 else "V", block, 1, out=arr, nthreads=1)
             return 0
         pool.ctx.kvm_ctx_set_gather(0, N, gather)
     return pool, keep
 
 
-@pytest.mark.parametrize("src", ["device", "pinned", "gather"])
-def test_remat_view_matches_oracle(k, dev, src):
-    wl = synth.get_workload("ctx64k").scaled(n_layers=2, budget_blocks=96, n_recent=8)
+@pytest.mark.parametrize("name,src", [("ctx64k", "device"), ("ctx64k", "pinned"),
+                                      ("ctx64k", "gather"), ("ctx64k_fp8", "device"),
+                                      ("ctx64k_fp8", "pinned"), ("ctx64k_fp8", "gather")])
+def test_remat_view_matches_oracle(k, dev, name, src):
+    wl = synth.get_workload(name).scaled(n_layers=2, budget_blocks=96, n_recent=8)
     N = 400
     say("remat", src)
     pool, keep = _remat_setup(k, dev, wl, N, 130, src, batch=16, staging=32)
@@ -431,7 +434,7 @@ def test_remat_error_paths(k, dev):
 
 # ------------------------------------------------------------ end to end ----
 
-@pytest.mark.parametrize("name", ["tiny", "ctx64k"])
+@pytest.mark.parametrize("name", ["tiny", "ctx64k", "ctx64k_fp8"])
 def test_end_to_end_step(k, dev, name):
     import torch
     wl = synth.get_workload(name)
