@@ -49,6 +49,8 @@ def parse():
                     help="steps of the pinned-host leg (0 to skip)")
     ap.add_argument("--delta-steps", type=int, default=4,
                     help="rematerializations timed in bounded delta re-RoPE mode (0: skip)")
+    ap.add_argument("--fp8", type=int, default=1,
+                    help="also time the view with FP8 E4M3 K/V pages (0: skip)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle sample")
     ap.add_argument("--cpu-pairs", type=int, default=6,
                     help="(layer, KV head) pairs in the CPU oracle sample")
@@ -205,6 +207,81 @@ class Workspace:
                           self.n_new, self.index, self.N)
         self.score_select()
         return self.ctx.kvm_rematerialize(self.sel, self.n_sel, self.page)
+
+
+def fp8_leg(k, ws, wl, dev, steps: int) -> dict:
+    """The same view with FP8 E4M3 K/V pages (the KV format of the pages' engine):
+    resident half registered, missing half from HBM copies, timed like the value
+    leg; plus the Mean-K build from FP8 K over 1024 blocks."""
+    import synth
+    import torch
+    w8 = synth.get_workload("ws1m_fp8")
+    page = w8.block_bytes
+    n_slots = ws.k_view.shape[0]
+    pools = [torch.zeros((n_slots, w8.block_elems), dtype=torch.uint8, device=dev)
+             for _ in range(3)]
+
+    def blocks_to_dev(which, blocks):
+        out = torch.empty((len(blocks), w8.block_elems), dtype=torch.uint8, device=dev)
+        h = torch.empty((256, w8.block_elems), dtype=torch.uint8).pin_memory()
+        hv = h.numpy()
+        for s0 in range(0, len(blocks), 256):
+            part = blocks[s0:s0 + 256]
+            for i, b in enumerate(part):
+                synth.kv_blocks(w8, which, int(b), 1, out=hv[i:i + 1])
+            out[s0:s0 + len(part)].copy_(h[:len(part)])
+        torch.cuda.synchronize()
+        return out
+    hk, hv_ = blocks_to_dev("K", ws.hits), blocks_to_dev("V", ws.hits)
+    mk, mv = blocks_to_dev("K", ws.misses), blocks_to_dev("V", ws.misses)
+    ctx = k.KvmCtx(ws.dims, k.KVM_FP8_E4M3, pools[0], pools[1], pools[2], n_slots,
+                   wl.final_blocks, (wl.budget_blocks + wl.reserve_blocks) * wl.block_tokens,
+                   wl.theta, wl.rope_layout, 64)
+    for i, b in enumerate(ws.misses):
+        ctx.kvm_ctx_set_source(int(b), 1, mk[i], mv[i], page, k.KVM_SRC_DEVICE)
+
+    def one():
+        ctx.kvm_ctx_evict(0, wl.final_blocks)
+        for i, b in enumerate(ws.hits):
+            ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv_[i], page)
+        torch.cuda.synchronize()
+        return ctx.kvm_rematerialize(ws.sel, ws.n_sel, ws.page)
+    one()
+    torch.cuda.synchronize()
+    k.kvm_profile_enable(True)
+    for _ in range(steps):
+        st = one()
+    torch.cuda.synchronize()
+    rc_, rt_ = k.kvm_profile_read().get("remat", (0, float("nan")))
+    k.kvm_profile_enable(False)
+    r_ms = rt_ / max(rc_, 1)
+    r_bytes = st["hits"] * 2 * page + st["misses"] * 4 * page
+    # Mean-K from FP8 K: 1024 blocks (the staged half's K copies)
+    nb = min(1024, len(ws.misses))
+    L, Hkv, d = w8.n_layers, w8.n_kv_heads, w8.head_dim
+    idx = torch.empty((L, Hkv, nb, d), dtype=torch.int16, device=dev)
+    k.kvm_build_index(ws.dims, k.KVM_FP8_E4M3, mk, page, 0, nb, idx, nb)
+    torch.cuda.synchronize()
+    k.kvm_profile_enable(True)
+    for _ in range(3):
+        k.kvm_build_index(ws.dims, k.KVM_FP8_E4M3, mk, page, 0, nb, idx, nb)
+    torch.cuda.synchronize()
+    bc, bt = k.kvm_profile_read().get("build_index", (0, float("nan")))
+    k.kvm_profile_enable(False)
+    b_ms = bt / max(bc, 1)
+    b_bytes = nb * (page + L * Hkv * d * 2)
+    ctx.close()
+    del pools, hk, hv_, mk, mv, idx
+    torch.cuda.empty_cache()
+    out = {"page_bytes": page, "remat": {"avg_ms": r_ms, "bytes": r_bytes,
+                                         "GBps": r_bytes / (r_ms * 1e-3) / 1e9,
+                                         "hbm_frac": r_bytes / (r_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                         "hits": st["hits"], "misses": st["misses"]},
+           "build": {"blocks": nb, "avg_ms": b_ms, "GBps": b_bytes / (b_ms * 1e-3) / 1e9,
+                     "hbm_frac": b_bytes / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+    log(f"fp8 leg: remat {r_ms:.2f} ms ({out['remat']['GBps']:.0f} GB/s), "
+        f"Mean-K build {b_ms:.3f} ms ({out['build']['GBps']:.0f} GB/s)")
+    return out
 
 
 def counter_traffic() -> dict:
@@ -541,6 +618,7 @@ def main():
                  "traffic": traffic_for(counter_traffic(), "remat_kernel", "true>")}
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
+    fp8 = fp8_leg(k, ws, wl, dev, args.steps) if args.fp8 else None
     # PCIe leg: misses from pinned host memory
     pcie = None
     if args.pcie_steps > 0:
@@ -587,6 +665,7 @@ def main():
         "build_rope": {"blocks": nr, "avg_ms": rope_ms, "GBps": rope_gbps,
                        "hbm_frac": rope_gbps / HBM_PEAK_GBPS},
         "delta_rerope": delta,
+        "fp8_pages": fp8,
         "pcie_leg": pcie,
         "kernels": kern,
     }
