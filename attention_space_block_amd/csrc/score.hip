@@ -26,11 +26,11 @@
 // the shared operand of a pair stays in that XCD's L2.
 //
 // Stored-score path (any dtype, small TG, and the host-tiled index): pass 1
-// computes every score once on the VALU, stores it (fp32) and emits per-chunk
-// (max, sum-exp) partials; a combine kernel forms the LSE in fp64; pass 2
-// reads the stored scores back and sums exp2(x - LSE) per block in fp64.
-// HBM-bound: one pass over the index plus a write and a read of TG*N*L*Hkv
-// floats. The host-tiled form streams 64 MiB-class tiles H2D through two
+// computes every score once on the VALU and stores it (fp32); a stats pass
+// forms per-chunk (max, sum-exp) partials from the stored scores, a combine
+// kernel the LSE in fp64; pass 2 reads the stored scores back and sums
+// exp2(x - LSE) per block in fp64. HBM-bound: one pass over the index plus a
+// write and two reads of TG*N*L*Hkv floats. The host-tiled form streams 64 MiB-class tiles H2D through two
 // staging buffers on a side stream, double-buffered with events.
 #include <math.h>
 
@@ -484,7 +484,7 @@ struct StoredArgs {
   int32_t nb;               // blocks in this launch
   int32_t n_blocks;         // N (layout of S)
   int32_t T, Hq, Hkv, G, TG, nlg;
-  int32_t chunks_total;     // ceil(N / 256)
+  int32_t chunks_total;     // ceil(N / STATS_CHUNK): (max, sum) partials per row
   float scale;
   float* S;                 // [nlg][N][TG]
   float2* part;             // [nlg][chunks_total][TG]
@@ -492,9 +492,8 @@ struct StoredArgs {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
-  extern __shared__ float smem[];       // q rows [TG][D] then reduction scratch
+  extern __shared__ float smem[];       // q rows [TG][D]
   float* qs = smem;
-  float* red = smem + (int64_t)a.TG * D; // [2][4 waves]
   const int32_t chunks_here = (a.nb + 255) / 256;
   const int32_t lg = blockIdx.x / chunks_here;
   const int32_t ch = blockIdx.x % chunks_here;
@@ -509,37 +508,86 @@ __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
   const int32_t bl = ch * 256 + threadIdx.x;       // block within this launch
   const bool valid = bl < a.nb;
   const int32_t b = a.b_first + bl;
+  if (!valid) return;                          // no barrier follows
   float k[D];
-  if (valid)
-    load_row<T, D>(reinterpret_cast<const T*>(a.index) + (int64_t)lg * a.lg_stride +
-                       (int64_t)bl * D, k);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int32_t gchunk = a.b_first / 256 + ch;
+  load_row<T, D>(reinterpret_cast<const T*>(a.index) + (int64_t)lg * a.lg_stride +
+                     (int64_t)bl * D, k);
+  float* srow = a.S + ((int64_t)lg * a.n_blocks + b) * a.TG;
   for (int rho = 0; rho < a.TG; ++rho) {
-    float x = -INFINITY;
-    if (valid) {
-      const float* qr = qs + rho * D;
-      float acc = 0.0f;
+    const float* qr = qs + rho * D;
+    float acc = 0.0f;
 #pragma unroll
-      for (int t = 0; t < D; ++t) acc = fmaf(qr[t], k[t], acc);
-      x = acc * a.scale;
-      a.S[((int64_t)lg * a.n_blocks + b) * a.TG + rho] = x;
+    for (int t = 0; t < D; ++t) acc = fmaf(qr[t], k[t], acc);
+    srow[rho] = acc * a.scale;
+  }
+}
+
+// (max, sum-exp) partials of the stored scores per (l, g, chunk of blocks, row),
+// in a pass of their own so pass 1 streams the index without reductions. Rows
+// are taken 8 at a time: each thread walks its blocks once per group with an
+// online (shift, sum) per row (one exp per score; the shift moves up when a
+// larger score arrives), then the pairs are merged in a fixed order (xor
+// shuffles, then the four waves in order), so the partials are deterministic.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;                 // both empty
+  s = s * hw_exp2(m - M) + s2 * hw_exp2(m2 - M);
+  m = M;
+}
+
+__global__ __launch_bounds__(256) void score_stored_stats(const float* __restrict__ S,
+                                                          int32_t n_blocks, int32_t TG,
+                                                          int32_t chunk, int32_t chunks_total,
+                                                          float2* __restrict__ part) {
+  constexpr int RG = 8;                        // rows per group
+  __shared__ float2 red[4][RG];
+  const int32_t lg = blockIdx.x / chunks_total, ch = blockIdx.x % chunks_total;
+  const int32_t b0 = ch * chunk;
+  const int32_t b1 = b0 + chunk < n_blocks ? b0 + chunk : n_blocks;
+  const float* Sl = S + (int64_t)lg * n_blocks * TG;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r0 = 0; r0 < TG; r0 += RG) {
+    const int nr = TG - r0 < RG ? TG - r0 : RG;
+    float m[RG], sm[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      m[r] = -INFINITY;
+      sm[r] = 0.0f;
     }
-    // workgroup max, then sum of exp2(x - max), fp32 tree
-    float mx = x;
+    for (int32_t b = b0 + (int32_t)threadIdx.x; b < b1; b += 256) {
+      const float* row = Sl + (int64_t)b * TG + r0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float e = valid ? hw_exp2(x - mx) : 0.0f;
+      for (int r = 0; r < RG; ++r) {
+        if (r < nr) {
+          const float x = row[r];
+          if (x > m[r]) {
+            sm[r] = sm[r] * hw_exp2(m[r] - x) + 1.0f;
+            m[r] = x;
+          } else {
+            sm[r] += hw_exp2(x - m[r]);
+          }
+        }
+      }
+    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
-    if (lane == 0) red[4 + wave] = e;
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m[r], off), s2 = __shfl_xor(sm[r], off);
+        lse_merge(m[r], sm[r], m2, s2);
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) red[wave][r] = make_float2(m[r], sm[r]);
+    }
     __syncthreads();
-    if (threadIdx.x == 0)
-      a.part[((int64_t)lg * a.chunks_total + gchunk) * a.TG + rho] =
-          make_float2(mx, (red[4] + red[5]) + (red[6] + red[7]));
+    if ((int)threadIdx.x < nr) {
+      const int r = threadIdx.x;
+      float mm = red[0][r].x, ss = red[0][r].y;
+      for (int w = 1; w < 4; ++w) lse_merge(mm, ss, red[w][r].x, red[w][r].y);
+      part[((int64_t)lg * chunks_total + ch) * TG + r0 + r] = make_float2(mm, ss);
+    }
     __syncthreads();
   }
 }
@@ -592,6 +640,9 @@ struct Plan {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// blocks per (max, sum-exp) partial of the stored-score path
+static constexpr int32_t STATS_CHUNK = 2048;
+
 static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, int32_t loc,
                       int64_t tile_blocks) {
   Plan p{};
@@ -616,7 +667,7 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
     p.off_rp = off;
     off = align256(off + (size_t)nlg * N * sizeof(float));
   } else {
-    p.chunks = (int32_t)((N + 255) / 256);
+    p.chunks = (int32_t)((N + STATS_CHUNK - 1) / STATS_CHUNK);
     p.off_S = off;
     off = align256(off + (size_t)nlg * N * p.TG * sizeof(float));
     p.off_part = off;
@@ -833,6 +884,10 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
       KVM_HIP(hipEventRecord(tr->used[bi], s));
     }
   }
+  { KernelTimer tm("score_stored_stats", s);
+  score_stored_stats<<<dim3((uint32_t)((int64_t)nlg * p.chunks)), dim3(256), 0, s>>>(
+      a.S, (int32_t)n_blocks, TG, STATS_CHUNK, p.chunks, a.part); }
+  KVM_HIP(hipGetLastError());
   const int64_t nl = (int64_t)nlg * TG;
   { KernelTimer tm("score_stored_lse", s);
   score_stored_lse<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
