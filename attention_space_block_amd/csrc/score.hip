@@ -522,6 +522,85 @@ __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
   }
 }
 
+// bf16 pass 1 on the matrix cores: the scores of one (l, g) are the product
+// Kbar[N x d] * Q_g^T[d x TG], taken in 16-row tiles with
+// v_mfma_f32_16x16x32_bf16: A = 16 index rows (lane l holds row l % 16,
+// elements 8*(l/16) .. +8 of each 32-wide k-step, read straight from global
+// memory), B = the TG query rows padded to 16-column tiles (stationary in
+// registers). Each lane's 4 results are rows 4*(l/16) .. +3 of the tile at
+// query row l % 16. The VALU only scales and stores, so the pass streams the
+// index at memory speed. A workgroup takes 1024 rows of one (l, g); each wave
+// keeps 4 tiles (16 KB) of loads in flight.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+static constexpr int32_t STORED_MFMA_ROWS = 1024;
+
+template <int D>
+__global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
+  constexpr int KS = D / 32;                   // 32-wide k-steps
+  constexpr int TU = 4;                        // 16-row tiles in flight per wave
+  constexpr int MAXCT = 4;                     // TG < 64: at most 4 column tiles
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t chunks_here = (a.nb + STORED_MFMA_ROWS - 1) / STORED_MFMA_ROWS;
+  const int32_t lg = blockIdx.x / chunks_here;
+  const int32_t ch = blockIdx.x % chunks_here;
+  const int32_t r_begin = ch * STORED_MFMA_ROWS;
+  const int32_t r_end = r_begin + STORED_MFMA_ROWS < a.nb ? r_begin + STORED_MFMA_ROWS : a.nb;
+  const int l = lg / a.Hkv, g = lg % a.Hkv;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int nct = (a.TG + 15) / 16;
+  // B: query row rho = 16*ct + r16, elements 32*ks + 8*kg .. +8
+  bf16x8_t bq[MAXCT][KS];
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int ct = 0; ct < MAXCT; ++ct) {
+    const int rho = 16 * ct + r16;
+    const bool ok = rho < a.TG;
+    const int hh = g * a.G + (ok ? rho / a.T : 0), m = ok ? rho % a.T : 0;
+    const uint16_t* qp = q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      bq[ct][ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(a.index) + (int64_t)lg * a.lg_stride;
+  float* Sl = a.S + ((int64_t)lg * a.n_blocks + a.b_first) * a.TG;
+  for (int32_t r0 = r_begin + wave * 16 * TU; r0 < r_end; r0 += 4 * 16 * TU) {
+    bf16x8_t av[TU][KS];
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+      int32_t row = r0 + 16 * t + r16;
+      row = row < r_end ? row : r_end - 1;     // rows past the end re-read the last one
+      const uint16_t* rp = base + (int64_t)row * D + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        av[t][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rp + 32 * ks));
+    }
+#pragma unroll
+    for (int t = 0; t < TU; ++t) {
+      const int32_t t0 = r0 + 16 * t;
+      if (t0 >= r_end) break;                  // uniform over the wave
+#pragma unroll
+      for (int ct = 0; ct < MAXCT; ++ct) {
+        if (ct >= nct) break;                  // uniform
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t][ks], bq[ct][ks], acc, 0, 0, 0);
+        const int rho = 16 * ct + r16;
+        if (rho < a.TG) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int32_t row = t0 + 4 * kg + v;
+            if (row < r_end) Sl[(int64_t)row * a.TG + rho] = acc[v] * a.scale;
+          }
+        }
+      }
+    }
+  }
+}
+
 // (max, sum-exp) partials of the stored scores per (l, g, chunk of blocks, row),
 // in a pass of their own so pass 1 streams the index without reductions. Rows
 // are taken 8 at a time: each thread walks its blocks once per group with an
@@ -718,8 +797,11 @@ static void launch_stored_pass1(const StoredArgs& a, hipStream_t s) {
 
 static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStream_t s) {
   if (dtype == KVM_BF16) {
-    if (D == 128) launch_stored_pass1<uint16_t, 128>(a, s);
-    else launch_stored_pass1<uint16_t, 64>(a, s);
+    const int32_t chunks_here = (a.nb + STORED_MFMA_ROWS - 1) / STORED_MFMA_ROWS;
+    const dim3 grid((uint32_t)((int64_t)a.nlg * chunks_here));
+    KernelTimer tm("score_stored_pass1", s);
+    if (D == 128) score_stored_pass1_mfma<128><<<grid, dim3(256), 0, s>>>(a);
+    else score_stored_pass1_mfma<64><<<grid, dim3(256), 0, s>>>(a);
   } else {
     if (D == 128) launch_stored_pass1<float, 128>(a, s);
     else launch_stored_pass1<float, 64>(a, s);
