@@ -484,7 +484,8 @@ struct StoredArgs {
   int32_t nb;               // blocks in this launch
   int32_t n_blocks;         // N (layout of S)
   int32_t T, Hq, Hkv, G, TG, nlg;
-  int32_t chunks_total;     // ceil(N / STATS_CHUNK): (max, sum) partials per row
+  int32_t chunks_total;     // (max, sum) partials per row: ceil(N / chunk)
+  int32_t chunk;            // blocks per partial (bf16: rows per pass-1 workgroup)
   float scale;
   float* S;                 // [nlg][N][TG]
   float2* part;             // [nlg][chunks_total][TG]
@@ -529,11 +530,19 @@ __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
 // memory), B = the TG query rows padded to 16-column tiles (stationary in
 // registers). Each lane's 4 results are rows 4*(l/16) .. +3 of the tile at
 // query row l % 16. The VALU only scales and stores, so the pass streams the
-// index at memory speed. A workgroup takes 1024 rows of one (l, g); each wave
-// keeps 4 tiles (16 KB) of loads in flight.
+// index at memory speed. A workgroup takes `chunk` (512) rows of one (l, g);
+// each wave keeps 4 tiles (16 KB) of loads in flight. Each lane also keeps an online (shift, sum-exp) of its query row, so
+// the workgroup writes the chunk's partials for the LSE itself.
+// Merge two (shift, sum-exp) pairs of the same row.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;                 // both empty
+  s = s * hw_exp2(m - M) + s2 * hw_exp2(m2 - M);
+  m = M;
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-static constexpr int32_t STORED_MFMA_ROWS = 1024;
 
 template <int D>
 __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
@@ -541,11 +550,12 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   constexpr int TU = 4;                        // 16-row tiles in flight per wave
   constexpr int MAXCT = 4;                     // TG < 64: at most 4 column tiles
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int32_t chunks_here = (a.nb + STORED_MFMA_ROWS - 1) / STORED_MFMA_ROWS;
+  __shared__ float2 red[4][64];
+  const int32_t chunks_here = (a.nb + a.chunk - 1) / a.chunk;
   const int32_t lg = blockIdx.x / chunks_here;
   const int32_t ch = blockIdx.x % chunks_here;
-  const int32_t r_begin = ch * STORED_MFMA_ROWS;
-  const int32_t r_end = r_begin + STORED_MFMA_ROWS < a.nb ? r_begin + STORED_MFMA_ROWS : a.nb;
+  const int32_t r_begin = ch * a.chunk;
+  const int32_t r_end = r_begin + a.chunk < a.nb ? r_begin + a.chunk : a.nb;
   const int l = lg / a.Hkv, g = lg % a.Hkv;
   const int r16 = lane & 15, kg = lane >> 4;
   const int nct = (a.TG + 15) / 16;
@@ -566,6 +576,13 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   }
   const uint16_t* base = reinterpret_cast<const uint16_t*>(a.index) + (int64_t)lg * a.lg_stride;
   float* Sl = a.S + ((int64_t)lg * a.n_blocks + a.b_first) * a.TG;
+  // online (shift, sum-exp) of the lane's query rows over its scores
+  float m_run[MAXCT], s_run[MAXCT];
+#pragma unroll
+  for (int ct = 0; ct < MAXCT; ++ct) {
+    m_run[ct] = -INFINITY;
+    s_run[ct] = 0.0f;
+  }
   for (int32_t r0 = r_begin + wave * 16 * TU; r0 < r_end; r0 += 4 * 16 * TU) {
     bf16x8_t av[TU][KS];
 #pragma unroll
@@ -593,11 +610,39 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int32_t row = t0 + 4 * kg + v;
-            if (row < r_end) Sl[(int64_t)row * a.TG + rho] = acc[v] * a.scale;
+            if (row < r_end) {
+              const float x = acc[v] * a.scale;
+              Sl[(int64_t)row * a.TG + rho] = x;
+              if (x > m_run[ct]) {
+                s_run[ct] = s_run[ct] * hw_exp2(m_run[ct] - x) + 1.0f;
+                m_run[ct] = x;
+              } else {
+                s_run[ct] += hw_exp2(x - m_run[ct]);
+              }
+            }
           }
         }
       }
     }
+  }
+  // merge the four lanes of each query row (xor 16, 32), then the waves in order
+  const int32_t gchunk = a.b_first / a.chunk + ch;
+#pragma unroll
+  for (int ct = 0; ct < MAXCT; ++ct) {
+    if (ct >= nct) break;
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(m_run[ct], off), s2 = __shfl_xor(s_run[ct], off);
+      lse_merge(m_run[ct], s_run[ct], m2, s2);
+    }
+    if (kg == 0) red[wave][16 * ct + r16] = make_float2(m_run[ct], s_run[ct]);
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < a.TG) {
+    const int r = threadIdx.x;
+    float mm = red[0][r].x, ss = red[0][r].y;
+    for (int w = 1; w < 4; ++w) lse_merge(mm, ss, red[w][r].x, red[w][r].y);
+    a.part[((int64_t)lg * a.chunks_total + gchunk) * a.TG + r] = make_float2(mm, ss);
   }
 }
 
@@ -607,12 +652,6 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
 // online (shift, sum) per row (one exp per score; the shift moves up when a
 // larger score arrives), then the pairs are merged in a fixed order (xor
 // shuffles, then the four waves in order), so the partials are deterministic.
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  const float M = fmaxf(m, m2);
-  if (M == -INFINITY) return;                 // both empty
-  s = s * hw_exp2(m - M) + s2 * hw_exp2(m2 - M);
-  m = M;
-}
 
 __global__ __launch_bounds__(256) void score_stored_stats(const float* __restrict__ S,
                                                           int32_t n_blocks, int32_t TG,
@@ -671,20 +710,30 @@ __global__ __launch_bounds__(256) void score_stored_stats(const float* __restric
   }
 }
 
-__global__ void score_stored_lse(const float2* __restrict__ part, int32_t nlg, int32_t chunks,
-                                 int32_t TG, float* __restrict__ lse) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)nlg * TG) return;
+// LSE (log2 domain) per (l, g, row) of the stored-score path from its chunk
+// partials: one wavefront per row; lanes stride over the chunks, then xor
+// trees (max in fp32, the rescaled sum in fp64), a fixed order throughout.
+__global__ __launch_bounds__(64) void score_stored_lse(const float2* __restrict__ part,
+                                                       int32_t nlg, int32_t chunks, int32_t TG,
+                                                       float* __restrict__ lse) {
+  const int64_t i = blockIdx.x;                // (lg, r)
+  if (i >= (int64_t)nlg * TG) return;          // uniform
   const int64_t lg = i / TG;
   const int32_t r = (int32_t)(i % TG);
+  const int lane = threadIdx.x;
+  const float2* p = part + lg * chunks * TG + r;
   float M = -INFINITY;
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, part[(lg * chunks + c) * TG + r].x);
+  for (int c = lane; c < chunks; c += 64) M = fmaxf(M, p[(int64_t)c * TG].x);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   double sum = 0.0;
-  for (int c = 0; c < chunks; ++c) {
-    const float2 p = part[(lg * chunks + c) * TG + r];
-    if (p.x != -INFINITY) sum += (double)p.y * exp2((double)p.x - (double)M);
+  for (int c = lane; c < chunks; c += 64) {
+    const float2 v = p[(int64_t)c * TG];
+    if (v.x != -INFINITY) sum += (double)v.y * exp2((double)v.x - (double)M);
   }
-  lse[i] = (float)((double)M + log2(sum));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane == 0) lse[i] = (float)((double)M + log2(sum));
 }
 
 __global__ __launch_bounds__(256) void score_stored_pass2(const float* __restrict__ S,
@@ -713,7 +762,7 @@ __global__ __launch_bounds__(256) void score_stored_pass2(const float* __restric
 
 struct Plan {
   bool mfma;
-  int32_t TG, TGp, nsplit, split_blocks, row_chunks, block_chunks, chunks;
+  int32_t TG, TGp, nsplit, split_blocks, row_chunks, block_chunks, chunks, chunk;
   size_t off_part, off_lse, off_rp, off_S, off_stage, bytes;
 };
 
@@ -721,6 +770,11 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // blocks per (max, sum-exp) partial of the stored-score path
 static constexpr int32_t STATS_CHUNK = 2048;
+
+// The bf16 stored-score pass 1 runs on the matrix cores for up to 64 query
+// rows (4 column tiles); wider fp32 or bf16 cases take the VALU kernel and the
+// separate stats pass.
+static bool stored_on_mfma(int32_t dtype, int32_t TG) { return dtype == KVM_BF16 && TG <= 64; }
 
 static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, int32_t loc,
                       int64_t tile_blocks) {
@@ -746,7 +800,16 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
     p.off_rp = off;
     off = align256(off + (size_t)nlg * N * sizeof(float));
   } else {
-    p.chunks = (int32_t)((N + STATS_CHUNK - 1) / STATS_CHUNK);
+    // (max, sum) partial granularity: bf16 pass 1 forms them per workgroup of
+    // 512 rows (host tiles are multiples of 512, so the resident and the
+    // host-tiled index give the same partials and bit-identical scores); the
+    // other cases use the stats pass over the whole score array
+    if (stored_on_mfma(dtype, p.TG)) {
+      p.chunk = 512;
+    } else {
+      p.chunk = STATS_CHUNK;
+    }
+    p.chunks = (int32_t)((N + p.chunk - 1) / p.chunk);
     p.off_S = off;
     off = align256(off + (size_t)nlg * N * p.TG * sizeof(float));
     p.off_part = off;
@@ -796,12 +859,15 @@ static void launch_stored_pass1(const StoredArgs& a, hipStream_t s) {
 }
 
 static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStream_t s) {
-  if (dtype == KVM_BF16) {
-    const int32_t chunks_here = (a.nb + STORED_MFMA_ROWS - 1) / STORED_MFMA_ROWS;
+  if (stored_on_mfma(dtype, a.TG)) {
+    const int32_t chunks_here = (a.nb + a.chunk - 1) / a.chunk;
     const dim3 grid((uint32_t)((int64_t)a.nlg * chunks_here));
     KernelTimer tm("score_stored_pass1", s);
     if (D == 128) score_stored_pass1_mfma<128><<<grid, dim3(256), 0, s>>>(a);
     else score_stored_pass1_mfma<64><<<grid, dim3(256), 0, s>>>(a);
+  } else if (dtype == KVM_BF16) {
+    if (D == 128) launch_stored_pass1<uint16_t, 128>(a, s);
+    else launch_stored_pass1<uint16_t, 64>(a, s);
   } else {
     if (D == 128) launch_stored_pass1<float, 128>(a, s);
     else launch_stored_pass1<float, 64>(a, s);
@@ -840,8 +906,8 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   if (index_loc == KVM_INDEX_DEVICE)
     KVM_CHECK_ARG(n_blocks <= index_cap_blocks, "n_blocks > index_cap_blocks");
   if (index_loc == KVM_INDEX_HOST_TILED) {
-    KVM_CHECK_ARG(tile_blocks >= 256 && tile_blocks % 256 == 0,
-                  "tile_blocks must be a positive multiple of 256");
+    KVM_CHECK_ARG(tile_blocks >= 512 && tile_blocks % 512 == 0,
+                  "tile_blocks must be a positive multiple of 512");
   }
   const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
   if (!p.mfma) {
@@ -928,6 +994,7 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   a.TG = TG;
   a.nlg = nlg;
   a.chunks_total = p.chunks;
+  a.chunk = p.chunk;
   a.scale = scale;
   a.S = reinterpret_cast<float*>(w + p.off_S);
   a.part = reinterpret_cast<float2*>(w + p.off_part);
@@ -966,13 +1033,15 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
       KVM_HIP(hipEventRecord(tr->used[bi], s));
     }
   }
-  { KernelTimer tm("score_stored_stats", s);
-  score_stored_stats<<<dim3((uint32_t)((int64_t)nlg * p.chunks)), dim3(256), 0, s>>>(
-      a.S, (int32_t)n_blocks, TG, STATS_CHUNK, p.chunks, a.part); }
-  KVM_HIP(hipGetLastError());
+  if (!stored_on_mfma(dtype, TG)) {            // else pass 1 wrote the partials itself
+    KernelTimer tm("score_stored_stats", s);
+    score_stored_stats<<<dim3((uint32_t)((int64_t)nlg * p.chunks)), dim3(256), 0, s>>>(
+        a.S, (int32_t)n_blocks, TG, p.chunk, p.chunks, a.part);
+    KVM_HIP(hipGetLastError());
+  }
   const int64_t nl = (int64_t)nlg * TG;
   { KernelTimer tm("score_stored_lse", s);
-  score_stored_lse<<<dim3((uint32_t)((nl + 255) / 256)), dim3(256), 0, s>>>(
+  score_stored_lse<<<dim3((uint32_t)nl), dim3(64), 0, s>>>(
       a.part, nlg, p.chunks, TG, reinterpret_cast<float*>(w + p.off_lse)); }
   KVM_HIP(hipGetLastError());
   const size_t shm2 = (size_t)nlg * TG * sizeof(float);

@@ -105,12 +105,14 @@ int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
  *
  * q       device, pre-RoPE queries [L][Hq][n_q_tokens][d] in `dtype`.
  * index   KVM_INDEX_DEVICE: device [L][Hkv][index_cap_blocks][d];
- *         KVM_INDEX_HOST_TILED: pinned host, tile-major: tile t (blocks
+ *         KVM_INDEX_HOST_TILED: pinned host, tile-major, tile_blocks a
+ *         positive multiple of 512: tile t (blocks
  *         [t*tile_blocks, (t+1)*tile_blocks)) is [L][Hkv][tile_blocks][d] at
  *         element offset t*L*Hkv*tile_blocks*d (the last tile is full-sized,
  *         rows past n_blocks are ignored). Tiles are streamed through two device
- *         staging buffers in `ws`; the softmax normalisation is global, so the
- *         result equals the resident form.
+ *         staging buffers in `ws`; the softmax normalisation is global and the
+ *         partial sums are grouped the same way, so the result is bit-identical
+ *         to the resident form.
  * scores  device float[n_blocks] (R_b).
  * ws      device workspace of at least kvm_score_ws_bytes(...) bytes.
  * Errors: KVM_EINVAL (shapes, null pointers, n_blocks < 1, n_q_tokens < 1),

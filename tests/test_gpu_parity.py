@@ -179,7 +179,7 @@ def test_scores_steep_ramp_match_oracle(k, dev):
 
 def test_host_tiled_scores_equal_resident(k, dev):
     import torch
-    wl = synth.get_workload("ws10m").scaled(n_layers=4, n_blocks=1300, tile_blocks=256)
+    wl = synth.get_workload("ws10m").scaled(n_layers=4, n_blocks=1300, tile_blocks=512)
     N, tb, nlg, d = wl.n_blocks, wl.tile_blocks, wl.n_layers * wl.n_kv_heads, wl.head_dim
     say("host tiled", N, tb)
     ntile = (N + tb - 1) // tb
@@ -199,6 +199,28 @@ def test_host_tiled_scores_equal_resident(k, dev):
     assert np.array_equal(res, til)
     ref = op.block_scores(op.as_f64(q, "bf16"), op.as_f64(index, "bf16"))
     assert np.max(np.abs(res - ref) / ref) <= 1e-5
+
+
+def test_host_tiled_wide_query_rows_match_oracle(k, dev):
+    """72 query rows per (l, g) from a host-tiled index: the stored-score path
+    with more rows than its matrix-core kernel takes (the VALU kernel and the
+    separate stats pass), against the oracle."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, n_q_tokens=12)
+    N, tb, nlg, d = 1300, 512, wl.n_layers * wl.n_kv_heads, wl.head_dim
+    ntile = (N + tb - 1) // tb
+    index = synth.index_direct(wl.scaled(index_direct=True), 0, N)
+    host = torch.zeros((ntile, nlg, tb, d), dtype=torch.int16).pin_memory()
+    hv = host.numpy().view(np.uint16)
+    ix = index.reshape(nlg, N, d)
+    for t in range(ntile):
+        n = min(tb, N - t * tb)
+        hv[t, :, :n] = ix[:, t * tb:t * tb + n]
+    q = synth.query(wl)
+    til = gc.score_dev(k, wl, gc.to_dev(q, dev), None, N, N, dev, loc=1, tile_blocks=tb,
+                       host_index=host).cpu().numpy().astype(np.float64)
+    ref = op.block_scores(op.as_f64(q, "bf16"), op.as_f64(index, "bf16"))
+    assert np.max(np.abs(til - ref) / ref) <= 1e-5
 
 
 # ---------------------------------------------------------------- select ----
