@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "profile.hpp"
@@ -56,12 +57,13 @@ static constexpr float LOG2E = 1.4426950408889634f;
 // blocks of one split in LDS tiles of 64 blocks.
 template <int D>
 struct MfmaShape {
-  static constexpr int KS = D / 16;               // MFMA k-steps
-  static constexpr int ROW_B = D * 2;             // bytes of one bf16 row
-  static constexpr int LDS_ROW = ROW_B;           // rows unpadded; 16-byte pieces XOR-swizzled
-  static constexpr int TILE = 64;                 // rows staged per iteration
-  static constexpr int SUB = TILE / 32;           // 32-row subtiles per stage
-  static constexpr int LOADS = TILE * ROW_B / (256 * 16);  // 16-B loads per thread
+  static_assert(D == 128, "the MFMA score path is laid out for d = 128");
+  static constexpr int KS = D / 16;                  // MFMA k-steps
+  static constexpr int ROW_B = D * 2;                // bytes of one bf16 row: 16 pieces of 16 B
+  static constexpr int TILE = 128;                   // rows staged per stage
+  static constexpr int SUB = TILE / 32;              // 32-row subtiles per stage
+  static constexpr int TILE_B = TILE * ROW_B;        // bytes per stage buffer
+  static constexpr int LOADS = TILE_B / (256 * 16);  // 16-byte copies per thread per stage
 };
 
 struct Pass1Args {
@@ -92,74 +94,140 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Interleave hint for the scheduler: one MFMA, then `valu` VALU instructions,
-// `n` times, so the matrix pipe and the VALU work on different subtiles at
-// once inside one wavefront.
-template <int N_MFMA, int VALU>
-__device__ __forceinline__ void interleave_mfma_valu() {
+// 32 rows of a staged LDS tile (A operand: lane (half, col) reads piece
+// 2*ks + half of row col at tile + aoff[ks]) times the wave's two stationary B
+// tiles, with the first level of two exp-sum trees of the previous subtile
+// (branch-free VALU work, independent of these MFMAs) woven into the MFMA
+// sequence: a wave issues those exps while its own matrix ops run instead of
+// waiting for them. Scheduling fences fix the order: each MFMA is followed by
+// its share of the 16 pairs (c, v), v < 8: t[c][v] = exp2(fma(p[c][v])) +
+// exp2(fma(p[c][v + 8])), shift sh(c, v). The operand reads run two k-steps
+// ahead; `extra` issues further LDS reads after the first k-step. `tile` is a
+// compile-time LDS address, so every read is a register plus an immediate.
+template <int KS, typename Shift, typename Extra>
+__device__ __forceinline__ void mfma_subtile_woven(f32x16 (&acc)[2], const char* tile,
+                                                   const uint32_t (&aoff)[KS],
+                                                   const bf16x8 (&bop)[2][KS],
+                                                   const f32x16 (&p)[2], float scale, Shift&& sh,
+                                                   float (&t)[2][8], Extra&& extra) {
+  constexpr int PPS = 8 / KS;   // pairs per MFMA slot
+  auto ld = [&](int ks) { return as_bf16x8(*reinterpret_cast<const uint4*>(tile + aoff[ks])); };
+  auto pairs = [&](int slot) {
 #pragma unroll
-  for (int i = 0; i < N_MFMA; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-  }
-}
-
-// 32 rows of the staged LDS tile (A operand, one 16-byte piece per lane and
-// k-step) times the wave's two stationary B tiles.
-template <int KS>
-__device__ __forceinline__ void mfma_subtile(f32x16 (&acc)[2], const char* arow, int half, int xr,
-                                             const bf16x8 (&bop)[2][KS]) {
+    for (int q = 0; q < PPS; ++q) {
+      const int pr = slot * PPS + q, c = pr >> 3, v = pr & 7;
+      t[c][v] = hw_exp2(fmaf(p[c][v], scale, -sh(c, v))) +
+                hw_exp2(fmaf(p[c][v + 8], scale, -sh(c, v + 8)));
+      asm volatile("" ::"v"(t[c][v]));   // keep the pair in its slot (no sinking)
+    }
+  };
   bf16x8 av[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    av[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(arow + (((ks * 2 + half) ^ xr) << 4)));
+  av[0] = ld(0);
+  if (KS > 1) av[1] = ld(1);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[0][ks], acc[0], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    pairs(2 * ks);
+    if (ks + 2 < KS) av[ks + 2] = ld(ks + 2);
+    if (ks == 0) extra();
+    __builtin_amdgcn_sched_barrier(0);
     acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[1][ks], acc[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    pairs(2 * ks + 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Online (shift, sum-exp) update of one lane's query row with 16 new scores
-// (raw dot products; x = acc * scale). The shift m_run is a running maximum
-// that is refreshed lazily: the 16 exps are taken against the current shift,
-// and only a lane whose tile sum exceeds 2^32 (a new score more than 32
-// log2-units above the shift), or that has no shift yet (-inf), or that
-// produced inf/NaN, takes the exact path: tile max, new shift, rescale. Any
-// shift gives the same log-sum-exp, and sums stay below 2^32 per term, so the
-// fp64 running sum loses nothing. A lane that has seen only -inf keeps
-// m = -inf and s = 0.
-__device__ __forceinline__ void lse_update(const f32x16& acc, float scale, float& m_run,
-                                           double& s_run) {
+// Per-lane byte offsets of the A-operand pieces inside a 32-row subtile:
+// lane (half, col) reads piece 2*ks + half of row col, stored XOR-swizzled at
+// piece slot (2*ks + half) ^ (col & 15).
+template <int KS, int ROW_B>
+__device__ __forceinline__ void operand_offsets(uint32_t (&aoff)[KS], int half, int col) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    aoff[ks] = (uint32_t)(col * ROW_B + (((ks * 2 + half) ^ (col & 15)) << 4));
+}
+
+// Runs stage(it, BUF) for it in [0, n) with the stage buffer BUF = it & 1 as a
+// compile-time constant.
+template <typename F>
+__device__ __forceinline__ void for_stages(int n, F&& stage) {
+  for (int it = 0; it < n; it += 2) {
+    stage(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n) stage(it + 1, std::integral_constant<int, 1>{});
+  }
+}
+
+// Remaining levels (w = 4, 2, 1) of the exp-sum tree whose first level
+// mfma_subtile_woven formed; the same order as exp_sum16.
+__device__ __forceinline__ float tree8(float (&t)[8]) {
+#pragma unroll
+  for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+    for (int v = 0; v < w; ++v) t[v] += t[v + w];
+  return t[0];
+}
+
+// Sum of exp2(acc[v] * scale - m) over a lane's 16 values, fixed tree order.
+__device__ __forceinline__ float exp_sum16(const f32x16& acc, float scale, float m) {
   float e[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m_run));
+  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m));
 #pragma unroll
   for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
     for (int v = 0; v < w; ++v) e[v] += e[v + w];
-  if (e[0] <= 4294967296.0f) {
-    s_run += (double)e[0];
-    return;
-  }
+  return e[0];
+}
+
+// Online (shift, sum-exp) update of one lane's query row with 16 new scores
+// (raw dot products; x = acc * scale). The shift m_run is a running maximum
+// that is refreshed lazily: the 16 exps are taken against the current shift
+// (tsum = exp_sum16(acc, scale, m_run)), and only a lane whose tile sum
+// exceeds 2^32 (a new score more than 32 log2-units above the shift), or that
+// has no shift yet (-inf), or that produced inf/NaN, takes the exact path:
+// tile max, new shift, rescale. Any shift gives the same log-sum-exp, and sums
+// stay below 2^32 per term, so the fp64 running sum loses nothing. A lane that
+// has seen only -inf keeps m = -inf and s = 0.
+__device__ __forceinline__ void lse_exact(const f32x16& acc, float scale, float& m_run,
+                                          double& s_run) {
   float mx = acc[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
   const float m_new = fmaxf(m_run, mx * scale);
   const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -m_use));
-#pragma unroll
-  for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-    for (int v = 0; v < w; ++v) e[v] += e[v + w];
   const float resc = hw_exp2(m_run - m_use);
-  s_run = s_run * (double)resc + (double)e[0];
+  s_run = s_run * (double)resc + (double)exp_sum16(acc, scale, m_use);
   m_run = m_new;
+}
+
+__device__ __forceinline__ void lse_commit(const f32x16& acc, float scale, float tsum,
+                                           float& m_run, double& s_run) {
+  if (tsum <= 4294967296.0f) s_run += (double)tsum;
+  else lse_exact(acc, scale, m_run, s_run);
+}
+
+__device__ __forceinline__ void lse_update(const f32x16& acc, float scale, float& m_run,
+                                           double& s_run) {
+  lse_commit(acc, scale, exp_sum16(acc, scale, m_run), m_run, s_run);
+}
+
+// lse_commit of both accumulators, with both tile sums consumed before any
+// branch (a select adds 0 on the exact path, which then starts from the
+// unchanged sum).
+__device__ __forceinline__ void lse_commit2(const f32x16 (&acc)[2], float scale, float ts0,
+                                            float ts1, float (&m_run)[2], double (&s_run)[2]) {
+  const bool ok0 = ts0 <= 4294967296.0f, ok1 = ts1 <= 4294967296.0f;
+  s_run[0] += (double)(ok0 ? ts0 : 0.0f);
+  s_run[1] += (double)(ok1 ? ts1 : 0.0f);
+  if (!ok0) lse_exact(acc[0], scale, m_run[0], s_run[0]);
+  if (!ok1) lse_exact(acc[1], scale, m_run[1], s_run[1]);
 }
 
 __device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nvalid) {
@@ -175,7 +243,7 @@ __device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nv
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   using S = MfmaShape<D>;
-  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE * S::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
   const int32_t per_lg = a.row_chunks * a.nsplit;
   const int32_t L_lg = (int32_t)(lid / per_lg);  // (l, g) flattened = l*Hkv + g
@@ -184,7 +252,8 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   const int32_t split = rem / a.row_chunks;
   const int32_t rchunk = rem % a.row_chunks;
   const int l = L_lg / a.Hkv, g = L_lg % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   // B operand: two 32-row tiles of this wave's query rows (stationary).
@@ -208,55 +277,77 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   int32_t b_end = b_begin + a.split_blocks;
   if (b_end > a.n_blocks) b_end = a.n_blocks;
   const int32_t ntiles = b_end > b_begin ? (b_end - b_begin + S::TILE - 1) / S::TILE : 0;
-  const uint16_t* kb = a.index + (int64_t)L_lg * a.cap * D;
+  const char* kb = reinterpret_cast<const char*>(a.index + (int64_t)L_lg * a.cap * D);
 
   float m_run[2] = {-INFINITY, -INFINITY};
   double s_run[2] = {0.0, 0.0};
 
-  // Direct global->LDS tile copy: slot S (16 bytes) of the tile receives
-  // piece (S & 15) ^ (row & 15) of row S >> 4, so the MFMA operand reads below
-  // (row r, piece c at (c ^ (r & 15))) hit distinct banks. Rows past the end
-  // re-read the last valid row (finite values, masked to -inf later).
-  auto dma_tile = [&](int tile, int buf) {
+  // Direct global->LDS stage copy. Copy i of a wave fills the 1 KiB at slot
+  // (i*4 + wave)*64: slot S (16 bytes) receives piece (S & 15) ^ (row & 15) of
+  // stage row S >> 4, so the operand reads (row r, piece c at c ^ (r & 15))
+  // hit distinct banks. A lane copies rows 16*i + dma_row of the stage, piece
+  // dma_piece: the global address is a uniform stage base plus one 32-bit lane
+  // offset. In a stage that runs past b_end the rows past it re-read the last
+  // valid row (finite values, masked to -inf later).
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_piece = (lane & 15) ^ (dma_row & 15);
+  const uint32_t dma_off = (uint32_t)(dma_row * S::ROW_B + dma_piece * 16);
+  auto dma_stage = [&](int tile, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int32_t t0 = b_begin + tile * S::TILE;
+    const char* base = kb + (int64_t)t0 * S::ROW_B;
+    if (t0 + S::TILE <= b_end) {
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
-      const int r = slot >> 4;
-      const int c = (slot & 15) ^ (r & 15);
-      const int32_t b = t0 + r < b_end ? t0 + r : b_end - 1;
-      dma16(kb + (int64_t)b * D + c * 8, &lds[buf][(i * 4 + wave) * 1024]);
+      for (int i = 0; i < S::LOADS; ++i)
+        dma16(base + i * 16 * S::ROW_B + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int32_t b = t0 + 16 * i + dma_row < b_end ? t0 + 16 * i + dma_row : b_end - 1;
+        dma16(kb + (int64_t)b * S::ROW_B + dma_piece * 16, &lds[BUF][(i * 4 + wave) * 1024]);
+      }
     }
   };
-  auto arow = [&](int buf, int sub) -> const char* {
-    return &lds[buf][(sub * 32 + col) * S::LDS_ROW];
-  };
-  auto update = [&](f32x16 (&acc)[2], int32_t nvalid) {
-    if (nvalid < 32) mask_rows(acc, half, nvalid);   // uniform: only a split's last tile
-    lse_update(acc[0], a.scale, m_run[0], s_run[0]);
-    lse_update(acc[1], a.scale, m_run[1], s_run[1]);
-  };
+  uint32_t aoff[S::KS];
+  operand_offsets<S::KS, S::ROW_B>(aoff, half, col);
 
-  // A stage holds SUB subtiles of 32 blocks; the next stage's global loads
-  // are in flight while all of them are multiplied and reduced.
-  f32x16 acc[2];
-  const int xr = col & 15;
-  if (ntiles > 0) dma_tile(0, 0);
+  // Software pipeline over 32-block subtiles: while the MFMAs of subtile j
+  // run, the wave takes the exps of subtile j-1 (its scores sit in the other
+  // accumulator set). ab[j & 1] holds subtile j; before the first subtile the
+  // other set holds -inf scores, which leave (m, s) = (-inf, 0) unchanged.
+  // The order of the updates, and so every rounding, is that of the plain
+  // loop. A stage holds SUB (even) subtiles; the next stage's global loads are
+  // in flight while they are multiplied and reduced.
+  static_assert(S::SUB % 2 == 0, "subtile slots alternate within a stage");
+  f32x16 ab[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ab[1][c][v] = -INFINITY;
+  if (ntiles > 0) dma_stage(0, std::integral_constant<int, 0>{});
   wait_dma();
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  for_stages(ntiles, [&](int it, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int32_t t0 = b_begin + it * S::TILE;
-    const bool more = it + 1 < ntiles;
-    if (more) dma_tile(it + 1, buf ^ 1);
-#pragma unroll 1
+    if (it + 1 < ntiles) dma_stage(it + 1, std::integral_constant<int, BUF ^ 1>{});
+#pragma unroll
     for (int sub = 0; sub < S::SUB; ++sub) {
-      mfma_subtile<S::KS>(acc, arow(buf, sub), half, xr, bq);
-      update(acc, b_end - (t0 + 32 * sub));
+      f32x16 (&cur)[2] = ab[sub & 1];
+      f32x16 (&prv)[2] = ab[(sub & 1) ^ 1];
+      float t[2][8];
+      const float m0 = m_run[0], m1 = m_run[1];
+      mfma_subtile_woven<S::KS>(cur, &lds[BUF][sub * 32 * S::ROW_B], aoff, bq, prv, a.scale,
+                                [&](int c, int) { return c ? m1 : m0; }, t, [] {});
+      lse_commit2(prv, a.scale, tree8(t[0]), tree8(t[1]), m_run, s_run);
+      const int32_t nvalid = b_end - (t0 + 32 * sub);
+      if (nvalid < 32) mask_rows(cur, half, nvalid);   // uniform: only a split's last stage
     }
     wait_dma();
     __syncthreads();
-  }
+  });
+  lse_update(ab[1][0], a.scale, m_run[0], s_run[0]);   // the last subtile
+  lse_update(ab[1][1], a.scale, m_run[1], s_run[1]);
   // Merge the two lane halves (same query row, disjoint blocks).
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -310,9 +401,10 @@ struct Pass2Args {
   uint32_t total_wg;
 };
 
-// Column sums over one subtile's 16 rows per lane: sum of exp2(acc*scale - lse).
-__device__ __forceinline__ void colsum_update(const f32x16& acc, const float (&ls)[16],
-                                              float scale, double& colsum) {
+// Column sum over one subtile's 16 rows of a lane: sum of exp2(acc*scale - lse),
+// fixed tree order.
+__device__ __forceinline__ float exp_sum16_rows(const f32x16& acc, const float (&ls)[16],
+                                                float scale) {
   float e[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) e[v] = hw_exp2(fmaf(acc[v], scale, -ls[v]));
@@ -320,20 +412,21 @@ __device__ __forceinline__ void colsum_update(const f32x16& acc, const float (&l
   for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
     for (int v = 0; v < w; ++v) e[v] += e[v + w];
-  colsum += (double)e[0];
+  return e[0];
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   using S = MfmaShape<D>;
-  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE * S::LDS_ROW];
+  __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   __shared__ __attribute__((aligned(16))) float lse_s[2][S::TILE];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
   const int32_t lg = (int32_t)(lid / a.block_chunks);
   if (lg >= a.nlg) return;                       // grid padding
   const int32_t bchunk = (int32_t)(lid % a.block_chunks);
   const int l = lg / a.Hkv, g = lg % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
 
   // B operand: this wave's two 32-block tiles (stationary).
@@ -354,55 +447,81 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   const float* lse_lg = a.lse + (int64_t)lg * a.TGp;
   const int32_t ntiles = (a.TG + S::TILE - 1) / S::TILE;
   // Query rows of (l, g) are contiguous: heads g*G .. g*G+G-1, tokens 0..T-1.
-  const uint16_t* qg = a.q + ((int64_t)l * a.Hq + (int64_t)g * a.G) * a.T * D;
-  auto dma_tile = [&](int tile, int buf) {
+  const char* qg =
+      reinterpret_cast<const char*>(a.q + ((int64_t)l * a.Hq + (int64_t)g * a.G) * a.T * D);
+  // Stage copies as in pass 1 (same slot layout), plus the stage's LSE values
+  // (waves 0 and 1, 64 each; rows past TG read the +inf padding of the LSE
+  // array, whose rows TG..TGp-1 exist because TGp is a multiple of 256).
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_piece = (lane & 15) ^ (dma_row & 15);
+  const uint32_t dma_off = (uint32_t)(dma_row * S::ROW_B + dma_piece * 16);
+  auto dma_stage = [&](int tile, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int32_t r0 = tile * S::TILE;
+    const char* base = qg + (int64_t)r0 * S::ROW_B;
+    if (r0 + S::TILE <= a.TG) {
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
-      const int r = slot >> 4;
-      const int c = (slot & 15) ^ (r & 15);
-      const int32_t rho = r0 + r < a.TG ? r0 + r : a.TG - 1;  // padded rows: lse = +inf
-      dma16(qg + (int64_t)rho * D + c * 8, &lds[buf][(i * 4 + wave) * 1024]);
+      for (int i = 0; i < S::LOADS; ++i)
+        dma16(base + i * 16 * S::ROW_B + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int32_t rho = r0 + 16 * i + dma_row < a.TG ? r0 + 16 * i + dma_row : a.TG - 1;
+        dma16(qg + (int64_t)rho * S::ROW_B + dma_piece * 16, &lds[BUF][(i * 4 + wave) * 1024]);
+      }
     }
-    if (wave == 0) dma4(lse_lg + r0 + lane, &lse_s[buf][0]);
+    if (wave < 2) dma4(lse_lg + r0 + wave * 64 + lane, &lse_s[BUF][wave * 64]);
   };
-  auto arow = [&](int buf, int sub) -> const char* {
-    return &lds[buf][(sub * 32 + col) * S::LDS_ROW];
-  };
+  uint32_t aoff[S::KS];
+  operand_offsets<S::KS, S::ROW_B>(aoff, half, col);
   // LSE of the 16 rows a lane holds in a subtile: rows 8*q4 + 4*half + 0..3.
-  auto load_lse = [&](float (&ls)[16], int buf, int sub) {
+  auto load_lse = [&](float (&ls)[16], const float* sub_lse) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 v4 =
-          *reinterpret_cast<const float4*>(&lse_s[buf][sub * 32 + 8 * q4 + 4 * half]);
+      const float4 v4 = *reinterpret_cast<const float4*>(sub_lse + 8 * q4 + 4 * half);
       ls[4 * q4 + 0] = v4.x;
       ls[4 * q4 + 1] = v4.y;
       ls[4 * q4 + 2] = v4.z;
       ls[4 * q4 + 3] = v4.w;
     }
   };
+  // Software pipeline as in pass 1: the exps and column sums of subtile j-1
+  // run under the MFMAs of subtile j. Each subtile's LSE values are read from
+  // LDS in the block that multiplies it (before the barrier that frees its
+  // buffer) and kept in registers for the next block. The dummy subtile
+  // before the first (-inf scores, LSE 0) adds exactly 0.
+  static_assert(S::SUB % 2 == 0, "subtile slots alternate within a stage");
   double colsum[2] = {0.0, 0.0};
-  f32x16 acc[2];
-  float ls[16];
-  const int xr = col & 15;
-  dma_tile(0, 0);
+  f32x16 ab[2][2];
+  float lsb[2][16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    ab[1][0][v] = -INFINITY;
+    ab[1][1][v] = -INFINITY;
+    lsb[1][v] = 0.0f;
+  }
+  dma_stage(0, std::integral_constant<int, 0>{});
   wait_dma();
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const bool more = it + 1 < ntiles;
-    if (more) dma_tile(it + 1, buf ^ 1);
-#pragma unroll 1
+  for_stages(ntiles, [&](int it, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (it + 1 < ntiles) dma_stage(it + 1, std::integral_constant<int, BUF ^ 1>{});
+#pragma unroll
     for (int sub = 0; sub < S::SUB; ++sub) {
-      mfma_subtile<S::KS>(acc, arow(buf, sub), half, xr, bk);
-      load_lse(ls, buf, sub);
-      colsum_update(acc[0], ls, a.scale, colsum[0]);
-      colsum_update(acc[1], ls, a.scale, colsum[1]);
+      const int j = sub & 1;
+      float t[2][8];
+      const float (&lp)[16] = lsb[j ^ 1];
+      mfma_subtile_woven<S::KS>(ab[j], &lds[BUF][sub * 32 * S::ROW_B], aoff, bk, ab[j ^ 1],
+                                a.scale, [&](int, int v) { return lp[v]; }, t,
+                                [&] { load_lse(lsb[j], &lse_s[BUF][sub * 32]); });
+      colsum[0] += (double)tree8(t[0]);
+      colsum[1] += (double)tree8(t[1]);
     }
     wait_dma();
     __syncthreads();
-  }
+  });
+  colsum[0] += (double)exp_sum16_rows(ab[1][0], lsb[1], a.scale);   // the last subtile
+  colsum[1] += (double)exp_sum16_rows(ab[1][1], lsb[1], a.scale);
 #pragma unroll
   for (int bt = 0; bt < 2; ++bt) {
     const double tot = colsum[bt] + __shfl_xor(colsum[bt], 32);
