@@ -4,31 +4,86 @@
 // selection in chronological (ascending) order with compact base positions
 // i * B (Sec. 4.4, Sec. 5).
 //
-// One 1024-thread workgroup does the whole selection: N is at most a few
-// hundred thousand blocks (a 10M-token workspace has 312,500), i.e. about a
-// megabyte of scores that stays in L2, so a single CU finishes in tens of
-// microseconds while scoring takes milliseconds.
-//  1. Validate (every score finite and >= 0; -0.0 counts as 0).
-//  2. Radix select on the fp32 bit pattern (non-negative floats order like
-//     their bits): four 8-bit digit passes with LDS histograms find the exact
-//     key T of the k-th largest candidate and how many candidates equal to T
-//     must be taken.
-//  3. Ordered compaction: each thread owns a contiguous index range; two
-//     wavefront-shuffle scans (ties, then selected counts) give every thread
-//     its tie rank and its output offset, so ties go to the lowest ids and the
+// Non-negative floats order like their bit patterns (-0.0 counts as 0), so
+// the k-th largest candidate is found by an exact radix select on the fp32
+// bits, 8 bits per round, spread over many workgroups (a 10M-token workspace
+// has 312,500 blocks; one workgroup spends most of its time in LDS atomics on
+// the few histogram bins that hold almost every key):
+//  1. sel_init resets the control words (digit prefix, keys still to take).
+//  2. Four rounds of sel_hist (each workgroup: LDS histogram of the current
+//     digit over its chunk of candidates that match the fixed digits, with
+//     per-thread run-length counting and one wave-aggregated add for the most
+//     common pending digit) and sel_digit (one workgroup: sum the chunk
+//     histograms, pick the digit holding the krem-th largest key, fix it).
+//     Afterwards T is the key of the k-th largest candidate and krem the
+//     number of candidates equal to T that are taken (the lowest ids).
+//  3. sel_count validates every score (finite, >= 0) and counts per chunk the
+//     kept blocks (sink, recent, keys > T) and the ties (keys == T).
+//  4. sel_write: each chunk's output offset is (kept before it) + min(ties
+//     before it, krem); inside the chunk every thread owns 16 consecutive
+//     blocks and two workgroup scans give its tie rank and its offset, so the
 //     output is ascending without a sort.
+// With n_blocks <= budget every block is selected (select_all_kernel).
 #include "common.hpp"
 #include "profile.hpp"
 
 namespace kvm {
 
+namespace {
+
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_PER = 16;                          // blocks per thread
+constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER;     // blocks per workgroup
+constexpr int CTL_WORDS = 64;                        // control area (words)
+enum { CTL_BAD = 0, CTL_PREFIX = 1, CTL_KREM = 2 };
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct SelWs {
+  uint32_t* ctl;    // [CTL_WORDS]
+  uint32_t* hist;   // [nwg][256]
+  uint32_t* cnt;    // [nwg][2]: kept, ties
+};
+
+int64_t sel_nwg(int64_t n) { return (n + SEL_CHUNK - 1) / SEL_CHUNK; }
+
+size_t sel_ws_bytes(int64_t n) {
+  const int64_t nwg = sel_nwg(n);
+  return align256(CTL_WORDS * 4) + align256((size_t)nwg * 256 * 4) + align256((size_t)nwg * 8);
+}
+
+SelWs sel_ws(void* ws, int64_t n) {
+  char* p = reinterpret_cast<char*>(ws);
+  const int64_t nwg = sel_nwg(n);
+  SelWs w;
+  w.ctl = reinterpret_cast<uint32_t*>(p);
+  w.hist = reinterpret_cast<uint32_t*>(p + align256(CTL_WORDS * 4));
+  w.cnt = reinterpret_cast<uint32_t*>(p + align256(CTL_WORDS * 4) +
+                                      align256((size_t)nwg * 256 * 4));
+  return w;
+}
+
+}  // namespace
+
 __device__ __forceinline__ uint32_t score_key(float f) {
   return f == 0.0f ? 0u : __float_as_uint(f);
 }
 
-// Exclusive scan of one uint32 per thread over the 1024-thread workgroup.
-// Returns the exclusive prefix; *total receives the sum over all threads.
+__device__ __forceinline__ bool score_bad(float f) {
+  return !(f >= 0.0f) || f == __builtin_inff();
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Exclusive scan of one uint32 per thread over a workgroup of NT threads
+// (NT / 64 <= 16 waves). Returns the exclusive prefix; *total receives the sum.
+template <int NT>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -39,15 +94,15 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_
   if (lane == 63) wave_tot[wave] = x;
   __syncthreads();
   if (wave == 0) {
-    uint32_t t = lane < 16 ? wave_tot[lane] : 0u;
+    uint32_t t = lane < NW ? wave_tot[lane] : 0u;
     uint32_t s = t;
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
+    for (int off = 1; off < NW; off <<= 1) {
       uint32_t y = __shfl_up(s, off);
       if (lane >= off) s += y;
     }
-    if (lane < 16) wave_tot[16 + lane] = s - t;  // exclusive wave offsets
-    if (lane == 15) wave_tot[32] = s;
+    if (lane < NW) wave_tot[16 + lane] = s - t;  // exclusive wave offsets
+    if (lane == NW - 1) wave_tot[32] = s;
   }
   __syncthreads();
   const uint32_t res = wave_tot[16 + wave] + x - v;
@@ -56,116 +111,226 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_
   return res;
 }
 
-__global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ scores,
-                                                      int64_t N, int32_t n_sink, int32_t n_recent,
-                                                      int32_t budget, int32_t B,
-                                                      int32_t* __restrict__ sel,
-                                                      int32_t* __restrict__ n_sel,
-                                                      int32_t* __restrict__ base_pos) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_tot[40];
-  __shared__ uint32_t s_prefix, s_krem;
-  const int tid = threadIdx.x;
+__global__ void sel_init(uint32_t* ctl, uint32_t k) {
+  if (threadIdx.x == 0) {
+    ctl[CTL_BAD] = 0u;
+    ctl[CTL_PREFIX] = 0u;
+    ctl[CTL_KREM] = k;
+  }
+}
 
-  int bad = 0;
-  for (int64_t i = tid; i < N; i += 1024) {
-    const float f = scores[i];
-    if (!(f >= 0.0f) || f == __builtin_inff()) bad = 1;
-  }
-  if (__syncthreads_or(bad)) {
-    if (tid == 0) *n_sel = KVM_ERANGE;
-    return;
-  }
-  if (N <= budget) {
-    for (int64_t i = tid; i < N; i += 1024) {
-      sel[i] = (int32_t)i;
-      base_pos[i] = (int32_t)i * B;
-    }
-    if (tid == 0) *n_sel = (int32_t)N;
-    return;
-  }
-
-  const int64_t c0 = n_sink, c1 = N - n_recent;
-  const uint32_t k = (uint32_t)(budget - n_sink - n_recent);
-  if (tid == 0) {
-    s_prefix = 0u;
-    s_krem = k;
+// Histogram of digit (key >> shift) & 255 over this chunk's candidates whose
+// digits above `shift` equal those already fixed in ctl[CTL_PREFIX].
+__global__ __launch_bounds__(SEL_THREADS) void sel_hist(const float* __restrict__ scores,
+                                                        int64_t c0, int64_t c1, int shift,
+                                                        const uint32_t* __restrict__ ctl,
+                                                        uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[256];
+  const int t = threadIdx.x, lane = t & 63;
+  h[t] = 0u;
+  const uint32_t hi = shift < 24 ? ctl[CTL_PREFIX] >> (shift + 8) : 0u;
+  const int64_t base = (int64_t)blockIdx.x * SEL_CHUNK;
+  uint32_t key[SEL_PER];
+  bool in[SEL_PER];
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {   // all loads first (coalesced across lanes)
+    const int64_t i = base + j * SEL_THREADS + t;
+    in[j] = i >= c0 && i < c1;
+    key[j] = in[j] ? score_key(scores[i]) : 0u;
   }
   __syncthreads();
-  if (k > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += 1024) hist[i] = 0u;
-      __syncthreads();
-      const uint32_t prefix = s_prefix;
-      for (int64_t c = c0 + tid; c < c1; c += 1024) {
-        const uint32_t key = score_key(scores[c]);
-        const bool match = shift == 24 || ((key >> (shift + 8)) == (prefix >> (shift + 8)));
-        if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0, krem = s_krem;
-        for (int dg = 255; dg >= 0; --dg) {
-          if (cum + hist[dg] >= krem) {
-            s_prefix = prefix | ((uint32_t)dg << shift);
-            s_krem = krem - cum;
-            break;
-          }
-          cum += hist[dg];
-        }
-      }
-      __syncthreads();
+  uint32_t cur = 0u, cnt = 0u;
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {
+    const bool match = in[j] && (shift == 24 || (key[j] >> (shift + 8)) == hi);
+    if (!match) continue;
+    const uint32_t d = (key[j] >> shift) & 255u;
+    if (cnt > 0 && d != cur) atomicAdd(&h[cur], cnt), cnt = 0u;
+    cur = d;
+    ++cnt;
+  }
+  // The wave's most common pending digit is usually the first lane's: add it
+  // once for all lanes that hold it, the rest directly.
+  bool act = cnt > 0;
+  const uint64_t m = __ballot(act);
+  if (m != 0) {
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    const uint32_t ld = __shfl(cur, leader);
+    const bool same = act && cur == ld;
+    const uint32_t tot = wave_sum(same ? cnt : 0u);
+    if (lane == leader) atomicAdd(&h[ld], tot);
+    if (same) act = false;
+  }
+  if (act) atomicAdd(&h[cur], cnt);
+  __syncthreads();
+  hist[(int64_t)blockIdx.x * 256 + t] = h[t];
+}
+
+// Fix the digit at `shift`: the largest digit dg whose keys, with all larger
+// digits, reach krem; krem becomes the rank of the target inside digit dg.
+__global__ __launch_bounds__(256) void sel_digit(const uint32_t* __restrict__ hist, int64_t nwg,
+                                                 int shift, uint32_t* __restrict__ ctl) {
+  __shared__ uint32_t wave_tot[40];
+  const int t = threadIdx.x;
+  const uint32_t krem = ctl[CTL_KREM], prefix = ctl[CTL_PREFIX];
+  uint32_t s = 0u;
+  for (int64_t w = 0; w < nwg; ++w) s += hist[w * 256 + t];
+  // above(t) = sum of digits > t: an exclusive scan in descending digit order.
+  const int r = 255 - t;
+  __shared__ uint32_t rev[256];
+  rev[r] = s;
+  __syncthreads();
+  const uint32_t v = rev[t];   // digit 255 - t
+  uint32_t total;
+  const uint32_t ex = block_exclusive_scan<256>(v, wave_tot, &total);
+  // thread t holds digit dg = 255 - t with above = ex
+  if (ex < krem && krem <= ex + v) {
+    ctl[CTL_PREFIX] = prefix | ((uint32_t)(255 - t) << shift);
+    ctl[CTL_KREM] = krem - ex;
+  }
+}
+
+// Per chunk: validation of every score, kept blocks and ties.
+__global__ __launch_bounds__(SEL_THREADS) void sel_count(const float* __restrict__ scores,
+                                                         int64_t N, int64_t c0, int64_t c1,
+                                                         int has_k, uint32_t* __restrict__ ctl,
+                                                         uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t red[2][SEL_THREADS / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t T = has_k ? ctl[CTL_PREFIX] : 0xffffffffu;
+  const int64_t base = (int64_t)blockIdx.x * SEL_CHUNK;
+  uint32_t kept = 0u, tie = 0u;
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {
+    const int64_t i = base + j * SEL_THREADS + t;
+    if (i >= N) continue;
+    const float f = scores[i];
+    bad |= score_bad(f);
+    if (i < c0 || i >= c1) {
+      ++kept;
+    } else if (has_k) {
+      const uint32_t key = score_key(f);
+      kept += key > T;
+      tie += key == T;
     }
   }
-  // T: key of the k-th largest candidate; take the first `krem` candidates
-  // (lowest ids) whose key equals T. With k == 0 nothing is taken.
-  const uint32_t T = k > 0 ? s_prefix : 0xffffffffu;
-  const uint32_t krem = k > 0 ? s_krem : 0u;
-
-  const int64_t per = (N + 1023) / 1024;
-  const int64_t lo = (int64_t)tid * per;
-  const int64_t hi = lo + per < N ? lo + per : N;
-  uint32_t n_above = 0, n_tie = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    if (i < c0 || i >= c1) {
-      ++n_above;
-    } else {
-      const uint32_t key = score_key(scores[i]);
-      if (k > 0 && key > T) ++n_above;
-      else if (k > 0 && key == T) ++n_tie;
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(&ctl[CTL_BAD], 1u);
+  kept = wave_sum(kept);
+  tie = wave_sum(tie);
+  if (lane == 0) {
+    red[0][wave] = kept;
+    red[1][wave] = tie;
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t a = 0u, b = 0u;
+#pragma unroll
+    for (int w = 0; w < SEL_THREADS / 64; ++w) {
+      a += red[0][w];
+      b += red[1][w];
     }
+    cnt[2 * blockIdx.x] = a;
+    cnt[2 * blockIdx.x + 1] = b;
+  }
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void sel_write(
+    const float* __restrict__ scores, int64_t N, int64_t c0, int64_t c1, int has_k,
+    const uint32_t* __restrict__ ctl, const uint32_t* __restrict__ cnt, int32_t B,
+    int32_t budget, int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int32_t* __restrict__ base_pos) {
+  __shared__ uint32_t wave_tot[40];
+  __shared__ uint32_t s_before[2];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (ctl[CTL_BAD] != 0u) {
+    if (blockIdx.x == 0 && t == 0) *n_sel = KVM_ERANGE;
+    return;
+  }
+  const uint32_t T = has_k ? ctl[CTL_PREFIX] : 0xffffffffu;
+  const uint32_t krem = has_k ? ctl[CTL_KREM] : 0u;
+  if (wave == 0) {   // kept blocks and ties in the chunks before this one
+    uint32_t a = 0u, b = 0u;
+    for (int64_t w = lane; w < blockIdx.x; w += 64) {
+      a += cnt[2 * w];
+      b += cnt[2 * w + 1];
+    }
+    a = wave_sum(a);
+    b = wave_sum(b);
+    if (lane == 0) {
+      s_before[0] = a;
+      s_before[1] = b;
+    }
+  }
+  __syncthreads();
+  const uint32_t kept_before = s_before[0], tie_before = s_before[1];
+  const uint32_t wg_ties = cnt[2 * blockIdx.x + 1];
+  const uint32_t wg_take = krem > tie_before ? (krem - tie_before < wg_ties ? krem - tie_before
+                                                                             : wg_ties)
+                                             : 0u;
+  const uint32_t out0 = kept_before + (tie_before < krem ? tie_before : krem);
+
+  const int64_t lo = (int64_t)blockIdx.x * SEL_CHUNK + (int64_t)t * SEL_PER;
+  uint32_t key[SEL_PER];
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) key[j] = lo + j < N ? score_key(scores[lo + j]) : 0u;
+  auto kind = [&](int j) -> int {   // 0 none, 1 kept, 2 tie
+    const int64_t i = lo + j;
+    if (i >= N) return 0;
+    if (i < c0 || i >= c1) return 1;
+    if (!has_k) return 0;
+    return key[j] > T ? 1 : (key[j] == T ? 2 : 0);
+  };
+  uint32_t n_kept = 0u, n_tie = 0u;
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {
+    const int k = kind(j);
+    n_kept += k == 1;
+    n_tie += k == 2;
   }
   uint32_t tie_total;
-  const uint32_t tie_base = block_exclusive_scan(n_tie, wave_tot, &tie_total);
-  uint32_t take_ties = 0;
-  if (krem > tie_base) take_ties = (krem - tie_base) < n_tie ? (krem - tie_base) : n_tie;
+  const uint32_t tie_base = block_exclusive_scan<SEL_THREADS>(n_tie, wave_tot, &tie_total);
+  uint32_t take = 0u;
+  if (wg_take > tie_base) take = wg_take - tie_base < n_tie ? wg_take - tie_base : n_tie;
   uint32_t out_total;
-  const uint32_t out_base = block_exclusive_scan(n_above + take_ties, wave_tot, &out_total);
-  uint32_t o = out_base, t_seen = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    bool take;
-    if (i < c0 || i >= c1) {
-      take = true;
-    } else {
-      const uint32_t key = score_key(scores[i]);
-      if (k > 0 && key > T) take = true;
-      else if (k > 0 && key == T) take = (t_seen++ < take_ties);
-      else take = false;
-    }
-    if (take) {
-      sel[o] = (int32_t)i;
+  const uint32_t out_base = block_exclusive_scan<SEL_THREADS>(n_kept + take, wave_tot, &out_total);
+  uint32_t o = out0 + out_base, seen = 0u;
+#pragma unroll
+  for (int j = 0; j < SEL_PER; ++j) {
+    const int k = kind(j);
+    const bool w = k == 1 || (k == 2 && seen++ < take);
+    if (w && o < (uint32_t)budget) {   // always true for consistent counts
+      sel[o] = (int32_t)(lo + j);
       base_pos[o] = (int32_t)o * B;
       ++o;
     }
   }
-  if (tid == 0) *n_sel = (int32_t)out_total;
+  if (blockIdx.x == gridDim.x - 1 && t == 0) *n_sel = (int32_t)(out0 + out_total);
+}
+
+// n_blocks <= budget: every block, after validation.
+__global__ __launch_bounds__(1024) void select_all_kernel(const float* __restrict__ scores,
+                                                          int64_t N, int32_t B,
+                                                          int32_t* __restrict__ sel,
+                                                          int32_t* __restrict__ n_sel,
+                                                          int32_t* __restrict__ base_pos) {
+  const int tid = threadIdx.x;
+  int bad = 0;
+  for (int64_t i = tid; i < N; i += 1024) bad |= score_bad(scores[i]);
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) *n_sel = KVM_ERANGE;
+    return;
+  }
+  for (int64_t i = tid; i < N; i += 1024) {
+    sel[i] = (int32_t)i;
+    base_pos[i] = (int32_t)i * B;
+  }
+  if (tid == 0) *n_sel = (int32_t)N;
 }
 
 }  // namespace kvm
 
 extern "C" size_t kvm_select_ws_bytes(int64_t n_blocks) {
-  (void)n_blocks;
-  return 0;
+  return kvm::sel_ws_bytes(n_blocks > 0 ? n_blocks : 1);
 }
 
 extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
@@ -173,8 +338,6 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
                           int32_t* n_sel, int32_t* base_pos, void* ws, size_t ws_bytes,
                           void* stream) {
   using namespace kvm;
-  (void)ws;
-  (void)ws_bytes;
   clear_error();
   KVM_CHECK_ARG(scores && sel && n_sel && base_pos, "null pointer");
   KVM_CHECK_ARG(n_blocks >= 1 && n_blocks < 0x7fffffffLL, "n_blocks out of range");
@@ -185,10 +348,36 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     return KVM_ERANGE;
   }
   KVM_CHECK_ARG((int64_t)budget_blocks * block_tokens < 0x7fffffffLL, "positions overflow int32");
-  KernelTimer tm("select", as_stream(stream));
-  select_kernel<<<1, 1024, 0, as_stream(stream)>>>(scores, n_blocks, n_sink, n_recent,
-                                                   budget_blocks, block_tokens, sel, n_sel,
-                                                   base_pos);
+  hipStream_t s = as_stream(stream);
+  KernelTimer tm("select", s);
+  if (n_blocks <= budget_blocks) {
+    select_all_kernel<<<1, 1024, 0, s>>>(scores, n_blocks, block_tokens, sel, n_sel, base_pos);
+    KVM_HIP(hipGetLastError());
+    return KVM_OK;
+  }
+  const size_t need = sel_ws_bytes(n_blocks);
+  if (!ws || ws_bytes < need) {
+    set_error("select workspace %zu < %zu bytes", ws_bytes, need);
+    return KVM_ENOMEM;
+  }
+  KVM_CHECK_ARG((uintptr_t)ws % 256 == 0, "ws must be 256-byte aligned");
+  const SelWs w = sel_ws(ws, n_blocks);
+  const int64_t nwg = sel_nwg(n_blocks);
+  const int64_t c0 = n_sink, c1 = n_blocks - n_recent;
+  const uint32_t k = (uint32_t)(budget_blocks - n_sink - n_recent);
+  sel_init<<<1, 64, 0, s>>>(w.ctl, k);
+  if (k > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      sel_hist<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, c0, c1, shift, w.ctl,
+                                                                 w.hist);
+      sel_digit<<<1, 256, 0, s>>>(w.hist, nwg, shift, w.ctl);
+    }
+  }
+  sel_count<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, n_blocks, c0, c1, k > 0,
+                                                              w.ctl, w.cnt);
+  sel_write<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, n_blocks, c0, c1, k > 0,
+                                                              w.ctl, w.cnt, block_tokens,
+                                                              budget_blocks, sel, n_sel, base_pos);
   KVM_HIP(hipGetLastError());
   return KVM_OK;
 }

@@ -48,6 +48,8 @@ class WorkingSetUpdater:
         self.base_pos = torch.empty(budget_blocks, dtype=torch.int32, device=device)
         self.page_table = torch.empty(budget_blocks, dtype=torch.int32, device=device)
         self.scores = torch.empty(index_cap, dtype=torch.float32, device=device)
+        self.sel_ws = torch.empty(api.kvm_select_ws_bytes(index_cap), dtype=torch.uint8,
+                                  device=device)
         self.ws = None
         self.ws_key = None
         self.n_blocks = 0
@@ -84,7 +86,8 @@ class WorkingSetUpdater:
 
     def select(self):
         api.kvm_select(self.scores, self.n_blocks, self.n_sink, self.n_recent, self.budget,
-                       self.dims.block_tokens, self.sel, self.n_sel, self.base_pos)
+                       self.dims.block_tokens, self.sel, self.n_sel, self.base_pos,
+                       self.sel_ws, self.sel_ws.numel())
 
     def rematerialize(self) -> dict:
         return self.ctx.kvm_rematerialize(self.sel, self.n_sel, self.page_table)

@@ -129,6 +129,7 @@ class Workspace:
         self.n_sel = torch.empty(1, dtype=torch.int32, device=dev)
         self.base = torch.empty(Kb, dtype=torch.int32, device=dev)
         self.page = torch.empty(Kb, dtype=torch.int32, device=dev)
+        self.sel_ws = torch.empty(k.kvm_select_ws_bytes(N), dtype=torch.uint8, device=dev)
         log(f"index ready in {time.time() - t0:.1f}s")
 
     def _gen_dev(self, which, b0, nb):
@@ -143,7 +144,8 @@ class Workspace:
         k.kvm_score_blocks(self.dims, self.dt, self.q, wl.n_q_tokens, self.index, self.N, self.N,
                            k.KVM_INDEX_DEVICE, 0, self.scores, self.ws, self.ws_bytes)
         k.kvm_select(self.scores, self.N, wl.n_sink, wl.n_recent, wl.budget_blocks,
-                     wl.block_tokens, self.sel, self.n_sel, self.base)
+                     wl.block_tokens, self.sel, self.n_sel, self.base, self.sel_ws,
+                     self.sel_ws.numel())
 
     def setup_pool(self, sel: np.ndarray):
         """Pool + context; even-ranked selected blocks resident, odd-ranked staged."""
@@ -420,6 +422,7 @@ def run_ws10m(args, k, wl, dev):
     sel = torch.empty(wl.budget_blocks, dtype=torch.int32, device=dev)
     n_sel = torch.empty(1, dtype=torch.int32, device=dev)
     base = torch.empty(wl.budget_blocks, dtype=torch.int32, device=dev)
+    sel_ws = torch.empty(k.kvm_select_ws_bytes(N), dtype=torch.uint8, device=dev)
     log(f"setup {time.time() - t0:.1f}s")
 
     def leg(loc):
@@ -430,7 +433,7 @@ def run_ws10m(args, k, wl, dev):
         def step():
             k.kvm_score_blocks(dims, bf, q, 1, src, N, N, loc, tiles, scores, ws, wsb)
             k.kvm_select(scores, N, wl.n_sink, wl.n_recent, wl.budget_blocks, wl.block_tokens,
-                         sel, n_sel, base)
+                         sel, n_sel, base, sel_ws, sel_ws.numel())
         for _ in range(max(1, args.warmup)):
             step()
         torch.cuda.synchronize()

@@ -97,7 +97,8 @@ def select_dev(k, scores, n_blocks: int, n_sink: int, n_recent: int, budget: int
     sel = torch.full((budget,), -7, dtype=torch.int32, device=dev)
     n_sel = torch.zeros(1, dtype=torch.int32, device=dev)
     base = torch.full((budget,), -7, dtype=torch.int32, device=dev)
-    k.kvm_select(scores, n_blocks, n_sink, n_recent, budget, B, sel, n_sel, base)
+    ws = torch.empty(k.kvm_select_ws_bytes(n_blocks), dtype=torch.uint8, device=dev)
+    k.kvm_select(scores, n_blocks, n_sink, n_recent, budget, B, sel, n_sel, base, ws, ws.numel())
     return sel, n_sel, base
 
 

@@ -251,6 +251,74 @@ def test_select_error_paths(k, dev):
     with pytest.raises(k.KvmError) as e:
         gc.select_dev(k, gc.to_dev(R, dev), 1000, 60, 60, 100, dev)
     assert e.value.code == k.api._abi.KVM_ERANGE
+    # a bad score in the sink, the recent region and the last (partial) chunk
+    R = synth.scores_f32(10, 9000)
+    for pos in (0, 8999, 8192, 4096):
+        R2 = R.copy()
+        R2[pos] = np.nan
+        _, n_sel, _ = gc.select_dev(k, gc.to_dev(R2, dev), 9000, 1, 8, 100, dev)
+        assert int(n_sel.item()) == k.api._abi.KVM_ERANGE
+    # a workspace smaller than kvm_select_ws_bytes
+    import torch
+    sel = torch.empty(100, dtype=torch.int32, device=dev)
+    n_sel = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(k.kvm_select_ws_bytes(9000) - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_select(gc.to_dev(R, dev), 9000, 1, 8, 100, 32, sel, n_sel, sel, ws, ws.numel())
+    assert e.value.code == k.api._abi.KVM_ENOMEM
+
+
+@pytest.mark.parametrize("N,sink,recent,budget,kind", [
+    (5000, 50, 50, 100, "cont"),        # no free slots: sink and recent only
+    (20000, 1, 3, 5000, "const"),       # every candidate ties, across chunk boundaries
+    (8192, 0, 0, 4097, "ties"),         # chunk-aligned N
+    (8193, 2, 0, 4096, "ties"),         # one block in the last chunk
+    (12287, 0, 7, 3000, "cont"),
+])
+def test_select_chunked_cases(k, dev, N, sink, recent, budget, kind):
+    say("select chunked", N, sink, recent, budget, kind)
+    R = synth.scores_f32(N + 3 * budget, N, kind=kind, levels=3)
+    sel, n_sel, base = gc.select_dev(k, gc.to_dev(R, dev), N, sink, recent, budget, dev)
+    want = select_blocks(R, sink, recent, budget)
+    n = int(n_sel.item())
+    assert n == len(want) == budget
+    assert np.array_equal(sel.cpu().numpy()[:n], want)
+    assert np.array_equal(base.cpu().numpy()[:n], compact_positions(n))
+
+
+def test_select_signed_zero_and_subnormal(k, dev):
+    """-0.0 equals 0.0 (a tie, lower id first); positive subnormals rank above
+    zero and below every normal number."""
+    N = 10000
+    R = np.zeros(N, dtype=np.float32)
+    R[1::3] = -0.0
+    tiny = np.float32(1e-44)                       # subnormal
+    R[5::97] = tiny
+    R[7::89] = np.float32(2.0) * tiny
+    R[11::1009] = np.float32(1e-3)
+    for budget in (40, 150, 300):
+        sel, n_sel, _ = gc.select_dev(k, gc.to_dev(R, dev), N, 1, 2, budget, dev)
+        want = select_blocks(R, 1, 2, budget)
+        n = int(n_sel.item())
+        assert n == budget
+        assert np.array_equal(sel.cpu().numpy()[:n], want)
+
+
+def test_select_workspace_reuse(k, dev):
+    """Two selections in a row on one workspace: the second starts from reset
+    control words."""
+    import torch
+    N, budget = 50000, 2048
+    ws = torch.empty(k.kvm_select_ws_bytes(N), dtype=torch.uint8, device=dev)
+    sel = torch.empty(budget, dtype=torch.int32, device=dev)
+    n_sel = torch.empty(1, dtype=torch.int32, device=dev)
+    base = torch.empty(budget, dtype=torch.int32, device=dev)
+    for seed, kind, n in ((21, "ties", N), (22, "cont", N - 4096)):
+        R = synth.scores_f32(seed, n, kind=kind, levels=5)
+        k.kvm_select(gc.to_dev(R, dev), n, 1, 64, budget, 32, sel, n_sel, base, ws, ws.numel())
+        want = select_blocks(R, 1, 64, budget)
+        assert int(n_sel.item()) == budget
+        assert np.array_equal(sel.cpu().numpy()[:budget], want)
 
 
 # ------------------------------------------------------ rematerialization ----
