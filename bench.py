@@ -286,6 +286,38 @@ def fp8_leg(k, ws, wl, dev, steps: int) -> dict:
     return out
 
 
+def measured_peaks(dev) -> dict:
+    """Achievable rates on this GPU from vendor library calls, for context next to
+    the datasheet peaks: a 2 GiB device-to-device copy (read + write bytes) and a
+    large bf16 GEMM (torch.mm on the vendor BLAS), each timed with events after as
+    many untimed repetitions."""
+    import torch
+    a = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    x = torch.randn(8192, 8192, device=dev).to(torch.bfloat16).contiguous()
+    y = torch.randn(8192, 8192, device=dev).to(torch.bfloat16).contiguous()
+    z = torch.empty_like(x)
+
+    def rate(fn, reps):
+        for _ in range(reps):       # bring the clocks up first: they ramp over tens of ms
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+    t_copy = rate(lambda: b.copy_(a), 30)
+    t_mm = rate(lambda: torch.mm(x, y, out=z), 40)
+    out = {"hbm_copy_GBps": 2 * a.numel() * 4 / t_copy / 1e9,
+           "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
+           "how": "torch copy_ of 2 GiB (bytes read + written; 30 untimed, 30 timed) and "
+                  "torch.mm 8192^3 bf16 (40 untimed, 40 timed), event-timed averages"}
+    del a, b, x, y, z
+    return out
+
+
 def counter_traffic() -> dict:
     """HBM bytes per dispatch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary, per kernel; a kernel whose source file changed since the counters
@@ -653,6 +685,13 @@ def main():
     dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
     roof = roofline(*dom)
     others = [roofline(n, i) for n, i in kern.items() if n != dom[0] and roofline(n, i)]
+    peaks = measured_peaks(dev)
+    for r in [roof] + others:
+        if r is not None:
+            mp = peaks["bf16_gemm_TFLOPs"] if r["bound"] == "mfma" else peaks["hbm_copy_GBps"]
+            r["frac_of_measured"] = r["achieved"] / mp
+    log(f"measured peaks: {peaks['hbm_copy_GBps']:.0f} GB/s copy, "
+        f"{peaks['bf16_gemm_TFLOPs']:.0f} TFLOP/s bf16 GEMM")
     bst = ws.build_stats
     build_bytes = bst["blocks"] * (page + L * wl.n_kv_heads * d * 2)
     build_gbps = build_bytes / (bst["ms"] * 1e-3) / 1e9
@@ -743,6 +782,7 @@ def main():
                    "n_blocks": N, "n_q_tokens": T, "budget_blocks": wl.budget_blocks},
         "roofline": roof,
         "rooflines_other": others,
+        "peaks_measured": peaks,
         "cpu_baseline": cpu,
         "remat": {"avg_ms": remat["avg_ms"] if remat else None, "bytes": remat_bytes,
                   "GBps": remat_gbps,
