@@ -23,8 +23,8 @@ EXPORTED = [
     "kvm_select_ws_bytes", "kvm_select", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
     "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
-    "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_profile_enable",
-    "kvm_profile_read",
+    "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_quantize_e4m3",
+    "kvm_profile_enable", "kvm_profile_read",
 ]
 
 
@@ -109,6 +109,7 @@ def lib():
             "kvm_ctx_evict": (ctypes.c_int, [vp, i64, i64]),
             "kvm_tier_simulate": (ctypes.c_int, [ctypes.POINTER(TierPolicy), i32, vp, vp, vp, vp,
                                                  vp, vp, vp]),
+            "kvm_quantize_e4m3": (ctypes.c_int, [vp, i32, i64, vp, vp]),
             "kvm_profile_enable": (ctypes.c_int, [i32]),
             "kvm_profile_read": (ctypes.c_int, [ctypes.POINTER(KernelStat), i32,
                                                 ctypes.POINTER(i32)]),

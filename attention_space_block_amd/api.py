@@ -65,6 +65,11 @@ def kvm_score_blocks(dims: Dims, dtype: int, q, n_q_tokens: int, index, index_ca
     _abi.check(rc, "kvm_score_blocks")
 
 
+def kvm_quantize_e4m3(src, src_dtype: int, n: int, dst, stream=None) -> None:
+    rc = _abi.lib().kvm_quantize_e4m3(_ptr(src), src_dtype, n, _ptr(dst), _stream(stream))
+    _abi.check(rc, "kvm_quantize_e4m3")
+
+
 def kvm_select_ws_bytes(n_blocks: int) -> int:
     return int(_abi.lib().kvm_select_ws_bytes(n_blocks))
 

@@ -8,6 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["api.hip", "profile.hip", "build_index.hip", "score.hip", "select.hip", "remat.hip",
+           "quantize.hip",
            "tier.cpp"]
 LIB = os.path.join(HERE, "libkvm.so")
 

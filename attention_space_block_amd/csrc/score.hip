@@ -52,23 +52,73 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 static constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// MFMA pass 1: partial (max, sum) of exp2(x) per query row and block split.
-// Workgroup: 4 waves x 64 query rows = 256 rows of one (l, g); loops over the
-// blocks of one split in LDS tiles of 64 blocks.
-template <int D>
+// MFMA passes. Element type E: uint16_t = bf16 operands on
+// v_mfma_f32_32x32x16_bf16 (8 k-steps of 16 per 128-wide row), uint8_t = FP8
+// E4M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (2 k-steps
+// of 64). Both take A as 32 rows (lane l: row l % 32) and B as 32 columns
+// (lane l: column l % 32), the two lane halves holding disjoint k pieces of
+// the same row; both operands use the same k pieces per lane, so the product
+// is the full dot product. The 32x32 fp32 result layout is the same for both.
+// A stage holds 128 rows in LDS, stored as 16-byte pieces XOR-swizzled by row
+// so the operand reads are free of bank conflicts.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <typename E>
 struct MfmaShape {
-  static_assert(D == 128, "the MFMA score path is laid out for d = 128");
-  static constexpr int KS = D / 16;                  // MFMA k-steps
-  static constexpr int ROW_B = D * 2;                // bytes of one bf16 row: 16 pieces of 16 B
+  static constexpr int D = 128;                      // the MFMA path is laid out for d = 128
+  static constexpr bool FP8 = sizeof(E) == 1;
+  static constexpr int ROW_B = D * (int)sizeof(E);   // bytes per row: 256 or 128
+  static constexpr int PIECES = ROW_B / 16;          // 16-byte pieces per row
+  static constexpr int KS = FP8 ? D / 64 : D / 16;   // MFMA k-steps
+  static constexpr int PPK = FP8 ? 2 : 1;            // pieces per lane per k-step
   static constexpr int TILE = 128;                   // rows staged per stage
   static constexpr int SUB = TILE / 32;              // 32-row subtiles per stage
   static constexpr int TILE_B = TILE * ROW_B;        // bytes per stage buffer
   static constexpr int LOADS = TILE_B / (256 * 16);  // 16-byte copies per thread per stage
+  static constexpr int RPC = 64 / PIECES;            // rows per 1 KiB wave copy
+  using Op = typename std::conditional<FP8, i32x8, bf16x8>::type;
+  // LDS slot of piece p of stage row r (an involution in p)
+  static __device__ __forceinline__ int slot(int r, int p) {
+    return FP8 ? (p ^ ((r >> 1) & 7)) : (p ^ (r & 15));
+  }
+  // lane (half) piece j of k-step ks
+  static __device__ __forceinline__ int piece(int ks, int half, int j) {
+    return (ks * 2 + half) * PPK + j;
+  }
+  static __device__ __forceinline__ Op make_op(const uint4 (&u)[PPK]) {
+    if constexpr (FP8) {
+      i32x8 r;
+      r[0] = (int)u[0].x; r[1] = (int)u[0].y; r[2] = (int)u[0].z; r[3] = (int)u[0].w;
+      r[4] = (int)u[1].x; r[5] = (int)u[1].y; r[6] = (int)u[1].z; r[7] = (int)u[1].w;
+      return r;
+    } else {
+      return as_bf16x8(u[0]);
+    }
+  }
+  static __device__ __forceinline__ f32x16 mma(const Op& a, const Op& b, const f32x16& c) {
+    if constexpr (FP8)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // a stationary operand row from global memory: the lane's pieces of each k-step
+  static __device__ __forceinline__ void load_row(const char* row, bool ok, int half,
+                                                  Op (&op)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 u[PPK];
+#pragma unroll
+      for (int j = 0; j < PPK; ++j)
+        u[j] = ok ? *reinterpret_cast<const uint4*>(row + piece(ks, half, j) * 16)
+                  : make_uint4(0, 0, 0, 0);
+      op[ks] = make_op(u);
+    }
+  }
 };
 
 struct Pass1Args {
-  const uint16_t* q;        // [L][Hq][T][D]
-  const uint16_t* index;    // [L][Hkv][cap][D]
+  const void* q;            // [L][Hq][T][D]
+  const void* index;        // [L][Hkv][cap][D]
   int64_t cap;
   int32_t n_blocks;
   int32_t T, Hq, Hkv, G, TG;
@@ -94,24 +144,32 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
 }
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 32 rows of a staged LDS tile (A operand: lane (half, col) reads piece
-// 2*ks + half of row col at tile + aoff[ks]) times the wave's two stationary B
-// tiles, with the first level of two exp-sum trees of the previous subtile
+// 32 rows of a staged LDS tile (A operand: lane (half, col) reads its pieces
+// of row col at tile + aoff[ks][j]) times the wave's two stationary B tiles,
+// with the first level of two exp-sum trees of the previous subtile
 // (branch-free VALU work, independent of these MFMAs) woven into the MFMA
 // sequence: a wave issues those exps while its own matrix ops run instead of
-// waiting for them. Scheduling fences fix the order: each MFMA is followed by
-// its share of the 16 pairs (c, v), v < 8: t[c][v] = exp2(fma(p[c][v])) +
-// exp2(fma(p[c][v + 8])), shift sh(c, v). The operand reads run two k-steps
-// ahead; `extra` issues further LDS reads after the first k-step. `tile` is a
-// compile-time LDS address, so every read is a register plus an immediate.
-template <int KS, typename Shift, typename Extra>
+// waiting for them. Scheduling fences fix the order: each of the 2*KS MFMA
+// slots carries its share of the 16 pairs (c, v), v < 8: t[c][v] =
+// exp2(fma(p[c][v])) + exp2(fma(p[c][v + 8])), shift sh(c, v). The operand
+// reads run ahead of the MFMAs; `extra` issues further LDS reads after the
+// first k-step. `tile` is a compile-time LDS address, so every read is a
+// register plus an immediate.
+template <typename S, typename Shift, typename Extra>
 __device__ __forceinline__ void mfma_subtile_woven(f32x16 (&acc)[2], const char* tile,
-                                                   const uint32_t (&aoff)[KS],
-                                                   const bf16x8 (&bop)[2][KS],
+                                                   const uint32_t (&aoff)[S::KS][S::PPK],
+                                                   const typename S::Op (&bop)[2][S::KS],
                                                    const f32x16 (&p)[2], float scale, Shift&& sh,
                                                    float (&t)[2][8], Extra&& extra) {
-  constexpr int PPS = 8 / KS;   // pairs per MFMA slot
-  auto ld = [&](int ks) { return as_bf16x8(*reinterpret_cast<const uint4*>(tile + aoff[ks])); };
+  constexpr int KS = S::KS;
+  constexpr int PPS = 16 / (2 * KS);   // pairs per MFMA slot
+  constexpr int AHEAD = KS > 1 ? 2 : 1;
+  auto ld = [&](int ks) {
+    uint4 u[S::PPK];
+#pragma unroll
+    for (int j = 0; j < S::PPK; ++j) u[j] = *reinterpret_cast<const uint4*>(tile + aoff[ks][j]);
+    return S::make_op(u);
+  };
   auto pairs = [&](int slot) {
 #pragma unroll
     for (int q = 0; q < PPS; ++q) {
@@ -121,9 +179,9 @@ __device__ __forceinline__ void mfma_subtile_woven(f32x16 (&acc)[2], const char*
       asm volatile("" ::"v"(t[c][v]));   // keep the pair in its slot (no sinking)
     }
   };
-  bf16x8 av[KS];
-  av[0] = ld(0);
-  if (KS > 1) av[1] = ld(1);
+  typename S::Op av[KS];
+#pragma unroll
+  for (int ks = 0; ks < AHEAD; ++ks) av[ks] = ld(ks);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -131,27 +189,32 @@ __device__ __forceinline__ void mfma_subtile_woven(f32x16 (&acc)[2], const char*
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[0][ks], acc[0], 0, 0, 0);
+    acc[0] = S::mma(av[ks], bop[0][ks], acc[0]);
     __builtin_amdgcn_sched_barrier(0);
     pairs(2 * ks);
-    if (ks + 2 < KS) av[ks + 2] = ld(ks + 2);
+    if (ks + AHEAD < KS) av[ks + AHEAD] = ld(ks + AHEAD);
     if (ks == 0) extra();
     __builtin_amdgcn_sched_barrier(0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], bop[1][ks], acc[1], 0, 0, 0);
+    acc[1] = S::mma(av[ks], bop[1][ks], acc[1]);
     __builtin_amdgcn_sched_barrier(0);
     pairs(2 * ks + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // With few MFMAs per block the compiler would otherwise sink them below the
+  // caller's branches, away from the exps they are meant to run under.
+  if constexpr (S::FP8) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
 }
 
 // Per-lane byte offsets of the A-operand pieces inside a 32-row subtile:
-// lane (half, col) reads piece 2*ks + half of row col, stored XOR-swizzled at
-// piece slot (2*ks + half) ^ (col & 15).
-template <int KS, int ROW_B>
-__device__ __forceinline__ void operand_offsets(uint32_t (&aoff)[KS], int half, int col) {
+// lane (half, col) reads pieces piece(ks, half, j) of row col.
+template <typename S>
+__device__ __forceinline__ void operand_offsets(uint32_t (&aoff)[S::KS][S::PPK], int half,
+                                                int col) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    aoff[ks] = (uint32_t)(col * ROW_B + (((ks * 2 + half) ^ (col & 15)) << 4));
+  for (int ks = 0; ks < S::KS; ++ks)
+#pragma unroll
+    for (int j = 0; j < S::PPK; ++j)
+      aoff[ks][j] = (uint32_t)(col * S::ROW_B + S::slot(col, S::piece(ks, half, j)) * 16);
 }
 
 // Runs stage(it, BUF) for it in [0, n) with the stage buffer BUF = it & 1 as a
@@ -240,9 +303,10 @@ __device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nv
     }
 }
 
-template <int D>
+template <typename E>
 __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
-  using S = MfmaShape<D>;
+  using S = MfmaShape<E>;
+  constexpr int D = S::D;
   __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
   const int32_t per_lg = a.row_chunks * a.nsplit;
@@ -257,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   const int half = lane >> 5, col = lane & 31;
 
   // B operand: two 32-row tiles of this wave's query rows (stationary).
-  bf16x8 bq[2][S::KS];
+  typename S::Op bq[2][S::KS];
   const int row_base = rchunk * 256 + wave * 64;
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -265,32 +329,30 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
     const bool ok = rho < a.TG;
     const int hh = g * a.G + (ok ? rho / a.T : 0);
     const int m = ok ? rho % a.T : 0;
-    const uint16_t* qp = a.q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      bq[ct][ks] = as_bf16x8(v);
-    }
+    const char* qp = reinterpret_cast<const char*>(a.q) +
+                     (((int64_t)l * a.Hq + hh) * a.T + m) * S::ROW_B;
+    S::load_row(qp, ok, half, bq[ct]);
   }
 
   const int32_t b_begin = split * a.split_blocks;
   int32_t b_end = b_begin + a.split_blocks;
   if (b_end > a.n_blocks) b_end = a.n_blocks;
   const int32_t ntiles = b_end > b_begin ? (b_end - b_begin + S::TILE - 1) / S::TILE : 0;
-  const char* kb = reinterpret_cast<const char*>(a.index + (int64_t)L_lg * a.cap * D);
+  const char* kb = reinterpret_cast<const char*>(a.index) + (int64_t)L_lg * a.cap * S::ROW_B;
 
   float m_run[2] = {-INFINITY, -INFINITY};
   double s_run[2] = {0.0, 0.0};
 
   // Direct global->LDS stage copy. Copy i of a wave fills the 1 KiB at slot
-  // (i*4 + wave)*64: slot S (16 bytes) receives piece (S & 15) ^ (row & 15) of
-  // stage row S >> 4, so the operand reads (row r, piece c at c ^ (r & 15))
-  // hit distinct banks. A lane copies rows 16*i + dma_row of the stage, piece
-  // dma_piece: the global address is a uniform stage base plus one 32-bit lane
-  // offset. In a stage that runs past b_end the rows past it re-read the last
-  // valid row (finite values, masked to -inf later).
-  const int dma_row = 4 * wave + (lane >> 4);
-  const int dma_piece = (lane & 15) ^ (dma_row & 15);
+  // (i*4 + wave)*64: 16-byte slot s of stage row r receives piece
+  // S::slot(r, s) (the swizzle is an involution), so the operand reads hit
+  // distinct banks. A lane copies stage rows 4*RPC*i + dma_row, piece
+  // dma_piece (the swizzle does not depend on i): the global address is a
+  // uniform stage base plus one 32-bit lane offset. In a stage that runs past
+  // b_end the rows past it re-read the last valid row (finite values, masked
+  // to -inf later).
+  const int dma_row = S::RPC * wave + lane / S::PIECES;
+  const int dma_piece = S::slot(dma_row, lane % S::PIECES);
   const uint32_t dma_off = (uint32_t)(dma_row * S::ROW_B + dma_piece * 16);
   auto dma_stage = [&](int tile, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -299,17 +361,18 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
     if (t0 + S::TILE <= b_end) {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i)
-        dma16(base + i * 16 * S::ROW_B + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
+        dma16(base + i * 4096 + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
     } else {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
-        const int32_t b = t0 + 16 * i + dma_row < b_end ? t0 + 16 * i + dma_row : b_end - 1;
+        const int32_t r = t0 + 4 * S::RPC * i + dma_row;
+        const int32_t b = r < b_end ? r : b_end - 1;
         dma16(kb + (int64_t)b * S::ROW_B + dma_piece * 16, &lds[BUF][(i * 4 + wave) * 1024]);
       }
     }
   };
-  uint32_t aoff[S::KS];
-  operand_offsets<S::KS, S::ROW_B>(aoff, half, col);
+  uint32_t aoff[S::KS][S::PPK];
+  operand_offsets<S>(aoff, half, col);
 
   // Software pipeline over 32-block subtiles: while the MFMAs of subtile j
   // run, the wave takes the exps of subtile j-1 (its scores sit in the other
@@ -337,8 +400,8 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
       f32x16 (&prv)[2] = ab[(sub & 1) ^ 1];
       float t[2][8];
       const float m0 = m_run[0], m1 = m_run[1];
-      mfma_subtile_woven<S::KS>(cur, &lds[BUF][sub * 32 * S::ROW_B], aoff, bq, prv, a.scale,
-                                [&](int c, int) { return c ? m1 : m0; }, t, [] {});
+      mfma_subtile_woven<S>(cur, &lds[BUF][sub * 32 * S::ROW_B], aoff, bq, prv, a.scale,
+                            [&](int c, int) { return c ? m1 : m0; }, t, [] {});
       lse_commit2(prv, a.scale, tree8(t[0]), tree8(t[1]), m_run, s_run);
       const int32_t nvalid = b_end - (t0 + 32 * sub);
       if (nvalid < 32) mask_rows(cur, half, nvalid);   // uniform: only a split's last stage
@@ -388,8 +451,8 @@ __global__ void score_lse_combine(const float2* __restrict__ part, int32_t nlg, 
 // ---------------------------------------------------------------------------
 // MFMA pass 2: column sums of exp2(x - lse) per (l, g) over all query rows.
 struct Pass2Args {
-  const uint16_t* q;
-  const uint16_t* index;
+  const void* q;
+  const void* index;
   int64_t cap;
   int32_t n_blocks;
   int32_t T, Hq, Hkv, G, TG, TGp;
@@ -415,9 +478,9 @@ __device__ __forceinline__ float exp_sum16_rows(const f32x16& acc, const float (
   return e[0];
 }
 
-template <int D>
+template <typename E>
 __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
-  using S = MfmaShape<D>;
+  using S = MfmaShape<E>;
   __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   __shared__ __attribute__((aligned(16))) float lse_s[2][S::TILE];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
@@ -430,30 +493,25 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   const int half = lane >> 5, col = lane & 31;
 
   // B operand: this wave's two 32-block tiles (stationary).
-  bf16x8 bk[2][S::KS];
+  typename S::Op bk[2][S::KS];
   const int32_t blk_base = bchunk * 256 + wave * 64;
-  const uint16_t* kb = a.index + (int64_t)lg * a.cap * D;
+  const char* kb = reinterpret_cast<const char*>(a.index) + (int64_t)lg * a.cap * S::ROW_B;
 #pragma unroll
   for (int bt = 0; bt < 2; ++bt) {
     const int32_t b = blk_base + bt * 32 + col;
     const bool ok = b < a.n_blocks;
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      uint4 v = ok ? *reinterpret_cast<const uint4*>(kb + (int64_t)b * D + ks * 16 + half * 8)
-                   : make_uint4(0, 0, 0, 0);
-      bk[bt][ks] = as_bf16x8(v);
-    }
+    S::load_row(kb + (int64_t)(ok ? b : 0) * S::ROW_B, ok, half, bk[bt]);
   }
   const float* lse_lg = a.lse + (int64_t)lg * a.TGp;
   const int32_t ntiles = (a.TG + S::TILE - 1) / S::TILE;
   // Query rows of (l, g) are contiguous: heads g*G .. g*G+G-1, tokens 0..T-1.
-  const char* qg =
-      reinterpret_cast<const char*>(a.q + ((int64_t)l * a.Hq + (int64_t)g * a.G) * a.T * D);
+  const char* qg = reinterpret_cast<const char*>(a.q) +
+                   ((int64_t)l * a.Hq + (int64_t)g * a.G) * a.T * S::ROW_B;
   // Stage copies as in pass 1 (same slot layout), plus the stage's LSE values
   // (waves 0 and 1, 64 each; rows past TG read the +inf padding of the LSE
   // array, whose rows TG..TGp-1 exist because TGp is a multiple of 256).
-  const int dma_row = 4 * wave + (lane >> 4);
-  const int dma_piece = (lane & 15) ^ (dma_row & 15);
+  const int dma_row = S::RPC * wave + lane / S::PIECES;
+  const int dma_piece = S::slot(dma_row, lane % S::PIECES);
   const uint32_t dma_off = (uint32_t)(dma_row * S::ROW_B + dma_piece * 16);
   auto dma_stage = [&](int tile, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -462,18 +520,19 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
     if (r0 + S::TILE <= a.TG) {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i)
-        dma16(base + i * 16 * S::ROW_B + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
+        dma16(base + i * 4096 + dma_off, &lds[BUF][(i * 4 + wave) * 1024]);
     } else {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
-        const int32_t rho = r0 + 16 * i + dma_row < a.TG ? r0 + 16 * i + dma_row : a.TG - 1;
+        const int32_t r = r0 + 4 * S::RPC * i + dma_row;
+        const int32_t rho = r < a.TG ? r : a.TG - 1;   // padded rows: lse = +inf
         dma16(qg + (int64_t)rho * S::ROW_B + dma_piece * 16, &lds[BUF][(i * 4 + wave) * 1024]);
       }
     }
     if (wave < 2) dma4(lse_lg + r0 + wave * 64 + lane, &lse_s[BUF][wave * 64]);
   };
-  uint32_t aoff[S::KS];
-  operand_offsets<S::KS, S::ROW_B>(aoff, half, col);
+  uint32_t aoff[S::KS][S::PPK];
+  operand_offsets<S>(aoff, half, col);
   // LSE of the 16 rows a lane holds in a subtile: rows 8*q4 + 4*half + 0..3.
   auto load_lse = [&](float (&ls)[16], const float* sub_lse) {
 #pragma unroll
@@ -511,9 +570,9 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
       const int j = sub & 1;
       float t[2][8];
       const float (&lp)[16] = lsb[j ^ 1];
-      mfma_subtile_woven<S::KS>(ab[j], &lds[BUF][sub * 32 * S::ROW_B], aoff, bk, ab[j ^ 1],
-                                a.scale, [&](int, int v) { return lp[v]; }, t,
-                                [&] { load_lse(lsb[j], &lse_s[BUF][sub * 32]); });
+      mfma_subtile_woven<S>(ab[j], &lds[BUF][sub * 32 * S::ROW_B], aoff, bk, ab[j ^ 1], a.scale,
+                            [&](int, int v) { return lp[v]; }, t,
+                            [&] { load_lse(lsb[j], &lse_s[BUF][sub * 32]); });
       colsum[0] += (double)tree8(t[0]);
       colsum[1] += (double)tree8(t[1]);
     }
@@ -901,7 +960,8 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
   const int32_t G = d->n_q_heads / d->n_kv_heads;
   const int32_t nlg = d->n_layers * d->n_kv_heads;
   p.TG = T * G;
-  p.mfma = dtype == KVM_BF16 && p.TG >= 64 && d->head_dim == 128 && loc == KVM_INDEX_DEVICE;
+  p.mfma = (dtype == KVM_BF16 || dtype == KVM_FP8_E4M3) && p.TG >= 64 && d->head_dim == 128 &&
+           loc == KVM_INDEX_DEVICE;
   size_t off = 0;
   if (p.mfma) {
     p.row_chunks = (p.TG + 255) / 256;
@@ -998,9 +1058,10 @@ static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStrea
 extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
                                      int64_t n_blocks, int32_t index_loc, int64_t tile_blocks) {
   using namespace kvm;
-  if (check_dims(dims, dtype) || dtype == KVM_FP8_E4M3 || n_q_tokens < 1 || n_blocks < 1)
-    return 0;
-  return make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks).bytes;
+  if (check_dims(dims, dtype) || n_q_tokens < 1 || n_blocks < 1) return 0;
+  const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
+  if (dtype == KVM_FP8_E4M3 && !p.mfma) return 0;   // FP8 scores: matrix-core path only
+  return p.bytes;
 }
 
 extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q,
@@ -1011,8 +1072,6 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   clear_error();
   int rc = check_dims(dims, dtype);
   if (rc) return rc;
-  KVM_CHECK_ARG(dtype != KVM_FP8_E4M3, "the index and queries of FP8 K/V are bf16: score with "
-                "KVM_BF16");
   KVM_CHECK_ARG(q && index && scores, "null pointer");
   KVM_CHECK_ARG(n_q_tokens >= 1 && n_blocks >= 1 && n_blocks < (1LL << 30),
                 "n_q_tokens / n_blocks out of range");
@@ -1029,6 +1088,10 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
                   "tile_blocks must be a positive multiple of 512");
   }
   const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
+  if (dtype == KVM_FP8_E4M3 && !p.mfma) {
+    set_error("FP8 scores need the matrix-core path: d = 128, T*G >= 64, index in HBM");
+    return KVM_ENOTSUP;
+  }
   if (!p.mfma) {
     const size_t shm = ((size_t)TG * D + 8) * sizeof(float);
     const size_t shm2 = (size_t)nlg * TG * sizeof(float);
@@ -1049,8 +1112,8 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   const double inv_lh = 1.0 / ((double)dims->n_layers * dims->n_q_heads);
   if (p.mfma) {
     Pass1Args a1{};
-    a1.q = reinterpret_cast<const uint16_t*>(q);
-    a1.index = reinterpret_cast<const uint16_t*>(index);
+    a1.q = q;
+    a1.index = index;
     a1.cap = index_cap_blocks;
     a1.n_blocks = (int32_t)n_blocks;
     a1.T = n_q_tokens;
@@ -1068,7 +1131,10 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     const int64_t wg1 = (int64_t)nlg * p.row_chunks * p.nsplit;
     a1.total_wg = (uint32_t)((wg1 + 7) / 8 * 8);
     { KernelTimer tm("score_pass1_mfma", s);
-    score_pass1_mfma<128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1); }
+    if (dtype == KVM_FP8_E4M3)
+      score_pass1_mfma<uint8_t><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
+    else
+      score_pass1_mfma<uint16_t><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1); }
     KVM_HIP(hipGetLastError());
     const int64_t nl = (int64_t)nlg * p.TGp;
     { KernelTimer tm("score_lse_combine", s);
@@ -1094,7 +1160,10 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     const int64_t wg2 = (int64_t)nlg * p.block_chunks;
     a2.total_wg = (uint32_t)((wg2 + 7) / 8 * 8);
     { KernelTimer tm("score_pass2_mfma", s);
-    score_pass2_mfma<128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
+    if (dtype == KVM_FP8_E4M3)
+      score_pass2_mfma<uint8_t><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
+    else
+      score_pass2_mfma<uint16_t><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
     KVM_HIP(hipGetLastError());
     { KernelTimer tm("score_reduce", s);
     score_reduce<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), 0, s>>>(

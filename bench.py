@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = ("history blocks scored/s + rematerialized KV GB/s (fraction of HBM peak), 1M-tok")
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(*a):
@@ -209,6 +210,60 @@ class Workspace:
                           self.n_new, self.index, self.N)
         self.score_select()
         return self.ctx.kvm_rematerialize(self.sel, self.n_sel, self.page)
+
+
+def fp8_scores_leg(k, ws, wl, dev, steps: int, warmup: int) -> dict:
+    """FP8 scoring ablation on the same workspace: the step's queries and the
+    Mean-K index converted to E4M3 (kvm_quantize_e4m3), scored on the FP8
+    matrix-core kernels and selected with the same budget; reports the pass
+    times and how much of the bf16 selection's free part the FP8 one keeps."""
+    import torch
+    N, T = ws.N, wl.n_q_tokens
+    q8 = torch.empty(ws.q.numel(), dtype=torch.uint8, device=dev)
+    i8 = torch.empty(ws.index.numel(), dtype=torch.uint8, device=dev)
+    k.kvm_quantize_e4m3(ws.q, k.KVM_BF16, ws.q.numel(), q8)
+    k.kvm_quantize_e4m3(ws.index, k.KVM_BF16, ws.index.numel(), i8)
+    wsb = k.kvm_score_ws_bytes(ws.dims, k.KVM_FP8_E4M3, T, N, 0, 0)
+    sws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    sc = torch.empty(N, dtype=torch.float32, device=dev)
+    sel = torch.empty_like(ws.sel)
+    n_sel = torch.empty_like(ws.n_sel)
+    base = torch.empty_like(ws.base)
+
+    def once():
+        k.kvm_score_blocks(ws.dims, k.KVM_FP8_E4M3, q8, T, i8, N, N, k.KVM_INDEX_DEVICE, 0, sc,
+                           sws, wsb)
+        k.kvm_select(sc, N, wl.n_sink, wl.n_recent, wl.budget_blocks, wl.block_tokens, sel,
+                     n_sel, base, ws.sel_ws, ws.sel_ws.numel())
+    for _ in range(max(1, warmup)):
+        once()
+    torch.cuda.synchronize()
+    k.kvm_profile_enable(True)
+    for _ in range(steps):
+        once()
+    torch.cuda.synchronize()
+    prof = k.kvm_profile_read()
+    k.kvm_profile_enable(False)
+    kern = {n: c_t[1] / c_t[0] for n, c_t in prof.items()}
+    ws.score_select()                          # the bf16 selection, for comparison
+    torch.cuda.synchronize()
+    n = int(ws.n_sel.item())
+    a = set(ws.sel.cpu().numpy()[:n].tolist())
+    b = set(sel.cpu().numpy()[:int(n_sel.item())].tolist())
+    free = wl.budget_blocks - wl.n_sink - wl.n_recent
+    flops = 2.0 * wl.n_layers * wl.n_q_heads * T * N * wl.head_dim
+    p1, p2 = kern.get("score_pass1_mfma"), kern.get("score_pass2_mfma")
+    out = {"pass1_ms": p1, "pass2_ms": p2,
+           "score_ms": sum(v for n_, v in kern.items() if n_.startswith("score")),
+           "pass1_TFLOPs": flops / (p1 * 1e-3) / 1e12 if p1 else None,
+           "fp8_peak_TFLOPs": MFMA_FP8_PEAK_TFLOPS,
+           "selection_kept_of_bf16_free": (len(a & b) - (n - free)) / free,
+           "note": "E4M3 queries and Mean-K (round to nearest even, saturating); "
+                   "fp32 accumulation, softmax as in bf16"}
+    del q8, i8, sws
+    log(f"fp8 scores: pass 1 {p1:.2f} ms, pass 2 {p2:.2f} ms, keeps "
+        f"{100 * out['selection_kept_of_bf16_free']:.1f}% of the bf16 free selection")
+    return out
 
 
 def fp8_leg(k, ws, wl, dev, steps: int) -> dict:
@@ -748,6 +803,7 @@ def main():
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
     fp8 = fp8_leg(k, ws, wl, dev, args.steps) if args.fp8 else None
+    fp8s = fp8_scores_leg(k, ws, wl, dev, args.steps, args.warmup) if args.fp8 else None
     # PCIe leg: misses from pinned host memory
     pcie = None
     if args.pcie_steps > 0:
@@ -796,6 +852,7 @@ def main():
                        "hbm_frac": rope_gbps / HBM_PEAK_GBPS},
         "delta_rerope": delta,
         "fp8_pages": fp8,
+        "fp8_scores": fp8s,
         "pcie_leg": pcie,
         "kernels": kern,
     }

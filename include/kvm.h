@@ -104,6 +104,11 @@ int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
  * and g(h) = h / (Hq/Hkv). sum_b R_b = n_q_tokens.
  *
  * q       device, pre-RoPE queries [L][Hq][n_q_tokens][d] in `dtype`.
+ *         dtype KVM_FP8_E4M3 scores E4M3 queries against an E4M3 index (the
+ *         FP8 scoring ablation; both from kvm_quantize_e4m3): the products are
+ *         exact and the sums and softmax run in fp32/fp64 as for bf16. Only
+ *         the matrix-core form exists for it: d = 128, T*G >= 64 and a
+ *         device index, else KVM_ENOTSUP (and kvm_score_ws_bytes returns 0).
  * index   KVM_INDEX_DEVICE: device [L][Hkv][index_cap_blocks][d];
  *         KVM_INDEX_HOST_TILED: pinned host, tile-major, tile_blocks a
  *         positive multiple of 512: tile t (blocks
@@ -124,6 +129,16 @@ int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q, int32_t
                      const void* index, int64_t index_cap_blocks, int64_t n_blocks,
                      int32_t index_loc, int64_t tile_blocks, float* scores, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* FP8 E4M3 (OCP E4M3FN) conversion for the FP8 scoring ablation (the pages'
+ * engine runs an FP8 KV cache, KVMem Sec. 6.1): dst[i] = the E4M3 byte nearest
+ * to src[i], ties to even, saturating at +-448 (infinities too), the sign kept
+ * on zero; NaN inputs give an unspecified byte.
+ * src       device, n values of src_dtype (KVM_F32 or KVM_BF16).
+ * dst       device, n bytes, 4-byte aligned; caller-owned.
+ * Errors: KVM_EINVAL (null pointer, dtype, n < 1, alignment). */
+int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, void* dst, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Default selector and compact positions, KVMem Sec. 4.3 (sink and recent

@@ -9,7 +9,7 @@ import pytest
 
 import synth
 from oracle import select_blocks, compact_positions
-from oracle.numerics import bf16_bits
+from oracle.numerics import bf16_bits, fp8_decode, fp8_encode
 from oracle import pipeline as op
 from tests import gpu_common as gc
 
@@ -148,6 +148,91 @@ def test_scores_match_oracle(k, dev, name, N, scale):
     assert abs(got.sum() - wl.n_q_tokens) <= 1e-5 * wl.n_q_tokens
     rel = np.abs(got - ref) / ref
     assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
+
+
+def _e4m3_probe_values(n: int, seed: int) -> np.ndarray:
+    """fp32 inputs for the E4M3 conversion: normals over many binades, every
+    E4M3 value and every midpoint between neighbours (the ties), values past the
+    saturation point, signed zeros, values below half the smallest subnormal,
+    and infinities."""
+    rng = np.random.default_rng(seed)
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = fp8_decode(codes)
+    mids = (vals[1:] + vals[:-1]) / 2
+    special = np.r_[vals, -vals, mids, -mids, 448.0, 449.0, 464.0, 480.0, 1e6, -1e6, 0.0, -0.0,
+                    2.0 ** -11, -(2.0 ** -11), np.inf, -np.inf]
+    rand = rng.standard_normal(n) * np.exp2(rng.integers(-12, 10, n))
+    return np.r_[special, rand].astype(np.float32)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_quantize_e4m3_bit_exact(k, dev, src):
+    """kvm_quantize_e4m3 equals the oracle's E4M3 encoder byte for byte
+    (nearest, ties to even, saturating), for a length with a ragged tail."""
+    import torch
+    x = _e4m3_probe_values(3001, 5)
+    if src == "bf16":
+        bits = synth.f32_to_bf16_bits(x)
+        xin, want = gc.to_dev(bits, dev), fp8_encode(op.as_f64(bits, "bf16"))
+        code = k.KVM_BF16
+    else:
+        xin, want = gc.to_dev(x, dev), fp8_encode(x.astype(np.float64))
+        code = k.KVM_F32
+    n = x.size
+    out = torch.full((n + 5,), 0x5A, dtype=torch.uint8, device=dev)
+    k.kvm_quantize_e4m3(xin, code, n, out)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:n], want), np.flatnonzero(got[:n] != want)[:10]
+    assert np.all(got[n:] == 0x5A)                 # nothing written past n
+
+
+@pytest.mark.parametrize("N,scale", [
+    (2048, {}),                                     # full ctx64k shape
+    (1000, {"n_layers": 2, "n_q_tokens": 77}),      # ragged rows (TG 462) and blocks
+])
+def test_fp8_scores_match_oracle(k, dev, N, scale):
+    """FP8 scoring ablation: E4M3 queries and Mean-K (encoded by the oracle) on
+    the FP8 matrix-core kernels, against the float64 Eq. (10) of the decoded
+    values."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(**scale) if scale else synth.get_workload("ctx64k")
+    say("fp8 scores", N, scale)
+    index = op.index_rows(wl, 0, N)
+    q = op.query_stored(wl, 0, index)
+    qb = fp8_encode(op.as_f64(q, "bf16"))
+    ib = fp8_encode(index)
+    ref = op.block_scores(fp8_decode(qb), fp8_decode(ib))
+    dims = k.dims_for(wl)
+    T = wl.n_q_tokens
+    ws_b = k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, T, N, 0, 0)
+    assert ws_b > 0
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    scores = torch.empty(N, dtype=torch.float32, device=dev)
+    k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, torch.from_numpy(qb).to(dev), T,
+                       torch.from_numpy(np.ascontiguousarray(ib)).to(dev), N, N, 0, 0, scores,
+                       ws, ws_b)
+    got = scores.cpu().numpy().astype(np.float64)
+    assert abs(got.sum() - T) <= 1e-5 * T
+    rel = np.abs(got - ref) / ref
+    assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
+
+
+def test_fp8_scores_unsupported_forms(k, dev):
+    """FP8 scores exist only on the matrix-core path."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=1, n_q_tokens=5)   # T*G = 30 < 64
+    dims = k.dims_for(wl)
+    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 5, 256, 0, 0) == 0
+    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 64, 1024, k.KVM_INDEX_HOST_TILED, 512) == 0
+    q = torch.zeros(wl.n_layers * wl.n_q_heads * 5 * wl.head_dim, dtype=torch.uint8, device=dev)
+    idx = torch.zeros(wl.n_layers * wl.n_kv_heads * 256 * wl.head_dim, dtype=torch.uint8,
+                      device=dev)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    scores = torch.empty(256, dtype=torch.float32, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, q, 5, idx, 256, 256, 0, 0, scores, ws,
+                           ws.numel())
+    assert e.value.code == k.api._abi.KVM_ENOTSUP
 
 
 def test_scores_steep_ramp_match_oracle(k, dev):
