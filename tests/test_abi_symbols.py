@@ -59,3 +59,15 @@ def test_validation_errors_need_no_gpu():
         assert e.code == -4
     else:
         raise AssertionError("expected KVM_ERANGE")
+    for args in ((16, 7, 100, 16), (16, k.KVM_BF16, 0, 16), (16, k.KVM_BF16, 100, 18),
+                 (0, k.KVM_F32, 100, 16)):
+        try:                                          # dtype, n, dst alignment, null src
+            k.kvm_quantize_e4m3(*args, stream=0)
+        except k.KvmError as e:
+            assert e.code == -1
+        else:
+            raise AssertionError(f"expected KVM_EINVAL for {args}")
+    # FP8 scores exist only on the matrix-core form (T*G >= 64, d = 128, device index)
+    d = k.Dims(1, 2, 12, 128, 32)
+    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 1, 256) == 0
+    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 16, 256) > 0
