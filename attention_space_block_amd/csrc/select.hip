@@ -9,16 +9,19 @@
 // bits, 8 bits per round, spread over many workgroups (a 10M-token workspace
 // has 312,500 blocks; one workgroup spends most of its time in LDS atomics on
 // the few histogram bins that hold almost every key):
-//  1. sel_init resets the control words (digit prefix, keys still to take).
-//  2. Four rounds of sel_hist (each workgroup: LDS histogram of the current
-//     digit over its chunk of candidates that match the fixed digits, with
-//     per-thread run-length counting and one wave-aggregated add for the most
-//     common pending digit) and sel_digit (one workgroup: sum the chunk
-//     histograms, pick the digit holding the krem-th largest key, fix it).
-//     Afterwards T is the key of the k-th largest candidate and krem the
-//     number of candidates equal to T that are taken (the lowest ids).
-//  3. sel_count validates every score (finite, >= 0) and counts per chunk the
-//     kept blocks (sink, recent, keys > T) and the ties (keys == T).
+//  1. sel_init resets the control words and the four round histograms.
+//  2. Four rounds of sel_hist: each workgroup first fixes the digits of the
+//     earlier rounds from their 256-bin histograms (a workgroup scan per
+//     round: the digit holding the krem-th largest key), then builds the
+//     LDS histogram of the current digit over its chunk of candidates that
+//     match them (per-thread run-length counting and one wave-aggregated add
+//     for the most common pending digit) and adds it to the round's global
+//     histogram. After four rounds T is the key of the k-th largest candidate
+//     and krem the number of candidates equal to T that are taken (the
+//     lowest ids).
+//  3. sel_count fixes the last digit the same way, validates every score
+//     (finite, >= 0) and counts per chunk the kept blocks (sink, recent,
+//     keys > T) and the ties (keys == T).
 //  4. sel_write: each chunk's output offset is (kept before it) + min(ties
 //     before it, krem); inside the chunk every thread owns 16 consecutive
 //     blocks and two workgroup scans give its tie rank and its offset, so the
@@ -36,12 +39,13 @@ constexpr int SEL_PER = 16;                          // blocks per thread
 constexpr int SEL_CHUNK = SEL_THREADS * SEL_PER;     // blocks per workgroup
 constexpr int CTL_WORDS = 64;                        // control area (words)
 enum { CTL_BAD = 0, CTL_PREFIX = 1, CTL_KREM = 2 };
+constexpr int HIST_WORDS = 4 * 256;                  // one 256-bin histogram per round
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 struct SelWs {
   uint32_t* ctl;    // [CTL_WORDS]
-  uint32_t* hist;   // [nwg][256]
+  uint32_t* hist;   // [4][256]: digit histogram of each round
   uint32_t* cnt;    // [nwg][2]: kept, ties
 };
 
@@ -49,17 +53,15 @@ int64_t sel_nwg(int64_t n) { return (n + SEL_CHUNK - 1) / SEL_CHUNK; }
 
 size_t sel_ws_bytes(int64_t n) {
   const int64_t nwg = sel_nwg(n);
-  return align256(CTL_WORDS * 4) + align256((size_t)nwg * 256 * 4) + align256((size_t)nwg * 8);
+  return align256(CTL_WORDS * 4) + align256(HIST_WORDS * 4) + align256((size_t)nwg * 8);
 }
 
-SelWs sel_ws(void* ws, int64_t n) {
+SelWs sel_ws(void* ws) {
   char* p = reinterpret_cast<char*>(ws);
-  const int64_t nwg = sel_nwg(n);
   SelWs w;
   w.ctl = reinterpret_cast<uint32_t*>(p);
   w.hist = reinterpret_cast<uint32_t*>(p + align256(CTL_WORDS * 4));
-  w.cnt = reinterpret_cast<uint32_t*>(p + align256(CTL_WORDS * 4) +
-                                      align256((size_t)nwg * 256 * 4));
+  w.cnt = reinterpret_cast<uint32_t*>(p + align256(CTL_WORDS * 4) + align256(HIST_WORDS * 4));
   return w;
 }
 
@@ -111,24 +113,56 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot, uint32_
   return res;
 }
 
-__global__ void sel_init(uint32_t* ctl, uint32_t k) {
-  if (threadIdx.x == 0) {
-    ctl[CTL_BAD] = 0u;
-    ctl[CTL_PREFIX] = 0u;
-    ctl[CTL_KREM] = k;
+__global__ __launch_bounds__(256) void sel_init(uint32_t* ctl, uint32_t* hist) {
+  for (int i = threadIdx.x; i < HIST_WORDS; i += 256) hist[i] = 0u;
+  if (threadIdx.x == 0) ctl[CTL_BAD] = 0u;
+}
+
+// The digits of rounds [0, rounds) from their histograms: in round r the digit
+// dg at shift 24 - 8r is the largest whose keys, with all larger digits, reach
+// krem; krem becomes the rank of the target inside digit dg. Every thread of a
+// 256-thread workgroup gets the result (one bin per thread, descending scan).
+__device__ void fix_digits(const uint32_t* __restrict__ hist, int rounds, uint32_t k,
+                           uint32_t* wave_tot, uint32_t* s_fix, uint32_t& prefix,
+                           uint32_t& krem) {
+  const int t = threadIdx.x;
+  prefix = 0u;
+  krem = k;
+  for (int r = 0; r < rounds; ++r) {
+    const int shift = 24 - 8 * r;
+    const uint32_t v = hist[r * 256 + (255 - t)];   // thread t holds digit 255 - t
+    uint32_t total;
+    const uint32_t ex = block_exclusive_scan<256>(v, wave_tot, &total);   // keys above it
+    if (t == 0) {
+      s_fix[0] = 0u;
+      s_fix[1] = 0u;
+    }
+    __syncthreads();
+    if (ex < krem && krem <= ex + v) {              // exactly one thread for consistent counts
+      s_fix[0] = (uint32_t)(255 - t);
+      s_fix[1] = ex;
+    }
+    __syncthreads();
+    prefix |= s_fix[0] << shift;
+    krem -= s_fix[1];
+    __syncthreads();
   }
 }
 
-// Histogram of digit (key >> shift) & 255 over this chunk's candidates whose
-// digits above `shift` equal those already fixed in ctl[CTL_PREFIX].
+// Round `round`: histogram of digit (key >> shift) & 255, shift = 24 - 8*round,
+// over this chunk's candidates whose higher digits equal the ones fixed by the
+// earlier rounds, added to hist[round].
 __global__ __launch_bounds__(SEL_THREADS) void sel_hist(const float* __restrict__ scores,
-                                                        int64_t c0, int64_t c1, int shift,
-                                                        const uint32_t* __restrict__ ctl,
-                                                        uint32_t* __restrict__ hist) {
+                                                        int64_t c0, int64_t c1, int round,
+                                                        uint32_t k, uint32_t* __restrict__ hist) {
   __shared__ uint32_t h[256];
+  __shared__ uint32_t wave_tot[40], s_fix[2];
   const int t = threadIdx.x, lane = t & 63;
+  const int shift = 24 - 8 * round;
+  uint32_t prefix, krem;
+  fix_digits(hist, round, k, wave_tot, s_fix, prefix, krem);
   h[t] = 0u;
-  const uint32_t hi = shift < 24 ? ctl[CTL_PREFIX] >> (shift + 8) : 0u;
+  const uint32_t hi = shift < 24 ? prefix >> (shift + 8) : 0u;
   const int64_t base = (int64_t)blockIdx.x * SEL_CHUNK;
   uint32_t key[SEL_PER];
   bool in[SEL_PER];
@@ -163,41 +197,26 @@ __global__ __launch_bounds__(SEL_THREADS) void sel_hist(const float* __restrict_
   }
   if (act) atomicAdd(&h[cur], cnt);
   __syncthreads();
-  hist[(int64_t)blockIdx.x * 256 + t] = h[t];
-}
-
-// Fix the digit at `shift`: the largest digit dg whose keys, with all larger
-// digits, reach krem; krem becomes the rank of the target inside digit dg.
-__global__ __launch_bounds__(256) void sel_digit(const uint32_t* __restrict__ hist, int64_t nwg,
-                                                 int shift, uint32_t* __restrict__ ctl) {
-  __shared__ uint32_t wave_tot[40];
-  const int t = threadIdx.x;
-  const uint32_t krem = ctl[CTL_KREM], prefix = ctl[CTL_PREFIX];
-  uint32_t s = 0u;
-  for (int64_t w = 0; w < nwg; ++w) s += hist[w * 256 + t];
-  // above(t) = sum of digits > t: an exclusive scan in descending digit order.
-  const int r = 255 - t;
-  __shared__ uint32_t rev[256];
-  rev[r] = s;
-  __syncthreads();
-  const uint32_t v = rev[t];   // digit 255 - t
-  uint32_t total;
-  const uint32_t ex = block_exclusive_scan<256>(v, wave_tot, &total);
-  // thread t holds digit dg = 255 - t with above = ex
-  if (ex < krem && krem <= ex + v) {
-    ctl[CTL_PREFIX] = prefix | ((uint32_t)(255 - t) << shift);
-    ctl[CTL_KREM] = krem - ex;
-  }
+  if (h[t] != 0u) atomicAdd(&hist[round * 256 + t], h[t]);
 }
 
 // Per chunk: validation of every score, kept blocks and ties.
 __global__ __launch_bounds__(SEL_THREADS) void sel_count(const float* __restrict__ scores,
                                                          int64_t N, int64_t c0, int64_t c1,
-                                                         int has_k, uint32_t* __restrict__ ctl,
+                                                         uint32_t k,
+                                                         const uint32_t* __restrict__ hist,
+                                                         uint32_t* __restrict__ ctl,
                                                          uint32_t* __restrict__ cnt) {
   __shared__ uint32_t red[2][SEL_THREADS / 64];
+  __shared__ uint32_t wave_tot[40], s_fix[2];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t T = has_k ? ctl[CTL_PREFIX] : 0xffffffffu;
+  const bool has_k = k > 0;
+  uint32_t T = 0xffffffffu, krem = 0u;
+  if (has_k) fix_digits(hist, 4, k, wave_tot, s_fix, T, krem);   // uniform branch
+  if (blockIdx.x == 0 && t == 0) {             // for sel_write
+    ctl[CTL_PREFIX] = T;
+    ctl[CTL_KREM] = krem;
+  }
   const int64_t base = (int64_t)blockIdx.x * SEL_CHUNK;
   uint32_t kept = 0u, tie = 0u;
   bool bad = false;
@@ -361,20 +380,18 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     return KVM_ENOMEM;
   }
   KVM_CHECK_ARG((uintptr_t)ws % 256 == 0, "ws must be 256-byte aligned");
-  const SelWs w = sel_ws(ws, n_blocks);
+  const SelWs w = sel_ws(ws);
   const int64_t nwg = sel_nwg(n_blocks);
   const int64_t c0 = n_sink, c1 = n_blocks - n_recent;
   const uint32_t k = (uint32_t)(budget_blocks - n_sink - n_recent);
-  sel_init<<<1, 64, 0, s>>>(w.ctl, k);
+  sel_init<<<1, 256, 0, s>>>(w.ctl, w.hist);
   if (k > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      sel_hist<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, c0, c1, shift, w.ctl,
+    for (int round = 0; round < 4; ++round)
+      sel_hist<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, c0, c1, round, k,
                                                                  w.hist);
-      sel_digit<<<1, 256, 0, s>>>(w.hist, nwg, shift, w.ctl);
-    }
   }
-  sel_count<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, n_blocks, c0, c1, k > 0,
-                                                              w.ctl, w.cnt);
+  sel_count<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, n_blocks, c0, c1, k,
+                                                              w.hist, w.ctl, w.cnt);
   sel_write<<<dim3((uint32_t)nwg), dim3(SEL_THREADS), 0, s>>>(scores, n_blocks, c0, c1, k > 0,
                                                               w.ctl, w.cnt, block_tokens,
                                                               budget_blocks, sel, n_sel, base_pos);
