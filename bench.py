@@ -730,7 +730,8 @@ def main():
             ach = flops_pass / (info["avg_ms"] * 1e-3) / 1e12
             return {"kernel": name, "bound": "mfma", "achieved": ach,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic_for(traffic, name)}
+                    "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                    "traffic": traffic_for(traffic, name, "<unsigned short>")}
         if name == "remat":
             return {"kernel": name, "bound": "hbm", "achieved": remat_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS,
