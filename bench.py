@@ -735,7 +735,7 @@ def main():
         if name == "remat":
             return {"kernel": name, "bound": "hbm", "achieved": remat_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS,
-                    "traffic": traffic_for(traffic, "remat_kernel", "false>")}
+                    "traffic": traffic_for(traffic, "remat_kernel", "<unsigned short, 128, 0, false>")}
         return None
 
     dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
@@ -800,7 +800,7 @@ def main():
         delta = {"avg_ms": d_ms, "deltas_per_call": dst["deltas"], "bytes": d_bytes,
                  "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
                  "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                 "traffic": traffic_for(counter_traffic(), "remat_kernel", "true>")}
+                 "traffic": traffic_for(counter_traffic(), "remat_kernel", "<unsigned short, 128, 0, true>")}
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
     fp8 = fp8_leg(k, ws, wl, dev, args.steps) if args.fp8 else None
