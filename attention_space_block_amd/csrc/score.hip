@@ -589,14 +589,25 @@ __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
   }
 }
 
-// R[b] = (sum over (l, g) of rp[lg][b], fixed order, fp64) / (L*Hq).
-__global__ void score_reduce(const float* __restrict__ rp, int32_t nlg, int32_t n_blocks,
-                             double inv_lh, float* __restrict__ scores) {
-  const int32_t b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= n_blocks) return;
+// R[b] = (sum over (l, g) of rp[lg][b], fp64) / (L*Hq). A workgroup takes 64
+// blocks; its four waves sum the (l, g) rows lg = w, w + 4, ... of them and the
+// four partial sums are added in wave order, so the result is deterministic.
+__global__ __launch_bounds__(256) void score_reduce(const float* __restrict__ rp, int32_t nlg,
+                                                   int32_t n_blocks, double inv_lh,
+                                                   float* __restrict__ scores) {
+  __shared__ double part[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int32_t b = blockIdx.x * 64 + lane;
   double s = 0.0;
-  for (int32_t lg = 0; lg < nlg; ++lg) s += (double)rp[(int64_t)lg * n_blocks + b];
-  scores[b] = (float)(s * inv_lh);
+  if (b < n_blocks) {
+#pragma unroll 8
+    for (int32_t lg = w; lg < nlg; lg += 4) s += (double)rp[(int64_t)lg * n_blocks + b];
+  }
+  part[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && b < n_blocks)
+    scores[b] = (float)((((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) *
+                        inv_lh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1166,7 +1177,7 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
       score_pass2_mfma<uint16_t><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
     KVM_HIP(hipGetLastError());
     { KernelTimer tm("score_reduce", s);
-    score_reduce<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), 0, s>>>(
+    score_reduce<<<dim3((uint32_t)((n_blocks + 63) / 64)), dim3(256), 0, s>>>(
         a2.rp, nlg, (int32_t)n_blocks, inv_lh, scores); }
     KVM_HIP(hipGetLastError());
     return KVM_OK;
