@@ -94,6 +94,43 @@ def test_ws1m_full_step(k, dev):
     pool.ctx.close()
 
 
+@pytest.mark.timeout(600)
+def test_ws10m_scores_resident_match_oracle(k, dev):
+    """The 10M-token workspace (312,500 blocks, index in HBM, one query token):
+    all scores against the oracle's stored values, and the selection. The index
+    is drawn tile by tile into pageable memory, so no large pinned buffer is
+    involved (the host-tiled form is the next test)."""
+    import torch
+    g = golden("ws10m")
+    wl = synth.get_workload("ws10m")
+    N, tb, d = wl.n_blocks, wl.tile_blocks, wl.head_dim
+    nlg = wl.n_layers * wl.n_kv_heads
+    say("ws10m: drawing the 41 GB index into HBM")
+    index = torch.empty((wl.n_layers, wl.n_kv_heads, N, d), dtype=torch.int16, device=dev)
+    iv = index.view(nlg, N, d)
+    buf = np.empty((nlg, tb, d), dtype=np.uint16)
+    for t in range((N + tb - 1) // tb):
+        nb = min(tb, N - t * tb)
+        synth.index_direct(wl, t * tb, nb, out=buf, lg_stride_elems=tb * d)
+        iv[:, t * tb:t * tb + nb, :].copy_(torch.from_numpy(buf[:, :nb, :].view(np.int16)))
+    q = gc.to_dev(synth.query(wl), dev)
+    say("ws10m: scoring")
+    res = gc.score_dev(k, wl, q, index, N, N, dev).cpu().numpy()
+    del index, iv
+    rel = np.abs(res.astype(np.float64) - g["R"]) / g["R"]
+    say("max rel err", rel.max(), "margin", float(g["margin"]))
+    assert rel.max() <= 1e-5
+    assert abs(res.astype(np.float64).sum() - wl.n_q_tokens) <= 1e-5 * wl.n_q_tokens
+    sel, n_sel, base = gc.select_dev(k, torch.from_numpy(res).to(dev), N, wl.n_sink,
+                                     wl.n_recent, wl.budget_blocks, dev)
+    n = int(n_sel.item())
+    assert n == wl.budget_blocks
+    s = sel.cpu().numpy()[:n]
+    if float(g["margin"]) > 2e-5:
+        assert np.array_equal(s, g["sel"])
+    gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
+
+
 @pytest.mark.skip(reason="with this test earlier in the same process, the next kvm_ctx_create "
                          "ended in a host segmentation fault (after 41 GB of pinned host "
                          "memory for the tiled index); the cause is not found, so the test "
