@@ -733,9 +733,48 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int D>
+// Operand traits of the stored pass 1: bf16 on v_mfma_f32_16x16x32_bf16 (k-steps
+// of 32; lane l holds elements 32*ks + 8*(l/16) .. +8 of its row), FP8 E4M3 on
+// v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (d = 128 in one step; lane
+// l holds bytes 32*(l/16) .. +32 of its row). Both operands use the same k
+// assignment, so the product is the full dot product; the 16x16 fp32 result
+// layout is the same for both.
+template <typename E, int D>
+struct StoredOps {
+  static constexpr int KS = D / 32;
+  using Op = bf16x8_t;
+  static __device__ __forceinline__ Op load(const char* row, int kg, int ks) {
+    return __builtin_bit_cast(bf16x8_t,
+                              *reinterpret_cast<const uint4*>(row + (32 * ks + 8 * kg) * 2));
+  }
+  static __device__ __forceinline__ Op zero() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+  static __device__ __forceinline__ f32x4_t mma(const Op& a, const Op& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct StoredOps<uint8_t, 128> {
+  static constexpr int KS = 1;
+  using Op = i32x8;
+  static __device__ __forceinline__ Op load(const char* row, int kg, int) {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(row + 32 * kg);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(row + 32 * kg + 16);
+    i32x8 r;
+    r[0] = (int)u0.x; r[1] = (int)u0.y; r[2] = (int)u0.z; r[3] = (int)u0.w;
+    r[4] = (int)u1.x; r[5] = (int)u1.y; r[6] = (int)u1.z; r[7] = (int)u1.w;
+    return r;
+  }
+  static __device__ __forceinline__ Op zero() { return i32x8{0, 0, 0, 0, 0, 0, 0, 0}; }
+  static __device__ __forceinline__ f32x4_t mma(const Op& a, const Op& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+template <typename E, int D>
 __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
-  constexpr int KS = D / 32;                   // 32-wide k-steps
+  using O = StoredOps<E, D>;
+  constexpr int KS = O::KS;
+  constexpr int ROW_B = D * (int)sizeof(E);
   constexpr int TU = 4;                        // 16-row tiles in flight per wave
   constexpr int MAXCT = 4;                     // TG < 64: at most 4 column tiles
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -748,22 +787,19 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   const int l = lg / a.Hkv, g = lg % a.Hkv;
   const int r16 = lane & 15, kg = lane >> 4;
   const int nct = (a.TG + 15) / 16;
-  // B: query row rho = 16*ct + r16, elements 32*ks + 8*kg .. +8
-  bf16x8_t bq[MAXCT][KS];
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  // B: query row rho = 16*ct + r16, the lane's k pieces
+  typename O::Op bq[MAXCT][KS];
+  const char* q = reinterpret_cast<const char*>(a.q);
 #pragma unroll
   for (int ct = 0; ct < MAXCT; ++ct) {
     const int rho = 16 * ct + r16;
     const bool ok = rho < a.TG;
     const int hh = g * a.G + (ok ? rho / a.T : 0), m = ok ? rho % a.T : 0;
-    const uint16_t* qp = q + (((int64_t)l * a.Hq + hh) * a.T + m) * D + 8 * kg;
+    const char* qp = q + (((int64_t)l * a.Hq + hh) * a.T + m) * ROW_B;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
-      bq[ct][ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int ks = 0; ks < KS; ++ks) bq[ct][ks] = ok ? O::load(qp, kg, ks) : O::zero();
   }
-  const uint16_t* base = reinterpret_cast<const uint16_t*>(a.index) + (int64_t)lg * a.lg_stride;
+  const char* base = reinterpret_cast<const char*>(a.index) + (int64_t)lg * a.lg_stride * sizeof(E);
   float* Sl = a.S + ((int64_t)lg * a.n_blocks + a.b_first) * a.TG;
   // online (shift, sum-exp) of the lane's query rows over its scores
   float m_run[MAXCT], s_run[MAXCT];
@@ -773,15 +809,14 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
     s_run[ct] = 0.0f;
   }
   for (int32_t r0 = r_begin + wave * 16 * TU; r0 < r_end; r0 += 4 * 16 * TU) {
-    bf16x8_t av[TU][KS];
+    typename O::Op av[TU][KS];
 #pragma unroll
     for (int t = 0; t < TU; ++t) {
       int32_t row = r0 + 16 * t + r16;
       row = row < r_end ? row : r_end - 1;     // rows past the end re-read the last one
-      const uint16_t* rp = base + (int64_t)row * D + 8 * kg;
+      const char* rp = base + (int64_t)row * ROW_B;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        av[t][ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(rp + 32 * ks));
+      for (int ks = 0; ks < KS; ++ks) av[t][ks] = O::load(rp, kg, ks);
     }
 #pragma unroll
     for (int t = 0; t < TU; ++t) {
@@ -793,7 +828,7 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t][ks], bq[ct][ks], acc, 0, 0, 0);
+          acc = O::mma(av[t][ks], bq[ct][ks], acc);
         const int rho = 16 * ct + r16;
         if (rho < a.TG) {
 #pragma unroll
@@ -960,10 +995,18 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // blocks per (max, sum-exp) partial of the stored-score path
 static constexpr int32_t STATS_CHUNK = 2048;
 
-// The bf16 stored-score pass 1 runs on the matrix cores for up to 64 query
-// rows (4 column tiles); wider fp32 or bf16 cases take the VALU kernel and the
-// separate stats pass.
-static bool stored_on_mfma(int32_t dtype, int32_t TG) { return dtype == KVM_BF16 && TG <= 64; }
+// The bf16 and FP8 stored-score pass 1 runs on the matrix cores for up to 64
+// query rows (4 column tiles); wider cases and fp32 take the VALU kernel and
+// the separate stats pass.
+static bool stored_on_mfma(int32_t dtype, int32_t TG) {
+  return (dtype == KVM_BF16 || dtype == KVM_FP8_E4M3) && TG <= 64;
+}
+
+// FP8 scores run only on the matrix cores with d = 128: the two-pass kernels
+// (T*G >= 64, index in HBM) or the stored pass 1 (T*G <= 64, either location).
+static bool fp8_supported(const Plan& p, int32_t D) {
+  return p.mfma || (p.TG <= 64 && D == 128);
+}
 
 static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, int32_t loc,
                       int64_t tile_blocks) {
@@ -1053,8 +1096,9 @@ static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStrea
     const int32_t chunks_here = (a.nb + a.chunk - 1) / a.chunk;
     const dim3 grid((uint32_t)((int64_t)a.nlg * chunks_here));
     KernelTimer tm("score_stored_pass1", s);
-    if (D == 128) score_stored_pass1_mfma<128><<<grid, dim3(256), 0, s>>>(a);
-    else score_stored_pass1_mfma<64><<<grid, dim3(256), 0, s>>>(a);
+    if (dtype == KVM_FP8_E4M3) score_stored_pass1_mfma<uint8_t, 128><<<grid, dim3(256), 0, s>>>(a);
+    else if (D == 128) score_stored_pass1_mfma<uint16_t, 128><<<grid, dim3(256), 0, s>>>(a);
+    else score_stored_pass1_mfma<uint16_t, 64><<<grid, dim3(256), 0, s>>>(a);
   } else if (dtype == KVM_BF16) {
     if (D == 128) launch_stored_pass1<uint16_t, 128>(a, s);
     else launch_stored_pass1<uint16_t, 64>(a, s);
@@ -1071,7 +1115,7 @@ extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_
   using namespace kvm;
   if (check_dims(dims, dtype) || n_q_tokens < 1 || n_blocks < 1) return 0;
   const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
-  if (dtype == KVM_FP8_E4M3 && !p.mfma) return 0;   // FP8 scores: matrix-core path only
+  if (dtype == KVM_FP8_E4M3 && !fp8_supported(p, dims->head_dim)) return 0;
   return p.bytes;
 }
 
@@ -1099,8 +1143,8 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
                   "tile_blocks must be a positive multiple of 512");
   }
   const Plan p = make_plan(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
-  if (dtype == KVM_FP8_E4M3 && !p.mfma) {
-    set_error("FP8 scores need the matrix-core path: d = 128, T*G >= 64, index in HBM");
+  if (dtype == KVM_FP8_E4M3 && !fp8_supported(p, D)) {
+    set_error("FP8 scores need d = 128 and either T*G <= 64 or an index in HBM");
     return KVM_ENOTSUP;
   }
   if (!p.mfma) {

@@ -67,7 +67,11 @@ def test_validation_errors_need_no_gpu():
             assert e.code == -1
         else:
             raise AssertionError(f"expected KVM_EINVAL for {args}")
-    # FP8 scores exist only on the matrix-core form (T*G >= 64, d = 128, device index)
-    d = k.Dims(1, 2, 12, 128, 32)
-    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 1, 256) == 0
+    # FP8 scores need d = 128 and either T*G <= 64 (stored path, either index
+    # location) or an index in HBM (two-pass path)
+    d = k.Dims(1, 2, 12, 128, 32)                    # G = 6
+    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 1, 256) > 0
     assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 16, 256) > 0
+    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 10, 1024, k.KVM_INDEX_HOST_TILED, 512) > 0
+    assert k.kvm_score_ws_bytes(d, k.KVM_FP8_E4M3, 11, 1024, k.KVM_INDEX_HOST_TILED, 512) == 0
+    assert k.kvm_score_ws_bytes(k.Dims(1, 2, 12, 64, 32), k.KVM_FP8_E4M3, 1, 256) == 0

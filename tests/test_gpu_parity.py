@@ -217,21 +217,88 @@ def test_fp8_scores_match_oracle(k, dev, N, scale):
     assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
 
 
-def test_fp8_scores_unsupported_forms(k, dev):
-    """FP8 scores exist only on the matrix-core path."""
+@pytest.mark.parametrize("N,T,L", [(700, 1, 2), (333, 5, 1), (1500, 10, 1)])
+def test_fp8_stored_scores_match_oracle(k, dev, N, T, L):
+    """FP8 scoring ablation on the stored-score path (T*G <= 64: decode-sized
+    query rows, 6 to 60 here, ragged against the 16-row tiles and the 512-block
+    partials): E4M3 queries and Mean-K against the float64 Eq. (10) of the
+    decoded values."""
     import torch
-    wl = synth.get_workload("ctx64k").scaled(n_layers=1, n_q_tokens=5)   # T*G = 30 < 64
+    wl = synth.get_workload("ctx64k").scaled(n_layers=L, n_q_tokens=T)
+    say("fp8 stored scores", N, T, L)
+    index = op.index_rows(wl, 0, N)
+    q = op.query_stored(wl, 0, index)
+    qb = fp8_encode(op.as_f64(q, "bf16"))
+    ib = fp8_encode(index)
+    ref = op.block_scores(fp8_decode(qb), fp8_decode(ib))
     dims = k.dims_for(wl)
-    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 5, 256, 0, 0) == 0
-    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 64, 1024, k.KVM_INDEX_HOST_TILED, 512) == 0
-    q = torch.zeros(wl.n_layers * wl.n_q_heads * 5 * wl.head_dim, dtype=torch.uint8, device=dev)
-    idx = torch.zeros(wl.n_layers * wl.n_kv_heads * 256 * wl.head_dim, dtype=torch.uint8,
-                      device=dev)
+    ws_b = k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, T, N, 0, 0)
+    assert ws_b > 0
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    scores = torch.empty(N, dtype=torch.float32, device=dev)
+    k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, torch.from_numpy(qb).to(dev), T,
+                       torch.from_numpy(np.ascontiguousarray(ib)).to(dev), N, N, 0, 0, scores,
+                       ws, ws_b)
+    got = scores.cpu().numpy().astype(np.float64)
+    assert abs(got.sum() - T) <= 1e-5 * T
+    rel = np.abs(got - ref) / ref
+    assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
+
+
+def test_fp8_host_tiled_scores_equal_resident(k, dev):
+    """An E4M3 index streamed from pinned host memory in 512-block tiles gives
+    the same scores, bit for bit, as the same index resident in HBM (same
+    kernels, same partial boundaries)."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, n_q_tokens=1)
+    N, T, tile = 1300, 1, 512
+    say("fp8 host-tiled scores", N)
+    index = op.index_rows(wl, 0, N)
+    qb = fp8_encode(op.as_f64(op.query_stored(wl, 0, index), "bf16"))
+    ib = np.ascontiguousarray(fp8_encode(index))                 # [L][Hkv][N][d]
+    dims = k.dims_for(wl)
+    q = torch.from_numpy(qb).to(dev)
+    ws_r = k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, T, N, 0, 0)
+    ws = torch.empty(ws_r, dtype=torch.uint8, device=dev)
+    want = torch.empty(N, dtype=torch.float32, device=dev)
+    k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, q, T, torch.from_numpy(ib).to(dev), N, N, 0, 0,
+                       want, ws, ws_r)
+    # host layout: tile-major [tile][L*Hkv][tile_blocks][d], the last tile zero-padded
+    nlg, d = wl.n_layers * wl.n_kv_heads, wl.head_dim
+    ntile = (N + tile - 1) // tile
+    host = torch.zeros(ntile * nlg * tile * d, dtype=torch.uint8, pin_memory=True)
+    hv = host.numpy().reshape(ntile, nlg, tile, d)
+    flat = ib.reshape(nlg, N, d)
+    for t in range(ntile):
+        n = min(tile, N - t * tile)
+        hv[t, :, :n] = flat[:, t * tile:t * tile + n]
+    ws_h = k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, T, N, k.KVM_INDEX_HOST_TILED, tile)
+    assert ws_h > 0
+    wsh = torch.empty(ws_h, dtype=torch.uint8, device=dev)
+    got = torch.empty(N, dtype=torch.float32, device=dev)
+    k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, q, T, host, 0, N, k.KVM_INDEX_HOST_TILED, tile,
+                       got, wsh, ws_h)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    ref = op.block_scores(fp8_decode(qb), fp8_decode(ib))
+    assert np.max(np.abs(got.cpu().numpy() - ref) / ref) <= 1e-5
+
+
+def test_fp8_scores_unsupported_forms(k, dev):
+    """FP8 scores need d = 128 and either T*G <= 64 or an index in HBM."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=1, n_q_tokens=11)   # T*G = 66 > 64
+    dims = k.dims_for(wl)
+    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 11, 256, 0, 0) > 0
+    assert k.kvm_score_ws_bytes(dims, k.KVM_FP8_E4M3, 11, 1024, k.KVM_INDEX_HOST_TILED, 512) == 0
+    q = torch.zeros(wl.n_layers * wl.n_q_heads * 11 * wl.head_dim, dtype=torch.uint8, device=dev)
+    host = torch.zeros(wl.n_layers * wl.n_kv_heads * 1024 * wl.head_dim, dtype=torch.uint8,
+                       pin_memory=True)
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-    scores = torch.empty(256, dtype=torch.float32, device=dev)
+    scores = torch.empty(1024, dtype=torch.float32, device=dev)
     with pytest.raises(k.KvmError) as e:
-        k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, q, 5, idx, 256, 256, 0, 0, scores, ws,
-                           ws.numel())
+        k.kvm_score_blocks(dims, k.KVM_FP8_E4M3, q, 11, host, 0, 1024, k.KVM_INDEX_HOST_TILED,
+                           512, scores, ws, ws.numel())
     assert e.value.code == k.api._abi.KVM_ENOTSUP
 
 
