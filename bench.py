@@ -512,13 +512,13 @@ def run_ws10m(args, k, wl, dev):
     sel_ws = torch.empty(k.kvm_select_ws_bytes(N), dtype=torch.uint8, device=dev)
     log(f"setup {time.time() - t0:.1f}s")
 
-    def leg(loc):
-        wsb = k.kvm_score_ws_bytes(dims, bf, 1, N, loc, tb if loc else 0)
+    def leg(loc, dt=bf, qq=q, dev_index=index, host_index=host):
+        wsb = k.kvm_score_ws_bytes(dims, dt, 1, N, loc, tb if loc else 0)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        src, tiles = (index, 0) if loc == k.KVM_INDEX_DEVICE else (host, tb)
+        src, tiles = (dev_index, 0) if loc == k.KVM_INDEX_DEVICE else (host_index, tb)
 
         def step():
-            k.kvm_score_blocks(dims, bf, q, 1, src, N, N, loc, tiles, scores, ws, wsb)
+            k.kvm_score_blocks(dims, dt, qq, 1, src, N, N, loc, tiles, scores, ws, wsb)
             k.kvm_select(scores, N, wl.n_sink, wl.n_recent, wl.budget_blocks, wl.block_tokens,
                          sel, n_sel, base, sel_ws, sel_ws.numel())
         for _ in range(max(1, args.warmup)):
@@ -538,6 +538,20 @@ def run_ws10m(args, k, wl, dev):
     ms_res, kern_res, r_res = leg(k.KVM_INDEX_DEVICE)
     ms_til, kern_til, r_til = leg(k.KVM_INDEX_HOST_TILED)
     assert torch.equal(r_res, r_til), "resident and host-tiled scores differ"
+    # FP8 scoring ablation: the same index and query encoded to E4M3 on the GPU;
+    # the host tiles reuse the pinned buffer (tile-major, 1 byte per element)
+    i8 = torch.empty((nlg, N, d), dtype=torch.uint8, device=dev)
+    q8 = torch.empty(q.numel(), dtype=torch.uint8, device=dev)
+    k.kvm_quantize_e4m3(index, bf, index.numel(), i8)
+    k.kvm_quantize_e4m3(q, bf, q.numel(), q8)
+    h8 = host.view(-1).view(torch.uint8)[:ntile * nlg * tb * d].view(ntile, nlg, tb, d)
+    for t in range(ntile):
+        nb = min(tb, N - t * tb)
+        h8[t, :, :nb, :].copy_(i8[:, t * tb:t * tb + nb, :].cpu())
+    ms_f8, kern_f8, r_f8 = leg(k.KVM_INDEX_DEVICE, k.KVM_FP8_E4M3, q8, i8, h8)
+    ms_f8t, kern_f8t, r_f8t = leg(k.KVM_INDEX_HOST_TILED, k.KVM_FP8_E4M3, q8, i8, h8)
+    assert torch.equal(r_f8, r_f8t), "resident and host-tiled FP8 scores differ"
+    f8_rel = float(((r_f8.double() - r_res.double()).abs() / r_res.double()).max())
     idx_bytes = N * nlg * d * 2
     s_bytes = 2 * N * L * Hq * 4            # stored scores written and read back
     p1 = kern_res.get("score_stored_pass1", {}).get("avg_ms")
@@ -549,8 +563,17 @@ def run_ws10m(args, k, wl, dev):
     til = {"ms_per_step": ms_til, "blocks_per_s": N / (ms_til * 1e-3),
            "h2d_GBps": idx_bytes / (ms_til * 1e-3) / 1e9, "tile_bytes": nlg * tb * d * 2,
            "kernels": kern_til}
+    f8p1 = kern_f8.get("score_stored_pass1", {}).get("avg_ms")
+    fp8 = {"resident": {"ms_per_step": ms_f8, "blocks_per_s": N / (ms_f8 * 1e-3),
+                        "pass1_GBps": (idx_bytes / 2 + s_bytes / 2) / (f8p1 * 1e-3) / 1e9
+                        if f8p1 else None, "kernels": kern_f8},
+           "host_tiled": {"ms_per_step": ms_f8t, "blocks_per_s": N / (ms_f8t * 1e-3),
+                          "h2d_GBps": idx_bytes / 2 / (ms_f8t * 1e-3) / 1e9,
+                          "tile_bytes": nlg * tb * d, "kernels": kern_f8t},
+           "max_rel_diff_vs_bf16": f8_rel}
     log(f"resident: {ms_res:.2f} ms/step; host-tiled: {ms_til:.1f} ms/step "
-        f"({til['h2d_GBps']:.1f} GB/s of index over PCIe)")
+        f"({til['h2d_GBps']:.1f} GB/s of index over PCIe); FP8 resident {ms_f8:.2f}, "
+        f"host-tiled {ms_f8t:.1f} ms/step")
     print(json.dumps({
         "metric": "history blocks scored/s, 10M-token workspace", "value": N / (ms_res * 1e-3),
         "unit": "blocks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -561,7 +584,7 @@ def run_ws10m(args, k, wl, dev):
                                "heads, d 128, 1 query token, budget 2048 blocks (sink 1, "
                                "recent 256); scoring + selection",
                    "tile_blocks": tb},
-        "resident": res, "host_tiled": til,
+        "resident": res, "host_tiled": til, "fp8_scores": fp8,
     }), flush=True)
 
 

@@ -106,8 +106,9 @@ int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
  * q       device, pre-RoPE queries [L][Hq][n_q_tokens][d] in `dtype`.
  *         dtype KVM_FP8_E4M3 scores E4M3 queries against an E4M3 index (the
  *         FP8 scoring ablation; both from kvm_quantize_e4m3): the products are
- *         exact and the sums and softmax run in fp32/fp64 as for bf16. Only
- *         the matrix-core form exists for it: d = 128, T*G >= 64 and a
+ *         exact and the sums and softmax run in fp32/fp64 as for bf16. It
+ *         runs on the matrix cores only and needs d = 128 and either
+ *         T*G <= 64 (stored-score form, device or host-tiled index) or a
  *         device index, else KVM_ENOTSUP (and kvm_score_ws_bytes returns 0).
  * index   KVM_INDEX_DEVICE: device [L][Hkv][index_cap_blocks][d];
  *         KVM_INDEX_HOST_TILED: pinned host, tile-major, tile_blocks a
