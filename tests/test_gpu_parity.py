@@ -187,6 +187,32 @@ def test_quantize_e4m3_bit_exact(k, dev, src):
 
 
 @pytest.mark.parametrize("N,scale", [
+    (1, {"n_layers": 1}),                                         # one block, two-pass form
+    (1, {"n_layers": 1, "n_q_tokens": 1}),                        # one block, stored form
+    (3, {"n_layers": 1, "n_q_tokens": 11}),                       # T*G = 66 over 3 blocks
+    (129, {"n_layers": 1, "n_q_heads": 16, "n_q_tokens": 32}),    # G = 2, T*G = 64: two-pass
+    (129, {"n_layers": 1, "n_q_heads": 16, "n_q_tokens": 31}),    # T*G = 62: stored form
+    (300, {"n_layers": 1, "n_q_heads": 8, "n_q_tokens": 64}),     # G = 1, T*G = 64
+    (300, {"n_layers": 1, "n_q_heads": 8, "n_q_tokens": 63}),     # G = 1, stored form
+    (200, {"n_layers": 2, "head_dim": 64, "n_q_tokens": 40}),     # d = 64 bf16, 240 rows
+])
+def test_scores_edge_shapes_match_oracle(k, dev, N, scale):
+    """Degenerate and boundary shapes: a single block (every softmax is 1, so
+    R = T), a handful of blocks on the two-pass form, T*G on either side of
+    the 64 rows where the stored-score form takes over, no grouping (G = 1),
+    and d = 64 with bf16."""
+    wl = synth.get_workload("ctx64k").scaled(**scale)
+    say("score edge", N, scale)
+    got, ref = _score_case(k, dev, wl, N)
+    T = wl.n_q_tokens
+    assert abs(got.sum() - T) <= 1e-5 * T
+    if N == 1:
+        assert abs(got[0] - T) <= 1e-5 * T
+    rel = np.abs(got - ref) / ref
+    assert rel.max() <= 1e-5, f"max rel err {rel.max()} at block {rel.argmax()}"
+
+
+@pytest.mark.parametrize("N,scale", [
     (2048, {}),                                     # full ctx64k shape
     (1000, {"n_layers": 2, "n_q_tokens": 77}),      # ragged rows (TG 462) and blocks
 ])
