@@ -960,19 +960,29 @@ __global__ __launch_bounds__(64) void score_stored_lse(const float2* __restrict_
   if (lane == 0) lse[i] = (float)((double)M + log2(sum));
 }
 
+// Pass 2 of the stored-score path: thread b sums exp2(S - LSE) over the TG
+// scores of each (l, g) in row order in fp32, and those sums over (l, g) in
+// order in fp64. TGC > 0 fixes the row count at compile time (decode-sized
+// query rows), so the loads of several (l, g) are in flight at once; the
+// arithmetic is the same either way.
+template <int TGC>
 __global__ __launch_bounds__(256) void score_stored_pass2(const float* __restrict__ S,
                                                           const float* __restrict__ lse,
-                                                          int32_t nlg, int32_t TG,
+                                                          int32_t nlg, int32_t TG_rt,
                                                           int32_t n_blocks, double inv_lh,
                                                           float* __restrict__ scores) {
+  const int TG = TGC > 0 ? TGC : TG_rt;
   extern __shared__ float lse_s[];  // [nlg*TG]
   for (int i = threadIdx.x; i < nlg * TG; i += 256) lse_s[i] = lse[i];
   __syncthreads();
   const int32_t b = blockIdx.x * 256 + threadIdx.x;
   if (b >= n_blocks) return;
+  const float* col = S + (int64_t)b * TG;
+  const int64_t lg_stride = (int64_t)n_blocks * TG;
   double s = 0.0;
+#pragma unroll 4
   for (int32_t lg = 0; lg < nlg; ++lg) {
-    const float* row = S + ((int64_t)lg * n_blocks + b) * TG;
+    const float* row = col + lg * lg_stride;
     const float* ls = lse_s + lg * TG;
     float t = 0.0f;
     for (int r = 0; r < TG; ++r) t += hw_exp2(row[r] - ls[r]);
@@ -1289,9 +1299,24 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   KVM_HIP(hipGetLastError());
   const size_t shm2 = (size_t)nlg * TG * sizeof(float);
   { KernelTimer tm("score_stored_pass2", s);
-  score_stored_pass2<<<dim3((uint32_t)((n_blocks + 255) / 256)), dim3(256), shm2, s>>>(
-      a.S, reinterpret_cast<const float*>(w + p.off_lse), nlg, TG, (int32_t)n_blocks, inv_lh,
-      scores); }
+  const dim3 g2((uint32_t)((n_blocks + 255) / 256));
+  const float* lse = reinterpret_cast<const float*>(w + p.off_lse);
+#define KVM_P2(C)                                                                       \
+  score_stored_pass2<C><<<g2, dim3(256), shm2, s>>>(a.S, lse, nlg, TG, (int32_t)n_blocks, \
+                                                    inv_lh, scores)
+  switch (TG) {
+    case 1: KVM_P2(1); break;
+    case 2: KVM_P2(2); break;
+    case 3: KVM_P2(3); break;
+    case 4: KVM_P2(4); break;
+    case 5: KVM_P2(5); break;
+    case 6: KVM_P2(6); break;
+    case 7: KVM_P2(7); break;
+    case 8: KVM_P2(8); break;
+    default: KVM_P2(0); break;
+  }
+#undef KVM_P2
+  }
   KVM_HIP(hipGetLastError());
   return KVM_OK;
 }
