@@ -770,7 +770,10 @@ struct StoredOps<uint8_t, 128> {
   }
 };
 
-template <typename E, int D>
+// STAGE (T*G <= 32): each wavefront collects the scores of its 64 rows in LDS
+// and writes them as one contiguous span with consecutive lanes on consecutive
+// words, instead of scattered per-tile stores of T*G words per row.
+template <typename E, int D, bool STAGE>
 __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   using O = StoredOps<E, D>;
   constexpr int KS = O::KS;
@@ -801,6 +804,8 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   }
   const char* base = reinterpret_cast<const char*>(a.index) + (int64_t)lg * a.lg_stride * sizeof(E);
   float* Sl = a.S + ((int64_t)lg * a.n_blocks + a.b_first) * a.TG;
+  extern __shared__ float stg_all[];           // STAGE: [4 waves][16*TU rows][TG]
+  float* stg = stg_all + wave * (16 * TU) * a.TG;
   // online (shift, sum-exp) of the lane's query rows over its scores
   float m_run[MAXCT], s_run[MAXCT];
 #pragma unroll
@@ -836,7 +841,8 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
             const int32_t row = t0 + 4 * kg + v;
             if (row < r_end) {
               const float x = acc[v] * a.scale;
-              Sl[(int64_t)row * a.TG + rho] = x;
+              if (STAGE) stg[(row - r0) * a.TG + rho] = x;
+              else Sl[(int64_t)row * a.TG + rho] = x;
               if (x > m_run[ct]) {
                 s_run[ct] = s_run[ct] * hw_exp2(m_run[ct] - x) + 1.0f;
                 m_run[ct] = x;
@@ -847,6 +853,18 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
           }
         }
       }
+    }
+    if (STAGE) {
+      // the wave's own LDS rows: its writes are visible to its reads once the
+      // LDS counter drains, and the next group's writes follow these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int32_t nrows = r_end - r0 < 16 * TU ? r_end - r0 : 16 * TU;
+      const int n = nrows * a.TG;
+      float* dst = Sl + (int64_t)r0 * a.TG;
+      for (int i = lane; i < n; i += 64) dst[i] = stg[i];
+      __builtin_amdgcn_wave_barrier();
     }
   }
   // merge the four lanes of each query row (xor 16, 32), then the waves in order
@@ -1106,9 +1124,17 @@ static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStrea
     const int32_t chunks_here = (a.nb + a.chunk - 1) / a.chunk;
     const dim3 grid((uint32_t)((int64_t)a.nlg * chunks_here));
     KernelTimer tm("score_stored_pass1", s);
-    if (dtype == KVM_FP8_E4M3) score_stored_pass1_mfma<uint8_t, 128><<<grid, dim3(256), 0, s>>>(a);
-    else if (D == 128) score_stored_pass1_mfma<uint16_t, 128><<<grid, dim3(256), 0, s>>>(a);
-    else score_stored_pass1_mfma<uint16_t, 64><<<grid, dim3(256), 0, s>>>(a);
+    const bool stage = a.TG <= 32;
+    const size_t shm = stage ? (size_t)4 * 64 * a.TG * sizeof(float) : 0;
+#define KVM_SP1(E, DD)                                                                     \
+  do {                                                                                     \
+    if (stage) score_stored_pass1_mfma<E, DD, true><<<grid, dim3(256), shm, s>>>(a);      \
+    else score_stored_pass1_mfma<E, DD, false><<<grid, dim3(256), 0, s>>>(a);             \
+  } while (0)
+    if (dtype == KVM_FP8_E4M3) KVM_SP1(uint8_t, 128);
+    else if (D == 128) KVM_SP1(uint16_t, 128);
+    else KVM_SP1(uint16_t, 64);
+#undef KVM_SP1
   } else if (dtype == KVM_BF16) {
     if (D == 128) launch_stored_pass1<uint16_t, 128>(a, s);
     else launch_stored_pass1<uint16_t, 64>(a, s);
