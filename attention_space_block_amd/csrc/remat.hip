@@ -324,8 +324,10 @@ struct kvm_ctx {
   kvm::RematJob* h_jobs = nullptr;   // pinned
   int32_t* h_sel = nullptr;          // pinned [n_slots + 1]
   int32_t* h_page = nullptr;         // pinned [n_slots]
-  hipStream_t side = nullptr;
+  hipStream_t side = nullptr;        // H2D of K pages (and of gathered pages)
+  hipStream_t side_v = nullptr;      // H2D of V pages from pinned sources
   std::vector<hipEvent_t> batch_ev;  // H2D batches (side stream)
+  std::vector<hipEvent_t> batch_ev_v;  // H2D batches (side_v)
   std::vector<hipEvent_t> ring_ev;   // ring half reuse
   char* ring = nullptr;              // pinned [2][batch][2][page]
   kvm::WorkerPool* pool = nullptr;
@@ -346,8 +348,10 @@ static void destroy(kvm_ctx* c) {
   if (!c) return;
   delete c->pool;
   for (auto e : c->batch_ev) (void)hipEventDestroy(e);
+  for (auto e : c->batch_ev_v) (void)hipEventDestroy(e);
   for (auto e : c->ring_ev) (void)hipEventDestroy(e);
   if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->side_v) (void)hipStreamDestroy(c->side_v);
   if (c->d_table) (void)hipFree(c->d_table);
   if (c->d_jobs) (void)hipFree(c->d_jobs);
   if (c->h_jobs) (void)hipHostFree(c->h_jobs);
@@ -464,6 +468,7 @@ extern "C" int kvm_ctx_create(const kvm_ctx_desc* desc, kvm_ctx** out) {
   KVM_HIP_C(hipHostMalloc(&c->h_page, (size_t)desc->n_slots * sizeof(int32_t),
                           hipHostMallocDefault));
   KVM_HIP_C(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+  KVM_HIP_C(hipStreamCreateWithFlags(&c->side_v, hipStreamNonBlocking));
 #undef KVM_HIP_C
   *out = c;
   return KVM_OK;
@@ -472,6 +477,7 @@ extern "C" int kvm_ctx_create(const kvm_ctx_desc* desc, kvm_ctx** out) {
 extern "C" void kvm_ctx_destroy(kvm_ctx* ctx) {
   if (!ctx) return;
   (void)hipStreamSynchronize(ctx->side);
+  (void)hipStreamSynchronize(ctx->side_v);
   kvm::destroy(ctx);
 }
 
@@ -644,6 +650,7 @@ extern "C" int kvm_ctx_sync(kvm_ctx* c) {
   using namespace kvm;
   KVM_CHECK_ARG(c, "ctx is NULL");
   KVM_HIP(hipStreamSynchronize(c->side));
+  KVM_HIP(hipStreamSynchronize(c->side_v));
   return KVM_OK;
 }
 
@@ -837,19 +844,25 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   if (rc) return rc;
   st.d2d_bytes += (int64_t)(hit_jobs.size() + delta_jobs.size()) * 2 * c->page_bytes +
                   (int64_t)dev_jobs.size() * 4 * c->page_bytes;
-  // 5. Misses from pinned host memory: DMA straight into the pages, batched.
+  // 5. Misses from pinned host memory: DMA straight into the pages, batched;
+  //    K pages on one side stream and V pages on another, so two copy engines
+  //    share the transfer (4 MiB copies run at about 50 GB/s on one stream and
+  //    56 GB/s on two).
   const int32_t bb = c->d.batch_blocks;
   int32_t cursor = n_first;
   const int32_t n_dma = (int32_t)dma_miss.size();
   const int32_t n_dma_batches = (n_dma + bb - 1) / bb;
   rc = ensure_events(c->batch_ev, (size_t)n_dma_batches + 2 * ((gather_miss.size() + bb - 1) / bb) + 2);
   if (rc) return rc;
+  rc = ensure_events(c->batch_ev_v, (size_t)n_dma_batches);
+  if (rc) return rc;
   int32_t ev_used = 0;
   if (n_dma > 0) {
-    // The side stream must not start before the caller's stream reached this point.
+    // The side streams must not start before the caller's stream reached this point.
     hipEvent_t start = c->batch_ev[ev_used++];
     KVM_HIP(hipEventRecord(start, s));
     KVM_HIP(hipStreamWaitEvent(c->side, start, 0));
+    KVM_HIP(hipStreamWaitEvent(c->side_v, start, 0));
   }
   for (int32_t bi = 0; bi < n_dma_batches; ++bi) {
     const int32_t first = cursor + bi * bb;
@@ -863,13 +876,16 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
       ++pages_in;
       if (!(jb.flags & JOB_K_ONLY)) {
         KVM_HIP(hipMemcpyAsync((char*)c->d.v_view + (int64_t)jb.slot * c->page_bytes, r.src_v,
-                               c->page_bytes, hipMemcpyHostToDevice, c->side));
+                               c->page_bytes, hipMemcpyHostToDevice, c->side_v));
         ++pages_in;
       }
     }
     hipEvent_t ev = c->batch_ev[ev_used++];
     KVM_HIP(hipEventRecord(ev, c->side));
     KVM_HIP(hipStreamWaitEvent(s, ev, 0));
+    hipEvent_t ev_v = c->batch_ev_v[bi];
+    KVM_HIP(hipEventRecord(ev_v, c->side_v));
+    KVM_HIP(hipStreamWaitEvent(s, ev_v, 0));
     rc = launch_range(first, cnt);
     if (rc) return rc;
     st.h2d_bytes += (int64_t)pages_in * c->page_bytes;
