@@ -48,11 +48,17 @@ enum { JOB_COPY_V = 2, JOB_DELTA = 4, JOB_K_ONLY = 8 };
 
 // (l, g) units of 32 token rows handled by one workgroup
 static constexpr int REMAT_UNITS = 8;
+// FP8 rows are half as long, so a thread's (cos, sin) pairs serve twice as many
+// rows before they are amortised like bf16's: 16 units per workgroup
+static constexpr int REMAT_UNITS_FP8 = 16;
+static constexpr int remat_units(int elem_bytes) {
+  return elem_bytes == 1 ? REMAT_UNITS_FP8 : REMAT_UNITS;
+}
 
 struct RematArgs {
   const RematJob* jobs;
   int32_t n_jobs;
-  int32_t wg_per_job;        // ceil(L * Hkv / REMAT_UNITS) workgroups per block
+  int32_t wg_per_job;        // ceil(L * Hkv / units) workgroups per block
   int32_t rows_per_page;     // L * Hkv * B
   int64_t page_bytes;
   char* k_view;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int RPI = 256 / TPR;                 // rows per workgroup pass
   constexpr int ROW_BYTES = D * sizeof(T);
   constexpr int HALF = D / 2;
-  constexpr int ROWS = REMAT_UNITS * 32;         // rows per workgroup
+  constexpr int ROWS = remat_units(sizeof(T)) * 32;   // rows per workgroup
   constexpr int NR = ROWS / RPI;                 // rows per thread
   constexpr int NJ = RPI >= 32 ? 1 : 32 / RPI;   // distinct token indices per thread
   constexpr int NC = P;                          // (cos, sin) pairs per piece pair
@@ -824,7 +830,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   const kvm_dims& dm = c->d.dims;
   RematArgs a{};
   a.rows_per_page = dm.n_layers * dm.n_kv_heads * B;
-  a.wg_per_job = (dm.n_layers * dm.n_kv_heads + REMAT_UNITS - 1) / REMAT_UNITS;
+  const int units = remat_units(dtype_bytes(c->d.dtype));
+  a.wg_per_job = (dm.n_layers * dm.n_kv_heads + units - 1) / units;
   a.page_bytes = c->page_bytes;
   a.k_view = (char*)c->d.k_view;
   a.v_view = (char*)c->d.v_view;
