@@ -881,6 +881,10 @@ def main():
         "kernels": kern,
     }
     out["score"]["blocks_per_s"] = N / (out["score"]["ms"] * 1e-3)
+    # (block, layer, KV head) index rows scored per second, and exps per second
+    # over both passes (one per score and pass)
+    out["score"]["rows_per_s"] = N * L * wl.n_kv_heads / (out["score"]["ms"] * 1e-3)
+    out["score"]["exps_per_s"] = 2.0 * L * Hq * T * N / (out["score"]["ms"] * 1e-3)
     print(json.dumps(out), flush=True)
 
 
