@@ -16,6 +16,48 @@ void set_error(const char* fmt, ...) {
 
 void clear_error() { g_err[0] = 0; }
 
+int check_range(const void* p, size_t bytes, RangeKind kind, const char* what) {
+  if (bytes == 0) return KVM_OK;
+  if (p == nullptr) {
+    set_error("%s is NULL", what);
+    return KVM_EINVAL;
+  }
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();                   // leave no sticky error behind
+    at.type = hipMemoryTypeUnregistered;
+  }
+  void* base = nullptr;
+  size_t size = 0;
+  const hipError_t e = hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size,
+                                             const_cast<void*>(p));
+  if (e != hipSuccess) (void)hipGetLastError();
+  if (e != hipSuccess || at.type == hipMemoryTypeUnregistered) {
+    set_error("%s (%p) is not in memory allocated through HIP (device, managed or pinned host)",
+              what, p);
+    return KVM_EINVAL;
+  }
+  if (kind == RANGE_PINNED_HOST && at.type != hipMemoryTypeHost) {
+    set_error("%s (%p) must be pinned host memory", what, p);
+    return KVM_EINVAL;
+  }
+  if (at.type == hipMemoryTypeDevice) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || at.device != dev) {
+      set_error("%s (%p) is device memory of GPU %d, not of the current GPU %d", what, p,
+                at.device, dev);
+      return KVM_EINVAL;
+    }
+  }
+  const size_t off = (size_t)((const char*)p - (const char*)base);
+  if (off > size || bytes > size - off) {
+    set_error("%s: %zu bytes from %p run past the end of its allocation (%zu bytes left)", what,
+              bytes, p, off > size ? (size_t)0 : size - off);
+    return KVM_EINVAL;
+  }
+  return KVM_OK;
+}
+
 int check_dims(const kvm_dims* d, int32_t dtype) {
   KVM_CHECK_ARG(d != nullptr, "dims is NULL");
   KVM_CHECK_ARG(dtype == KVM_F32 || dtype == KVM_BF16 || dtype == KVM_FP8_E4M3,

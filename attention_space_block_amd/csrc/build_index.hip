@@ -377,6 +377,11 @@ extern "C" int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* 
   KVM_CHECK_ARG((n_blocks * dims->n_layers * dims->n_kv_heads + 3) / 4 < 0x7fffffffLL,
                 "grid too large");
   const int32_t nlg = dims->n_layers * dims->n_kv_heads;
+  KVM_CHECK_RANGE(k_raw, (size_t)((n_blocks - 1) * k_block_stride + blk), RANGE_DEVICE, "k_raw");
+  KVM_CHECK_RANGE(index,
+                  (size_t)nlg * index_cap_blocks * dims->head_dim *
+                      dtype_bytes(index_dtype(dtype)),
+                  RANGE_DEVICE, "index");
   hipStream_t s = as_stream(stream);
   if (dtype == KVM_FP8_E4M3) {
     if (dims->head_dim == 128)

@@ -34,6 +34,23 @@ void clear_error();
     }                                                                              \
   } while (0)
 
+// Memory-range check of a pointer argument (host calls only, no device work):
+// the bytes [p, p + bytes) must lie in one allocation made through HIP that
+// the current device can reach (device, managed or pinned host memory), so a
+// pageable, freed or short buffer is reported as KVM_EINVAL instead of
+// faulting in a kernel or a copy. RANGE_PINNED_HOST additionally requires
+// pinned host memory (DMA sources, the host-tiled index). Device memory of
+// another GPU is rejected. Allocators that carve tensors out of larger
+// segments are checked against the segment.
+enum RangeKind { RANGE_DEVICE = 0, RANGE_PINNED_HOST = 1 };
+int check_range(const void* p, size_t bytes, RangeKind kind, const char* what);
+
+#define KVM_CHECK_RANGE(p, bytes, kind, what)                         \
+  do {                                                                \
+    const int rc_ = ::kvm::check_range((p), (bytes), (kind), (what)); \
+    if (rc_) return rc_;                                              \
+  } while (0)
+
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 inline int dtype_bytes(int32_t dtype) {

@@ -45,6 +45,8 @@ extern "C" int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, 
   KVM_CHECK_ARG(n >= 1 && n < (1LL << 40), "n out of range");
   KVM_CHECK_ARG((uintptr_t)dst % 4 == 0, "dst must be 4-byte aligned");
   KVM_CHECK_ARG((uintptr_t)src % (src_dtype == KVM_F32 ? 4 : 2) == 0, "src misaligned");
+  KVM_CHECK_RANGE(src, (size_t)n * (src_dtype == KVM_F32 ? 4 : 2), RANGE_DEVICE, "src");
+  KVM_CHECK_RANGE(dst, (size_t)n, RANGE_DEVICE, "dst");
   const int64_t groups = (n + 3) / 4;
   const dim3 grid((uint32_t)((groups + 255) / 256));
   hipStream_t s = as_stream(stream);

@@ -422,6 +422,14 @@ extern "C" int kvm_ctx_create(const kvm_ctx_desc* desc, kvm_ctx** out) {
   KVM_CHECK_ARG(((uintptr_t)desc->k_view | (uintptr_t)desc->v_view | (uintptr_t)desc->k_shadow) %
                         16 == 0,
                 "pool pointers must be 16-byte aligned");
+  {
+    const kvm_dims& d0 = desc->dims;
+    const size_t pool = (size_t)desc->n_slots * d0.n_layers * d0.n_kv_heads * d0.block_tokens *
+                        d0.head_dim * dtype_bytes(desc->dtype);
+    KVM_CHECK_RANGE(desc->k_view, pool, RANGE_DEVICE, "k_view");
+    KVM_CHECK_RANGE(desc->v_view, pool, RANGE_DEVICE, "v_view");
+    if (desc->k_shadow) KVM_CHECK_RANGE(desc->k_shadow, pool, RANGE_DEVICE, "k_shadow");
+  }
   kvm_ctx* c = new kvm_ctx();
   c->d = *desc;
   if (c->d.batch_blocks <= 0) c->d.batch_blocks = 64;
@@ -508,6 +516,12 @@ extern "C" int kvm_ctx_build_index_rope(kvm_ctx* c, const void* k_rope, int64_t 
               (long long)(pos0 + (int64_t)dm.block_tokens * n_blocks), c->d.max_pos);
     return KVM_ERANGE;
   }
+  KVM_CHECK_RANGE(k_rope, (size_t)((n_blocks - 1) * block_stride + c->page_bytes), RANGE_DEVICE,
+                  "k_rope");
+  KVM_CHECK_RANGE(index,
+                  (size_t)dm.n_layers * dm.n_kv_heads * index_cap_blocks * dm.head_dim *
+                      dtype_bytes(index_dtype(c->d.dtype)),
+                  RANGE_DEVICE, "index");
   return launch_build_rope(c->d.dtype, dm.head_dim, c->d.rope_layout, k_rope, block_stride,
                            n_blocks, dm.n_layers * dm.n_kv_heads, pos0, c->d_table,
                            first_block, index_cap_blocks, index, as_stream(stream));
@@ -527,6 +541,12 @@ extern "C" int kvm_ctx_set_source(kvm_ctx* c, int64_t first_block, int64_t n_blo
     KVM_CHECK_ARG(k_base && v_base && block_stride >= c->page_bytes, "source pointers/stride");
     KVM_CHECK_ARG(((uintptr_t)k_base | (uintptr_t)v_base | (uintptr_t)block_stride) % 16 == 0,
                   "sources must be 16-byte aligned");
+    if (n_blocks > 0) {
+      const size_t span = (size_t)((n_blocks - 1) * block_stride + c->page_bytes);
+      const RangeKind kind = loc == KVM_SRC_HOST_PINNED ? RANGE_PINNED_HOST : RANGE_DEVICE;
+      KVM_CHECK_RANGE(k_base, span, kind, "k source");
+      KVM_CHECK_RANGE(v_base, span, kind, "v source");
+    }
   }
   for (int64_t i = 0; i < n_blocks; ++i) {
     BlockRec& r = c->rec[first_block + i];
@@ -581,6 +601,11 @@ extern "C" int kvm_ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_
   KVM_CHECK_ARG(first_block >= 0 && n_blocks >= 0 && first_block + n_blocks <= c->d.max_blocks,
                 "block range outside the record capacity");
   KVM_CHECK_ARG(block_stride >= c->page_bytes, "block_stride");
+  if (n_blocks > 0) {
+    const size_t span = (size_t)((n_blocks - 1) * block_stride + c->page_bytes);
+    KVM_CHECK_RANGE(k_raw, span, RANGE_DEVICE, "k_raw");
+    KVM_CHECK_RANGE(v_raw, span, RANGE_DEVICE, "v_raw");
+  }
   hipStream_t s = as_stream(stream);
   // Only pages of blocks outside the current view (or free pages) are reused.
   std::vector<std::pair<int64_t, int32_t>> lru;
@@ -674,6 +699,7 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   using namespace kvm;
   clear_error();
   KVM_CHECK_ARG(c && sel_dev && n_sel_dev && page_table_dev, "null pointer");
+  KVM_CHECK_RANGE(n_sel_dev, sizeof(int32_t), RANGE_DEVICE, "n_sel");
   hipStream_t s = as_stream(stream);
   const int32_t B = c->d.dims.block_tokens;
   // 1. Read the selection (stream-ordered; waits only for `stream`).
@@ -694,6 +720,8 @@ extern "C" int kvm_rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32
   }
   int32_t* sel = c->h_sel + 1;
   const bool delta_mode = c->d.delta_limit > 0;
+  KVM_CHECK_RANGE(sel_dev, (size_t)n * sizeof(int32_t), RANGE_DEVICE, "sel");
+  KVM_CHECK_RANGE(page_table_dev, (size_t)n * sizeof(int32_t), RANGE_DEVICE, "page_table");
   if (n > 0) {
     KVM_HIP(hipMemcpyAsync(sel, sel_dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s));
     KVM_HIP(hipStreamSynchronize(s));

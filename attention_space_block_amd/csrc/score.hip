@@ -1197,6 +1197,18 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   }
   KVM_CHECK_ARG(((uintptr_t)q | (uintptr_t)index | (uintptr_t)ws) % 16 == 0,
                 "q, index and ws must be 16-byte aligned");
+  const size_t eb = (size_t)dtype_bytes(dtype);
+  KVM_CHECK_RANGE(q, (size_t)dims->n_layers * dims->n_q_heads * n_q_tokens * D * eb,
+                  RANGE_DEVICE, "q");
+  if (index_loc == KVM_INDEX_DEVICE) {
+    KVM_CHECK_RANGE(index, (size_t)nlg * index_cap_blocks * D * eb, RANGE_DEVICE, "index");
+  } else {
+    const size_t ntile = (size_t)((n_blocks + tile_blocks - 1) / tile_blocks);
+    KVM_CHECK_RANGE(index, ntile * nlg * tile_blocks * D * eb, RANGE_PINNED_HOST,
+                    "host-tiled index");
+  }
+  KVM_CHECK_RANGE(scores, (size_t)n_blocks * sizeof(float), RANGE_DEVICE, "scores");
+  KVM_CHECK_RANGE(ws, p.bytes, RANGE_DEVICE, "ws");
   hipStream_t s = as_stream(stream);
   char* w = reinterpret_cast<char*>(ws);
   const float scale = LOG2E / sqrtf((float)D);

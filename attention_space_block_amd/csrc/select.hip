@@ -27,6 +27,8 @@
 //     blocks and two workgroup scans give its tie rank and its offset, so the
 //     output is ascending without a sort.
 // With n_blocks <= budget every block is selected (select_all_kernel).
+#include <algorithm>
+
 #include "common.hpp"
 #include "profile.hpp"
 
@@ -367,9 +369,14 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     return KVM_ERANGE;
   }
   KVM_CHECK_ARG((int64_t)budget_blocks * block_tokens < 0x7fffffffLL, "positions overflow int32");
+  const size_t out_bytes = (size_t)std::min<int64_t>(budget_blocks, n_blocks) * sizeof(int32_t);
+  KVM_CHECK_RANGE(scores, (size_t)n_blocks * sizeof(float), RANGE_DEVICE, "scores");
+  KVM_CHECK_RANGE(sel, out_bytes, RANGE_DEVICE, "sel");
+  KVM_CHECK_RANGE(base_pos, out_bytes, RANGE_DEVICE, "base_pos");
+  KVM_CHECK_RANGE(n_sel, sizeof(int32_t), RANGE_DEVICE, "n_sel");
   hipStream_t s = as_stream(stream);
-  KernelTimer tm("select", s);
   if (n_blocks <= budget_blocks) {
+    KernelTimer tm("select", s);
     select_all_kernel<<<1, 1024, 0, s>>>(scores, n_blocks, block_tokens, sel, n_sel, base_pos);
     KVM_HIP(hipGetLastError());
     return KVM_OK;
@@ -380,6 +387,8 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     return KVM_ENOMEM;
   }
   KVM_CHECK_ARG((uintptr_t)ws % 256 == 0, "ws must be 256-byte aligned");
+  KVM_CHECK_RANGE(ws, need, RANGE_DEVICE, "ws");
+  KernelTimer tm("select", s);
   const SelWs w = sel_ws(ws);
   const int64_t nwg = sel_nwg(n_blocks);
   const int64_t c0 = n_sink, c1 = n_blocks - n_recent;

@@ -45,7 +45,13 @@ extern "C" {
 
 typedef enum {
   KVM_OK = 0,
-  KVM_EINVAL = -1,  /* bad shape, pointer, alignment or enum value */
+  KVM_EINVAL = -1,  /* bad shape, pointer, alignment or enum value; also a
+                       pointer argument whose byte range is not inside one
+                       allocation made through HIP (device, managed or pinned
+                       host memory), or device memory where pinned host
+                       memory is required, checked before any work is queued
+                       (allocators that sub-allocate are checked against their
+                       segment) */
   KVM_ENOMEM = -2,  /* workspace, pool or record capacity too small */
   KVM_EHIP = -3,    /* a HIP runtime call failed; see kvm_last_error() */
   KVM_ERANGE = -4,  /* budget < sink + recent, block id out of range, block

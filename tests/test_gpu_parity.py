@@ -681,6 +681,65 @@ def test_remat_unchanged_position_is_not_rewritten(k, dev):
     gc.check_view(wl, sel.cpu().numpy(), pool.page.cpu().numpy()[:11], pool)
 
 
+def test_memory_range_checks(k, dev):
+    """Pointer arguments are checked against their allocation before any work
+    is queued: ranges past the end of an allocation, pageable host memory and
+    device memory where pinned host memory is required are KVM_EINVAL. The cases
+    are chosen so that nothing would be touched out of bounds even without the
+    checks (one (layer, KV head), so only in-range rows are ever read)."""
+    import torch
+    EINVAL = k.api._abi.KVM_EINVAL
+    dims = k.Dims(1, 1, 6, 128, 32)
+    page = 32 * 128 * 2
+    huge = 1 << 28                                   # rows claimed: 64 GiB of index
+    # an index capacity far beyond the allocation
+    q = torch.zeros(6 * 16 * 128, dtype=torch.int16, device=dev)
+    index = torch.zeros(256 * 128, dtype=torch.int16, device=dev)
+    ws_b = k.kvm_score_ws_bytes(dims, k.KVM_BF16, 16, 256, 0, 0)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    scores = torch.empty(256, dtype=torch.float32, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_score_blocks(dims, k.KVM_BF16, q, 16, index, huge, 256, 0, 0, scores, ws, ws_b)
+    assert e.value.code == EINVAL and "past the end" in str(e.value)
+    raw = torch.zeros(4 * page // 2, dtype=torch.int16, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_build_index(dims, k.KVM_BF16, raw, page, 0, 4, index, huge)
+    assert e.value.code == EINVAL and "past the end" in str(e.value)
+    # a host-tiled index must be pinned host memory
+    ws_t = k.kvm_score_ws_bytes(dims, k.KVM_BF16, 1, 512, k.KVM_INDEX_HOST_TILED, 512)
+    wst = torch.empty(ws_t, dtype=torch.uint8, device=dev)
+    dev_tiles = torch.zeros(512 * 128, dtype=torch.int16, device=dev)
+    s512 = torch.empty(512, dtype=torch.float32, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_score_blocks(dims, k.KVM_BF16, q, 1, dev_tiles, 0, 512, k.KVM_INDEX_HOST_TILED,
+                           512, s512, wst, ws_t)
+    assert e.value.code == EINVAL and "pinned host" in str(e.value)
+    # lower-tier sources: kind and residency
+    pool = [torch.zeros((4, page // 2), dtype=torch.int16, device=dev) for _ in range(3)]
+    ctx = k.KvmCtx(dims, k.KVM_BF16, pool[0], pool[1], pool[2], 4, 16, 4096)
+    src_dev = torch.zeros((2, page // 2), dtype=torch.int16, device=dev)
+    src_cpu = torch.zeros((2, page // 2), dtype=torch.int16)
+    src_pin = torch.zeros((2, page // 2), dtype=torch.int16).pin_memory()
+    with pytest.raises(k.KvmError) as e:
+        ctx.kvm_ctx_set_source(0, 2, src_dev, src_dev, page, k.KVM_SRC_HOST_PINNED)
+    assert e.value.code == EINVAL and "pinned host" in str(e.value)
+    with pytest.raises(k.KvmError) as e:
+        ctx.kvm_ctx_set_source(0, 2, src_cpu, src_cpu, page, k.KVM_SRC_DEVICE)
+    assert e.value.code == EINVAL and "not in memory allocated through HIP" in str(e.value)
+    with pytest.raises(k.KvmError) as e:                 # 3 blocks from a 2-block buffer
+        ctx.kvm_ctx_set_source(0, 3, src_pin, src_pin, page, k.KVM_SRC_HOST_PINNED)
+    assert e.value.code == EINVAL
+    ctx.kvm_ctx_set_source(0, 2, src_pin, src_pin, page, k.KVM_SRC_HOST_PINNED)
+    ctx.kvm_ctx_set_source(0, 2, src_dev, src_dev, page, k.KVM_SRC_DEVICE)
+    ctx.close()
+    # a pool in pageable memory
+    cpu_pool = torch.zeros((4, page // 2), dtype=torch.int16)
+    with pytest.raises(k.KvmError) as e:
+        k.KvmCtx(dims, k.KVM_BF16, cpu_pool, cpu_pool, cpu_pool, 4, 16, 4096)
+    assert e.value.code == EINVAL
+    torch.cuda.synchronize()
+
+
 def test_remat_error_paths(k, dev):
     import torch
     wl = synth.get_workload("tiny")
