@@ -52,6 +52,8 @@ def parse():
                     help="rematerializations timed in bounded delta re-RoPE mode (0: skip)")
     ap.add_argument("--fp8", type=int, default=1,
                     help="also time the view with FP8 E4M3 K/V pages (0: skip)")
+    ap.add_argument("--median-runs", type=int, default=50,
+                    help="runs of the kernel-median leg after 10 untimed ones (0: skip)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the CPU oracle sample")
     ap.add_argument("--cpu-pairs", type=int, default=6,
                     help="(layer, KV head) pairs in the CPU oracle sample")
@@ -396,6 +398,39 @@ def traffic_for(traffic: dict, short: str, tail: str | None = None):
         if name.split("<")[0].endswith(short) and (tail is None or name.endswith(tail)):
             return val
     return None
+
+
+def kernel_medians(k, ws, runs: int, remat_bytes: int, warm: int = 10) -> dict:
+    """Medians over `runs` launches of the score passes and the remat kernel,
+    after `warm` untimed scorings: scorings back to back, each remat after the
+    pool reset (outside its launch), every launch timed by the library's events."""
+    import torch
+    for _ in range(warm):
+        ws.score_select()
+    torch.cuda.synchronize()
+    p1, p2, rm = [], [], []
+    for _ in range(runs):
+        k.kvm_profile_enable(True)
+        ws.score_select()
+        torch.cuda.synchronize()
+        st = k.kvm_profile_read()
+        k.kvm_profile_enable(False)
+        p1.append(st["score_pass1_mfma"][1] / st["score_pass1_mfma"][0])
+        p2.append(st["score_pass2_mfma"][1] / st["score_pass2_mfma"][0])
+    for _ in range(runs):
+        ws.reset_pool()
+        torch.cuda.synchronize()
+        k.kvm_profile_enable(True)
+        ws.ctx.kvm_rematerialize(ws.sel, ws.n_sel, ws.page)
+        torch.cuda.synchronize()
+        st = k.kvm_profile_read()
+        k.kvm_profile_enable(False)
+        rm.append(st["remat"][1] / st["remat"][0])
+    r = float(np.median(rm))
+    return {"runs": runs, "warmup": warm, "score_pass1_ms": float(np.median(p1)),
+            "score_pass2_ms": float(np.median(p2)), "remat_ms": r,
+            "remat_GBps": remat_bytes / (r * 1e-3) / 1e9,
+            "remat_hbm_frac": remat_bytes / (r * 1e-3) / 1e9 / HBM_PEAK_GBPS}
 
 
 def cpu_baseline(wl, pairs: int) -> dict:
@@ -839,6 +874,10 @@ def main():
                 "step_h2d_GBps": pst["h2d_bytes"] / (pms * 1e-3) / 1e9}
         log(f"pcie leg: {pms:.2f} ms/step")
         ws.set_miss_sources("hbm")
+    med = None
+    if args.median_runs > 0:
+        log(f"kernel medians over {args.median_runs} runs")
+        med = kernel_medians(k, ws, args.median_runs, remat_bytes)
     cpu = None
     if args.cpu_baseline:
         log("timing the CPU oracle sample")
@@ -864,6 +903,7 @@ def main():
         "rooflines_other": others,
         "peaks_measured": peaks,
         "cpu_baseline": cpu,
+        "kernel_medians": med,
         "remat": {"avg_ms": remat["avg_ms"] if remat else None, "bytes": remat_bytes,
                   "GBps": remat_gbps,
                   "hbm_frac": remat_gbps / HBM_PEAK_GBPS if remat_gbps else None,
