@@ -367,11 +367,16 @@ def measured_peaks(dev) -> dict:
         return e0.elapsed_time(e1) / reps * 1e-3
     t_copy = rate(lambda: b.copy_(a), 30)
     t_mm = rate(lambda: torch.mm(x, y, out=z), 40)
+    h = torch.empty(1 << 30, dtype=torch.uint8).pin_memory()
+    d = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    t_h2d = rate(lambda: d.copy_(h, non_blocking=True), 4)
     out = {"hbm_copy_GBps": 2 * a.numel() * 4 / t_copy / 1e9,
            "bf16_gemm_TFLOPs": 2 * 8192 ** 3 / t_mm / 1e12,
-           "how": "torch copy_ of 2 GiB (bytes read + written; 30 untimed, 30 timed) and "
-                  "torch.mm 8192^3 bf16 (40 untimed, 40 timed), event-timed averages"}
-    del a, b, x, y, z
+           "h2d_pinned_GBps": h.numel() / t_h2d / 1e9,
+           "how": "torch copy_ of 2 GiB (bytes read + written; 30 untimed, 30 timed), "
+                  "torch.mm 8192^3 bf16 (40 untimed, 40 timed) and a 1 GiB copy from pinned "
+                  "host memory (4 untimed, 4 timed), event-timed averages"}
+    del a, b, x, y, z, h, d
     return out
 
 
@@ -871,7 +876,9 @@ def main():
         pms = 1e3 * sum(ptimes) / len(ptimes)
         pcie = {"ms_per_step": pms, "blocks_per_s": N / (pms * 1e-3),
                 "h2d_bytes": pst["h2d_bytes"], "batches": pst["batches"],
-                "step_h2d_GBps": pst["h2d_bytes"] / (pms * 1e-3) / 1e9}
+                "step_h2d_GBps": pst["h2d_bytes"] / (pms * 1e-3) / 1e9,
+                "frac_of_h2d_peak_measured": (pst["h2d_bytes"] / (pms * 1e-3) / 1e9 /
+                                              peaks["h2d_pinned_GBps"]) if peaks else None}
         log(f"pcie leg: {pms:.2f} ms/step")
         ws.set_miss_sources("hbm")
     med = None
