@@ -536,8 +536,28 @@ def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0, delt
                                       ("ctx64k_fp8", "pinned"), ("ctx64k_fp8", "gather")])
 def test_remat_view_matches_oracle(k, dev, name, src):
     wl = synth.get_workload(name).scaled(n_layers=2, budget_blocks=96, n_recent=8)
+    say("remat", name, src)
+    _remat_two_steps(k, dev, wl, src)
+
+
+@pytest.mark.parametrize("name,scale,src", [
+    ("ctx64k", {}, "device"), ("ctx64k_fp8", {}, "gather"), ("tiny", {}, "device"),
+    ("ctx64k", {"head_dim": 64}, "pinned"), ("ctx64k_fp8", {"head_dim": 64}, "device"),
+])
+def test_remat_half_split_pairs_match_oracle(k, dev, name, scale, src):
+    """The same two steps with RoPE's half-split pairing (t, t + d/2): bf16,
+    FP8 and fp32 pages, d = 128 and 64."""
+    wl = synth.get_workload(name).scaled(n_layers=2, budget_blocks=96, n_recent=8,
+                                         rope_layout=1, **scale)
+    say("remat half-split", name, scale, src)
+    _remat_two_steps(k, dev, wl, src)
+
+
+def _remat_two_steps(k, dev, wl, src):
+    """Two rematerializations of a 96-block view over 130 pages: all misses,
+    then a selection that keeps about half of the view (hits stay in place,
+    their positions change); every page against the oracle."""
     N = 400
-    say("remat", src)
     pool, keep = _remat_setup(k, dev, wl, N, 130, src, batch=16, staging=32)
     R = synth.scores_f32(21, N)
     sel, n_sel, base = gc.select_dev(k, gc.to_dev(R, dev), N, wl.n_sink, wl.n_recent,
@@ -589,14 +609,15 @@ def _pair_error_in_bound(got, exact, n_delta, layout):
     return float(np.max(err / (2.0 ** (np.floor(np.log2(np.maximum(norm, 2.0 ** -100))) - 7))))
 
 
-@pytest.mark.parametrize("src", ["device", "pinned", "gather"])
-def test_delta_rerope_bounded_and_rebuilt(k, dev, src):
+@pytest.mark.parametrize("src,layout", [("device", 0), ("pinned", 0), ("gather", 0),
+                                        ("device", 1)])
+def test_delta_rerope_bounded_and_rebuilt(k, dev, src, layout):
     """Bounded delta re-RoPE (limit 2): three tracked blocks keep being selected
     while the number of earlier blocks in the view changes, so their compact
     positions shift; every third change rebuilds K from raw K."""
     import torch
     from oracle import bounded_delta_rope, rope_rotate
-    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, rope_layout=layout)
     N, B, limit = 64, wl.block_tokens, 2
     pool, keep = _remat_setup(k, dev, wl, N, 40, src, batch=4, staging=8, delta_limit=limit,
                               max_pos=N * B)
@@ -616,12 +637,13 @@ def test_delta_rerope_bounded_and_rebuilt(k, dev, src):
         pg = pool.page.cpu().numpy()[:len(sel_list)]
         kinds_now, worst = {}, 0.0
         for i, b in enumerate(sel_list):
-            xs, kinds, counts = bounded_delta_rope(raw_k[b], placements[b], limit, "bf16")
+            xs, kinds, counts = bounded_delta_rope(raw_k[b], placements[b], limit, "bf16",
+                                                   layout=wl.rope_layout)
             kinds_now[b] = kinds[-1]
             assert pool.ctx.kvm_ctx_block_deltas(b) == counts[-1]
             got = op.as_f64(gc.to_host_bits(pool.k_view[int(pg[i])]).reshape(raw_k[b].shape),
                             "bf16")
-            exact = rope_rotate(raw_k[b], i * B + np.arange(B))
+            exact = rope_rotate(raw_k[b], i * B + np.arange(B), layout=wl.rope_layout)
             worst = max(worst, _pair_error_in_bound(got, exact, counts[-1], wl.rope_layout))
             if kinds[-1] == "full":
                 assert np.max(np.abs(got - exact)) <= 2e-2
@@ -633,7 +655,8 @@ def test_delta_rerope_bounded_and_rebuilt(k, dev, src):
         assert st["rebuilds"] == want["full"] - misses
         say(f"step {t}: prefix {a}, deltas {st['deltas']}, rebuilds {st['rebuilds']}, "
             f"misses {st['misses']}, worst pair error {worst:.2f} ulp")
-    kinds_30 = bounded_delta_rope(raw_k[30], placements[30], limit, "bf16")[1]
+    kinds_30 = bounded_delta_rope(raw_k[30], placements[30], limit, "bf16",
+                                  layout=wl.rope_layout)[1]
     assert kinds_30 == ["full", "delta", "delta", "full", "same", "delta", "delta", "full"]
     pool.ctx.close()
 
