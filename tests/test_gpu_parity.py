@@ -540,6 +540,18 @@ def test_remat_view_matches_oracle(k, dev, name, src):
     _remat_two_steps(k, dev, wl, src)
 
 
+@pytest.mark.parametrize("name", ["ctx64k", "ctx64k_fp8"])
+def test_head_dim_64_build_and_remat_match_oracle(k, dev, name):
+    """d = 64 with interleaved pairs, bf16 and FP8 K: the Mean-K rows bit-exact
+    against the oracle, then the two rematerialization steps."""
+    wl = synth.get_workload(name).scaled(n_layers=2, head_dim=64)
+    say("d = 64", name)
+    raw = gc.raw_to_device(wl, "K", 0, 130, dev)
+    idx = gc.build_index_dev(k, wl, raw, dev)
+    assert np.array_equal(gc.as_f64(gc.to_host_bits(idx)), op.index_rows(wl, 0, 130))
+    _remat_two_steps(k, dev, wl.scaled(budget_blocks=96, n_recent=8), "device")
+
+
 @pytest.mark.parametrize("name,scale,src", [
     ("ctx64k", {}, "device"), ("ctx64k_fp8", {}, "gather"), ("tiny", {}, "device"),
     ("ctx64k", {"head_dim": 64}, "pinned"), ("ctx64k_fp8", {"head_dim": 64}, "device"),
