@@ -31,14 +31,17 @@ def from_bf16_bits(bits) -> np.ndarray:
 
 
 def round_to_dtype(x, dtype: str) -> np.ndarray:
-    """Store float64 values in the index dtype: bf16 (RNE) or fp32 (RNE); "f64"
-    keeps the float64 value (used by pins that check identities exactly)."""
+    """Store float64 values in the index or page dtype: bf16 (RNE), fp32 (RNE)
+    or fp8 (E4M3, nearest, ties to even, saturating; the page format of FP8 KV);
+    "f64" keeps the float64 value (used by pins that check identities exactly)."""
     if dtype == "f64":
         return np.asarray(x, dtype=np.float64)
     if dtype == "bf16":
         return bf16_round(x)
     if dtype == "f32":
         return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8_decode(fp8_encode(x))
     raise ValueError(dtype)
 
 

@@ -673,6 +673,54 @@ def test_delta_rerope_bounded_and_rebuilt(k, dev, src, layout):
     pool.ctx.close()
 
 
+def test_delta_rerope_fp8_pages_bounded(k, dev):
+    """Bounded delta re-RoPE over FP8 E4M3 pages (limit 2): the same tracked
+    placements as the bf16 test. Each in-place rotation decodes E4M3 exactly,
+    rotates in fp32 and stores one E4M3 value, so a pair's error after n deltas
+    stays within (n + 1) half-spacings of E4M3 at the pair's length (subnormal
+    spacing 2^-9 below 2^-6), plus the fp32 rotation's error; rebuilds from raw
+    K are within half a spacing of the exact value. V stays byte-exact."""
+    import torch
+    from oracle import bounded_delta_rope, rope_rotate
+    wl = synth.get_workload("ctx64k_fp8").scaled(n_layers=2)
+    N, B, limit = 64, wl.block_tokens, 2
+    pool, keep = _remat_setup(k, dev, wl, N, 40, "device", batch=4, staging=8,
+                              delta_limit=limit, max_pos=N * B)
+    tracked = [30, 31, 45]
+    prefix = [5, 9, 2, 12, 12, 7, 3, 10]
+    placements = {}
+    raw_k = {b: fp8_decode(synth.kv_blocks(wl, "K", b, 1)[0]) for b in range(N)}
+    for t, a in enumerate(prefix):
+        sel_list = list(range(a)) + tracked
+        for i, b in enumerate(sel_list):
+            placements.setdefault(b, []).append(i * B)
+        sel = torch.tensor(sel_list, dtype=torch.int32, device=dev)
+        n_sel = torch.tensor([len(sel_list)], dtype=torch.int32, device=dev)
+        st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+        torch.cuda.synchronize()
+        pg = pool.page.cpu().numpy()[:len(sel_list)]
+        for i, b in enumerate(sel_list):
+            _, kinds, counts = bounded_delta_rope(raw_k[b], placements[b], limit, "fp8")
+            assert pool.ctx.kvm_ctx_block_deltas(b) == counts[-1]
+            got = fp8_decode(pool.k_view[int(pg[i])].cpu().numpy()).reshape(raw_k[b].shape)
+            exact = rope_rotate(raw_k[b], i * B + np.arange(B))
+            ea, eb = got[..., 0::2] - exact[..., 0::2], got[..., 1::2] - exact[..., 1::2]
+            err = np.hypot(ea, eb)
+            norm = np.hypot(exact[..., 0::2], exact[..., 1::2])
+            grown = norm * (1 + 0.1 * (counts[-1] + 1))          # length after rounding
+            spacing = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(grown, 2.0 ** -100))) - 3),
+                                 2.0 ** -9)
+            bound = (counts[-1] + 1) * (np.sqrt(2) / 2 * spacing) + 1e-6 * norm
+            assert np.all(err <= bound), f"block {b} after {counts[-1]} deltas"
+            v = pool.v_view[int(pg[i])].cpu().numpy()
+            assert np.array_equal(v, synth.kv_blocks(wl, "V", b, 1).reshape(-1))
+        say(f"fp8 step {t}: prefix {a}, deltas {st['deltas']}, rebuilds {st['rebuilds']}, "
+            f"misses {st['misses']}")
+    kinds_30 = bounded_delta_rope(raw_k[30], placements[30], limit, "fp8")[1]
+    assert kinds_30 == ["full", "delta", "delta", "full", "same", "delta", "delta", "full"]
+    pool.ctx.close()
+
+
 def test_delta_rerope_error_growth(k, dev):
     """One block shifted 12 times with a limit of 12: the K error after n
     deltas stays within (n + 1) * sqrt(2)/2 ulp per pair; the printed worst

@@ -92,3 +92,16 @@ def test_fp8_round_trip_of_every_finite_code():
     from oracle.numerics import fp8_decode, fp8_encode
     fin = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
     assert np.array_equal(fp8_encode(fp8_decode(fin)), fin)
+
+
+def test_round_to_fp8_is_nearest_e4m3_value():
+    """Page stores in FP8 (the bounded delta re-RoPE model of FP8 pages) round
+    to the nearest E4M3 value, ties to the even code, saturating at 448."""
+    from oracle.numerics import round_to_dtype
+    x = np.array([1.0625, 1.1, 1.1875, -3.3, 500.0, -1e9, 2.0 ** -10, 3 * 2.0 ** -10,
+                  0.0, 2.0 ** -9, 240.0, 0.013])
+    want = np.array([1.0, 1.125, 1.25, -3.25, 448.0, -448.0, 0.0, 2.0 ** -8,
+                     0.0, 2.0 ** -9, 240.0, 0.013671875])
+    got = round_to_dtype(x, "fp8")
+    assert np.array_equal(got, want)
+    assert np.array_equal(round_to_dtype(got, "fp8"), got)
