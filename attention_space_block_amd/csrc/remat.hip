@@ -48,11 +48,14 @@ enum { JOB_COPY_V = 2, JOB_DELTA = 4, JOB_K_ONLY = 8 };
 
 // (l, g) units of 32 token rows handled by one workgroup
 static constexpr int REMAT_UNITS = 8;
-// FP8 rows are half as long, so a thread's (cos, sin) pairs serve twice as many
-// rows before they are amortised like bf16's: 16 units per workgroup
+// Units per workgroup scale inversely with the element size, so a thread holds
+// the same bytes of rows in every dtype: FP8 rows are half as long (16 units;
+// a thread's (cos, sin) pairs then serve as many bytes as in bf16), fp32 rows
+// twice as long (4 units; 8 would take all 256 registers, one wave per SIMD)
 static constexpr int REMAT_UNITS_FP8 = 16;
+static constexpr int REMAT_UNITS_F32 = 4;
 static constexpr int remat_units(int elem_bytes) {
-  return elem_bytes == 1 ? REMAT_UNITS_FP8 : REMAT_UNITS;
+  return elem_bytes == 1 ? REMAT_UNITS_FP8 : elem_bytes == 4 ? REMAT_UNITS_F32 : REMAT_UNITS;
 }
 
 struct RematArgs {

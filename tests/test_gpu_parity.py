@@ -540,6 +540,16 @@ def test_remat_view_matches_oracle(k, dev, name, src):
     _remat_two_steps(k, dev, wl, src)
 
 
+def test_fp32_head_dim_128_build_and_remat_match_oracle(k, dev):
+    """fp32 K/V at d = 128 (interleaved pairs): Mean-K bit-exact, then the two
+    rematerialization steps."""
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, dtype="f32")
+    raw = gc.raw_to_device(wl, "K", 0, 130, dev)
+    idx = gc.build_index_dev(k, wl, raw, dev)
+    assert np.array_equal(gc.as_f64(gc.to_host_bits(idx)), op.index_rows(wl, 0, 130))
+    _remat_two_steps(k, dev, wl.scaled(budget_blocks=96, n_recent=8), "pinned")
+
+
 @pytest.mark.parametrize("name", ["ctx64k", "ctx64k_fp8"])
 def test_head_dim_64_build_and_remat_match_oracle(k, dev, name):
     """d = 64 with interleaved pairs, bf16 and FP8 K: the Mean-K rows bit-exact
@@ -555,6 +565,7 @@ def test_head_dim_64_build_and_remat_match_oracle(k, dev, name):
 @pytest.mark.parametrize("name,scale,src", [
     ("ctx64k", {}, "device"), ("ctx64k_fp8", {}, "gather"), ("tiny", {}, "device"),
     ("ctx64k", {"head_dim": 64}, "pinned"), ("ctx64k_fp8", {"head_dim": 64}, "device"),
+    ("ctx64k", {"dtype": "f32"}, "device"),
 ])
 def test_remat_half_split_pairs_match_oracle(k, dev, name, scale, src):
     """The same two steps with RoPE's half-split pairing (t, t + d/2): bf16,
