@@ -27,12 +27,7 @@ int check_range(const void* p, size_t bytes, RangeKind kind, const char* what) {
     (void)hipGetLastError();                   // leave no sticky error behind
     at.type = hipMemoryTypeUnregistered;
   }
-  void* base = nullptr;
-  size_t size = 0;
-  const hipError_t e = hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size,
-                                             const_cast<void*>(p));
-  if (e != hipSuccess) (void)hipGetLastError();
-  if (e != hipSuccess || at.type == hipMemoryTypeUnregistered) {
+  if (at.type == hipMemoryTypeUnregistered) {
     set_error("%s (%p) is not in memory allocated through HIP (device, managed or pinned host)",
               what, p);
     return KVM_EINVAL;
@@ -48,6 +43,15 @@ int check_range(const void* p, size_t bytes, RangeKind kind, const char* what) {
                 at.device, dev);
       return KVM_EINVAL;
     }
+  }
+  // The extent check needs the allocation's range; memory the runtime knows
+  // but cannot give a range for (virtual-memory mappings) is accepted as is.
+  void* base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&base), &size,
+                            const_cast<void*>(p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return KVM_OK;
   }
   const size_t off = (size_t)((const char*)p - (const char*)base);
   if (off > size || bytes > size - off) {

@@ -41,7 +41,8 @@ void clear_error();
 // faulting in a kernel or a copy. RANGE_PINNED_HOST additionally requires
 // pinned host memory (DMA sources, the host-tiled index). Device memory of
 // another GPU is rejected. Allocators that carve tensors out of larger
-// segments are checked against the segment.
+// segments are checked against the segment; memory the runtime reports but
+// cannot give a range for (virtual-memory mappings) skips the extent check.
 enum RangeKind { RANGE_DEVICE = 0, RANGE_PINNED_HOST = 1 };
 int check_range(const void* p, size_t bytes, RangeKind kind, const char* what);
 

@@ -51,7 +51,8 @@ typedef enum {
                        host memory), or device memory where pinned host
                        memory is required, checked before any work is queued
                        (allocators that sub-allocate are checked against their
-                       segment) */
+                       segment; memory without a reported range, such as
+                       virtual-memory mappings, skips the extent check) */
   KVM_ENOMEM = -2,  /* workspace, pool or record capacity too small */
   KVM_EHIP = -3,    /* a HIP runtime call failed; see kvm_last_error() */
   KVM_ERANGE = -4,  /* budget < sink + recent, block id out of range, block
