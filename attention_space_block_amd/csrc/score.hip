@@ -53,20 +53,23 @@ static constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // MFMA passes. Element type E: uint16_t = bf16 operands on
-// v_mfma_f32_32x32x16_bf16 (8 k-steps of 16 per 128-wide row), uint8_t = FP8
-// E4M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales (2 k-steps
-// of 64). Both take A as 32 rows (lane l: row l % 32) and B as 32 columns
+// v_mfma_f32_32x32x16_bf16 (k-steps of 16: 8 per 128-wide row, 4 per 64-wide
+// row), uint8_t = FP8 E4M3 operands on v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit scales (2 k-steps of 64, d = 128). Both take A as 32 rows (lane l: row l % 32) and B as 32 columns
 // (lane l: column l % 32), the two lane halves holding disjoint k pieces of
 // the same row; both operands use the same k pieces per lane, so the product
 // is the full dot product. The 32x32 fp32 result layout is the same for both.
 // A stage holds 128 rows in LDS, stored as 16-byte pieces XOR-swizzled by row
-// so the operand reads are free of bank conflicts.
+// so the operand reads are free of bank conflicts: 256-byte rows by row % 16,
+// 128-byte rows (bf16 d = 64, FP8 d = 128) by (row / 2) % 8, so that 16 lanes
+// reading one piece of 16 consecutive rows hit 16 distinct 16-byte bank groups.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <typename E>
+template <typename E, int DD>
 struct MfmaShape {
-  static constexpr int D = 128;                      // the MFMA path is laid out for d = 128
+  static constexpr int D = DD;                       // head dim: 128, or 64 for bf16
   static constexpr bool FP8 = sizeof(E) == 1;
+  static_assert(D == 128 || (!FP8 && D == 64), "MFMA passes: d = 128, or bf16 with d = 64");
   static constexpr int ROW_B = D * (int)sizeof(E);   // bytes per row: 256 or 128
   static constexpr int PIECES = ROW_B / 16;          // 16-byte pieces per row
   static constexpr int KS = FP8 ? D / 64 : D / 16;   // MFMA k-steps
@@ -79,7 +82,7 @@ struct MfmaShape {
   using Op = typename std::conditional<FP8, i32x8, bf16x8>::type;
   // LDS slot of piece p of stage row r (an involution in p)
   static __device__ __forceinline__ int slot(int r, int p) {
-    return FP8 ? (p ^ ((r >> 1) & 7)) : (p ^ (r & 15));
+    return ROW_B == 128 ? (p ^ ((r >> 1) & 7)) : (p ^ (r & 15));
   }
   // lane (half) piece j of k-step ks
   static __device__ __forceinline__ int piece(int ks, int half, int j) {
@@ -200,9 +203,9 @@ __device__ __forceinline__ void mfma_subtile_woven(f32x16 (&acc)[2], const char*
     pairs(2 * ks + 1);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // With few MFMAs per block the compiler would otherwise sink them below the
-  // caller's branches, away from the exps they are meant to run under.
-  if constexpr (S::FP8) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+  // With few MFMAs per block (FP8, bf16 at d = 64) the compiler would otherwise
+  // sink them below the caller's branches, away from the exps they run under.
+  if constexpr (S::KS <= 4) asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
 }
 
 // Per-lane byte offsets of the A-operand pieces inside a 32-row subtile:
@@ -303,9 +306,9 @@ __device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nv
     }
 }
 
-template <typename E>
+template <typename E, int DD>
 __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
-  using S = MfmaShape<E>;
+  using S = MfmaShape<E, DD>;
   constexpr int D = S::D;
   __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
@@ -478,9 +481,9 @@ __device__ __forceinline__ float exp_sum16_rows(const f32x16& acc, const float (
   return e[0];
 }
 
-template <typename E>
+template <typename E, int DD>
 __global__ __launch_bounds__(256, 2) void score_pass2_mfma(Pass2Args a) {
-  using S = MfmaShape<E>;
+  using S = MfmaShape<E, DD>;
   __shared__ __attribute__((aligned(16))) char lds[2][S::TILE_B];
   __shared__ __attribute__((aligned(16))) float lse_s[2][S::TILE];
   const uint32_t lid = xcd_remap(blockIdx.x, a.total_wg);
@@ -1042,8 +1045,9 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
   const int32_t G = d->n_q_heads / d->n_kv_heads;
   const int32_t nlg = d->n_layers * d->n_kv_heads;
   p.TG = T * G;
-  p.mfma = (dtype == KVM_BF16 || dtype == KVM_FP8_E4M3) && p.TG >= 64 && d->head_dim == 128 &&
-           loc == KVM_INDEX_DEVICE;
+  p.mfma = ((dtype == KVM_BF16 && (d->head_dim == 128 || d->head_dim == 64)) ||
+            (dtype == KVM_FP8_E4M3 && d->head_dim == 128)) &&
+           p.TG >= 64 && loc == KVM_INDEX_DEVICE;
   size_t off = 0;
   if (p.mfma) {
     p.row_chunks = (p.TG + 255) / 256;
@@ -1235,9 +1239,11 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     a1.total_wg = (uint32_t)((wg1 + 7) / 8 * 8);
     { KernelTimer tm("score_pass1_mfma", s);
     if (dtype == KVM_FP8_E4M3)
-      score_pass1_mfma<uint8_t><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
+      score_pass1_mfma<uint8_t, 128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
+    else if (D == 128)
+      score_pass1_mfma<uint16_t, 128><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1);
     else
-      score_pass1_mfma<uint16_t><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1); }
+      score_pass1_mfma<uint16_t, 64><<<dim3(a1.total_wg), dim3(256), 0, s>>>(a1); }
     KVM_HIP(hipGetLastError());
     const int64_t nl = (int64_t)nlg * p.TGp;
     { KernelTimer tm("score_lse_combine", s);
@@ -1264,9 +1270,11 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     a2.total_wg = (uint32_t)((wg2 + 7) / 8 * 8);
     { KernelTimer tm("score_pass2_mfma", s);
     if (dtype == KVM_FP8_E4M3)
-      score_pass2_mfma<uint8_t><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
+      score_pass2_mfma<uint8_t, 128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
+    else if (D == 128)
+      score_pass2_mfma<uint16_t, 128><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2);
     else
-      score_pass2_mfma<uint16_t><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
+      score_pass2_mfma<uint16_t, 64><<<dim3(a2.total_wg), dim3(256), 0, s>>>(a2); }
     KVM_HIP(hipGetLastError());
     { KernelTimer tm("score_reduce", s);
     score_reduce<<<dim3((uint32_t)((n_blocks + 63) / 64)), dim3(256), 0, s>>>(

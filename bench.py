@@ -794,7 +794,7 @@ def main():
             return {"kernel": name, "bound": "mfma", "achieved": ach,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                    "traffic": traffic_for(traffic, name, "<unsigned short>")}
+                    "traffic": traffic_for(traffic, name, "<unsigned short, 128>")}
         if name == "remat":
             return {"kernel": name, "bound": "hbm", "achieved": remat_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS,

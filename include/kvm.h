@@ -128,12 +128,13 @@ int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
  *         to the resident form.
  * scores  device float[n_blocks] (R_b).
  * ws      device workspace of at least kvm_score_ws_bytes(...) bytes.
- * Forms: bf16 and FP8 with d = 128, T*G >= 64 and the index in HBM run two
- *         matrix-core passes over the index; every other case stores the scores
+ * Forms: bf16 (d = 64 or 128) and FP8 (d = 128) with T*G >= 64 and the index
+ *         in HBM run two matrix-core passes over the index; every other case stores the scores
  *         in `ws` in one pass over the index (matrix cores for bf16 and FP8 with
  *         T*G <= 64, vector units otherwise). The vector form needs
  *         (T*G*d + 8)*4 <= 65536 and L*Hkv*T*G*4 <= 65536 bytes (shared memory),
- *         else KVM_ENOTSUP: e.g. fp32 or d = 64 with T*G up to 255 at d = 64.
+ *         else KVM_ENOTSUP: e.g. fp32, or a host-tiled index, with T*G up to 255 at
+ *         d = 64.
  * Errors: KVM_EINVAL (shapes, null pointers, n_blocks < 1, n_q_tokens < 1),
  *         KVM_ENOMEM (ws_bytes too small), KVM_ENOTSUP (dtype/head_dim, or the
  *         T*G limits above). */

@@ -195,12 +195,14 @@ def test_quantize_e4m3_bit_exact(k, dev, src):
     (300, {"n_layers": 1, "n_q_heads": 8, "n_q_tokens": 64}),     # G = 1, T*G = 64
     (300, {"n_layers": 1, "n_q_heads": 8, "n_q_tokens": 63}),     # G = 1, stored form
     (200, {"n_layers": 2, "head_dim": 64, "n_q_tokens": 40}),     # d = 64 bf16, 240 rows
+    (1000, {"n_layers": 2, "head_dim": 64, "n_q_tokens": 77}),    # d = 64, 462 ragged rows
+    (300, {"n_layers": 2, "head_dim": 64, "n_q_tokens": 5}),      # d = 64, stored form
 ])
 def test_scores_edge_shapes_match_oracle(k, dev, N, scale):
     """Degenerate and boundary shapes: a single block (every softmax is 1, so
     R = T), a handful of blocks on the two-pass form, T*G on either side of
     the 64 rows where the stored-score form takes over, no grouping (G = 1),
-    and d = 64 with bf16."""
+    and d = 64 with bf16 on the two-pass (128-byte rows) and stored forms."""
     wl = synth.get_workload("ctx64k").scaled(**scale)
     say("score edge", N, scale)
     got, ref = _score_case(k, dev, wl, N)
