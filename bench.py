@@ -405,6 +405,16 @@ def traffic_for(traffic: dict, short: str, tail: str | None = None):
     return None
 
 
+def workload_desc(wl) -> str:
+    """The workload as the JSON line names it, from its own sizes."""
+    label = {"ws1m": "1M-token workspace", "ctx64k": "64K-token history"}.get(
+        wl.name, f"{wl.n_blocks * wl.block_tokens}-token workspace")
+    return (f"{label}: {wl.n_blocks} blocks x {wl.block_tokens} tokens, {wl.n_layers} layers, "
+            f"{wl.n_kv_heads} KV / {wl.n_q_heads} query heads, d {wl.head_dim}, "
+            f"{wl.n_q_tokens} query tokens, budget {wl.budget_blocks} blocks (sink {wl.n_sink}, "
+            f"recent {wl.n_recent}), half of the view resident")
+
+
 def kernel_medians(k, ws, runs: int, remat_bytes: int, warm: int = 10) -> dict:
     """Medians over `runs` launches of the score passes and the remat kernel,
     after `warm` untimed scorings: scorings back to back, each remat after the
@@ -786,7 +796,9 @@ def main():
     remat = kern.get("remat")
     remat_gbps = remat_bytes / (remat["avg_ms"] * 1e-3) / 1e9 if remat else None
     # rooflines: the dominant kernel of the step, and the other kernels of the path
-    traffic = counter_traffic()
+    # the committed counters were taken on the 1M-token workspace: other
+    # workloads report no traffic rather than that workload's bytes
+    traffic = counter_traffic() if args.workload == "ws1m" else {}
 
     def roofline(name, info):
         if name.startswith("score_pass"):
@@ -863,7 +875,7 @@ def main():
         delta = {"avg_ms": d_ms, "deltas_per_call": dst["deltas"], "bytes": d_bytes,
                  "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
                  "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                 "traffic": traffic_for(counter_traffic(), "remat_kernel", "<unsigned short, 128, 0, true>")}
+                 "traffic": traffic_for(traffic, "remat_kernel", "<unsigned short, 128, 0, true>")}
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
     fp8 = fp8_leg(k, ws, wl, dev, args.steps) if args.fp8 else None
@@ -890,7 +902,7 @@ def main():
         log("timing the CPU oracle sample")
         cpu = cpu_baseline(wl, args.cpu_pairs)
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "ws1m" else METRIC.replace("1M-tok", args.workload),
         "value": N / (ms * 1e-3),
         "unit": "blocks/s",
         "n_gpus": 1,
@@ -902,9 +914,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based generator; no dataset)",
-        "config": {"workload": "1M-token workspace: 32768 blocks x 32 tokens, 64 layers, "
-                               "8 KV / 48 query heads, d 128, 512 query tokens, budget 4096 "
-                               "blocks (sink 1, recent 64), half of the view resident",
+        "config": {"workload": workload_desc(wl),
                    "n_blocks": N, "n_q_tokens": T, "budget_blocks": wl.budget_blocks},
         "roofline": roof,
         "rooflines_other": others,
