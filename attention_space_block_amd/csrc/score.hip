@@ -715,15 +715,15 @@ __global__ __launch_bounds__(256) void score_stored_pass1(StoredArgs a) {
   }
 }
 
-// bf16 pass 1 on the matrix cores: the scores of one (l, g) are the product
-// Kbar[N x d] * Q_g^T[d x TG], taken in 16-row tiles with
-// v_mfma_f32_16x16x32_bf16: A = 16 index rows (lane l holds row l % 16,
-// elements 8*(l/16) .. +8 of each 32-wide k-step, read straight from global
-// memory), B = the TG query rows padded to 16-column tiles (stationary in
-// registers). Each lane's 4 results are rows 4*(l/16) .. +3 of the tile at
-// query row l % 16. The VALU only scales and stores, so the pass streams the
-// index at memory speed. A workgroup takes `chunk` (512) rows of one (l, g);
-// each wave keeps 4 tiles (16 KB) of loads in flight. Each lane also keeps an online (shift, sum-exp) of its query row, so
+// Stored-score pass 1 on the matrix cores (bf16, or FP8 at d = 128): the scores
+// of one (l, g) are the product Kbar[N x d] * Q_g^T[d x TG], taken in 16-row
+// tiles (StoredOps below): A = 16 index rows (lane l holds row l % 16 and its
+// k pieces, read straight from global memory), B = the TG query rows padded to
+// 16-column tiles (stationary in registers). Each lane's 4 results are rows
+// 4*(l/16) .. +3 of the tile at query row l % 16. The VALU only scales and
+// stores, so the pass streams the index at memory speed. A workgroup takes
+// `chunk` (512) rows of one (l, g); each wave keeps 4 tiles of loads in
+// flight. Each lane also keeps an online (shift, sum-exp) of its query row, so
 // the workgroup writes the chunk's partials for the LSE itself.
 // Merge two (shift, sum-exp) pairs of the same row.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
