@@ -380,11 +380,22 @@ def measured_peaks(dev) -> dict:
     return out
 
 
+def source_fingerprint(path: str) -> str:
+    """First 16 hex digits of the SHA-256 of a source file with its comments and
+    blank lines removed, so that only a change of code invalidates counters."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)      # block comments
+    text = re.sub(r"//[^\n]*", "", text)                    # line comments
+    code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def counter_traffic() -> dict:
     """HBM bytes per dispatch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, per kernel; a kernel whose source file changed since the counters
-    were taken maps to None."""
-    import hashlib
+    summary, per kernel; a kernel whose source code (comments aside) changed
+    since the counters were taken maps to None."""
     path = os.path.join(ROOT, "profiles", "ws1m_traffic.json")
     if not os.path.exists(path):
         return {}
@@ -392,8 +403,7 @@ def counter_traffic() -> dict:
     out = {}
     for name, v in data.get("per_dispatch", {}).items():
         src = os.path.join(ROOT, v["source"])
-        ok = os.path.exists(src) and hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] == \
-            v["source_sha256_16"]
+        ok = os.path.exists(src) and source_fingerprint(src) == v["source_sha256_16"]
         out[name] = (v["read_bytes"] + v["write_bytes"]) if ok else None
     return out
 
