@@ -21,9 +21,9 @@ Eq. (10) (only the prose survives), and whether the paper's engine used base
 """
 from .numerics import bf16_round, bf16_bits, round_to_dtype  # noqa: F401
 from .meank import mean_k, mean_k_index, mean_k_from_rope  # noqa: F401
-from .scores import block_scores, lg_partial_scores  # noqa: F401
+from .scores import block_scores, block_scores_streamed, lg_partial_scores  # noqa: F401
 from .select import select_blocks, compact_positions, cutoff_margin  # noqa: F401
 from .rope import rope_frequencies, rope_rotate, rope_matrix, bounded_delta_rope  # noqa: F401
-from .plan import working_set_delta  # noqa: F401
+from .plan import working_set_delta, PagePool, PoolFull  # noqa: F401
 from .accounting import kv_bytes, index_bytes  # noqa: F401
 from .tier import simulate_host_tier  # noqa: F401

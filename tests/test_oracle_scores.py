@@ -93,3 +93,47 @@ def test_tiny_workspace_planted_block_ranks_first():
     assert int(np.argmax(res["R"])) == wl.planted_block
     assert wl.planted_block in set(res["sel"].tolist())
     assert len(res["sel"]) == 11 and list(res["base_pos"]) == list(range(0, 352, 32))
+
+
+# --------------------------------------------------- streamed (tiled) form ----
+# KVMem Sec. 5: scoring an index that does not fit at once keeps the global
+# softmax normalisation, so it equals Eq. (10) over the complete index.
+
+from oracle.scores import block_scores_streamed  # noqa: E402
+
+
+def _slicer(idx):
+    return lambda l, g: idx[l, g]
+
+
+def test_streamed_scores_equal_resident_scores():
+    rng = np.random.default_rng(31)
+    for (L, Hkv, G, T, N, d) in [(2, 2, 3, 4, 37, 16), (3, 1, 2, 5, 1, 8),
+                                 (1, 4, 1, 1, 129, 32), (2, 3, 2, 3, 250, 8)]:
+        q, idx = rand_case(rng, L=L, Hkv=Hkv, G=G, T=T, N=N, d=d)
+        want = block_scores(q, idx, threads=1)
+        got = block_scores_streamed(q, _slicer(idx), Hkv, N, threads=3)
+        assert np.array_equal(got, want)
+        assert abs(got.sum() - T) < 1e-12
+
+
+def test_streamed_scores_catch_a_transposed_pair():
+    # A planted mistake (the (l, g) slice of another pair) must change R.
+    rng = np.random.default_rng(32)
+    q, idx = rand_case(rng, L=2, Hkv=2, G=3, T=4, N=37, d=16)
+    want = block_scores_streamed(q, _slicer(idx), 2, 37, threads=2)
+    wrong = block_scores_streamed(q, lambda l, g: idx[1 - l, g], 2, 37, threads=2)
+    assert np.max(np.abs(wrong - want)) > 1e-3
+    wrong = block_scores_streamed(q, lambda l, g: idx[l, 1 - g], 2, 37, threads=2)
+    assert np.max(np.abs(wrong - want)) > 1e-3
+
+
+def test_streamed_constant_index_and_single_row():
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((2, 4, 3, 8))
+    idx = np.broadcast_to(rng.standard_normal((2, 2, 1, 8)), (2, 2, 50, 8)).copy()
+    assert np.allclose(block_scores_streamed(q, _slicer(idx), 2, 50), 3 / 50, rtol=0, atol=1e-15)
+    q = rng.standard_normal((1, 1, 1, 32))
+    idx = rng.standard_normal((1, 1, 200, 32)) * 3
+    want = scipy.special.softmax(idx[0, 0] @ q[0, 0, 0] / math.sqrt(32))
+    assert np.allclose(block_scores_streamed(q, _slicer(idx), 1, 200), want, rtol=1e-13, atol=0)
