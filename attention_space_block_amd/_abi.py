@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvm.so")
 
 KVM_OK, KVM_EINVAL, KVM_ENOMEM, KVM_EHIP, KVM_ERANGE, KVM_ENOTSUP = 0, -1, -2, -3, -4, -5
+KVM_EINTERNAL = -6
 KVM_F32, KVM_BF16, KVM_FP8_E4M3 = 0, 1, 2
 KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED = 0, 1
 KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE = 0, 1, 2

@@ -1,20 +1,8 @@
-// Entry points that are not tied to one kernel: version, errors, validation.
-#include <stdarg.h>
+// Memory-range validation of pointer arguments (HIP runtime queries only).
 
 #include "common.hpp"
 
 namespace kvm {
-
-static thread_local char g_err[512];
-
-void set_error(const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
-  va_end(ap);
-}
-
-void clear_error() { g_err[0] = 0; }
 
 int check_range(const void* p, size_t bytes, RangeKind kind, const char* what) {
   if (bytes == 0) return KVM_OK;
@@ -62,26 +50,6 @@ int check_range(const void* p, size_t bytes, RangeKind kind, const char* what) {
   return KVM_OK;
 }
 
-int check_dims(const kvm_dims* d, int32_t dtype) {
-  KVM_CHECK_ARG(d != nullptr, "dims is NULL");
-  KVM_CHECK_ARG(dtype == KVM_F32 || dtype == KVM_BF16 || dtype == KVM_FP8_E4M3,
-                "dtype %d invalid", dtype);
-  KVM_CHECK_ARG(d->n_layers > 0 && d->n_kv_heads > 0 && d->n_q_heads > 0,
-                "layers/heads must be positive");
-  KVM_CHECK_ARG(d->n_q_heads % d->n_kv_heads == 0, "n_q_heads %% n_kv_heads != 0");
-  if (d->head_dim != 64 && d->head_dim != 128) {
-    set_error("head_dim %d unsupported (64, 128)", d->head_dim);
-    return KVM_ENOTSUP;
-  }
-  if (d->block_tokens != 32) {
-    set_error("block_tokens %d unsupported (32)", d->block_tokens);
-    return KVM_ENOTSUP;
-  }
-  return KVM_OK;
-}
-
 }  // namespace kvm
 
-extern "C" int kvm_version(void) { return 100; }
 
-extern "C" const char* kvm_last_error(void) { return kvm::g_err; }

@@ -356,7 +356,7 @@ int launch_build_rope(int32_t dtype, int32_t d, int32_t layout, const void* k_ro
 
 }  // namespace kvm
 
-extern "C" int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
+static int kvm_build_index_body(const kvm_dims* dims, int32_t dtype, const void* k_raw,
                                int64_t k_block_stride, int64_t first_block, int64_t n_blocks,
                                void* index, int64_t index_cap_blocks, void* stream) {
   using namespace kvm;
@@ -407,4 +407,13 @@ extern "C" int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* 
   }
   KVM_HIP(hipGetLastError());
   return KVM_OK;
+}
+
+extern "C" int kvm_build_index(const kvm_dims* dims, int32_t dtype, const void* k_raw,
+                               int64_t k_block_stride, int64_t first_block, int64_t n_blocks,
+                               void* index, int64_t index_cap_blocks, void* stream) {
+  return kvm::guarded([&] {
+    return kvm_build_index_body(dims, dtype, k_raw, k_block_stride, first_block, n_blocks, index,
+                                index_cap_blocks, stream);
+  });
 }

@@ -8,21 +8,9 @@
 
 #include <string>
 
-#include "kvm.h"
+#include "host_common.hpp"
 
 namespace kvm {
-
-// ---- error reporting (thread-local last error) ---------------------------
-void set_error(const char* fmt, ...);
-void clear_error();
-
-#define KVM_CHECK_ARG(cond, ...)        \
-  do {                                  \
-    if (!(cond)) {                      \
-      ::kvm::set_error(__VA_ARGS__);    \
-      return KVM_EINVAL;                \
-    }                                   \
-  } while (0)
 
 #define KVM_HIP(call)                                                              \
   do {                                                                             \
@@ -53,15 +41,6 @@ int check_range(const void* p, size_t bytes, RangeKind kind, const char* what);
   } while (0)
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-inline int dtype_bytes(int32_t dtype) {
-  return dtype == KVM_F32 ? 4 : dtype == KVM_FP8_E4M3 ? 1 : 2;
-}
-// dtype of the Mean-K index rows for K of `dtype` (bf16 for FP8 K)
-inline int32_t index_dtype(int32_t dtype) { return dtype == KVM_FP8_E4M3 ? KVM_BF16 : dtype; }
-
-// Validate dims shared by every entry point.
-int check_dims(const kvm_dims* d, int32_t dtype);
 
 // Launcher of the de-RoPE Mean-K kernel (build_index.hip); arguments checked
 // by the caller. table: device [>= pos0 + 32*n_blocks][d/2] (cos, sin).

@@ -39,6 +39,7 @@ hipEvent_t get_event() {
 }  // namespace
 
 KernelTimer::KernelTimer(const char* name, hipStream_t s) : name_(name), s_(s) {
+  if (!name_) return;   // untimed launch
   std::lock_guard<std::mutex> g(g_mu);
   if (!g_on) return;
   a_ = get_event();
@@ -55,7 +56,7 @@ KernelTimer::~KernelTimer() {
 
 }  // namespace kvm
 
-extern "C" int kvm_profile_enable(int32_t on) {
+static int kvm_profile_enable_body(int32_t on) {
   using namespace kvm;
   std::lock_guard<std::mutex> g(g_mu);
   g_on = on != 0;
@@ -63,7 +64,13 @@ extern "C" int kvm_profile_enable(int32_t on) {
   return KVM_OK;
 }
 
-extern "C" int kvm_profile_read(kvm_kernel_stat* out, int32_t max, int32_t* n) {
+extern "C" int kvm_profile_enable(int32_t on) {
+  return kvm::guarded([&] {
+    return kvm_profile_enable_body(on);
+  });
+}
+
+static int kvm_profile_read_body(kvm_kernel_stat* out, int32_t max, int32_t* n) {
   using namespace kvm;
   clear_error();
   KVM_CHECK_ARG(n != nullptr && (out != nullptr || max == 0), "null pointer");
@@ -93,4 +100,10 @@ extern "C" int kvm_profile_read(kvm_kernel_stat* out, int32_t max, int32_t* n) {
     out[i].total_ms = g_tot[i].ms;
   }
   return KVM_OK;
+}
+
+extern "C" int kvm_profile_read(kvm_kernel_stat* out, int32_t max, int32_t* n) {
+  return kvm::guarded([&] {
+    return kvm_profile_read_body(out, max, n);
+  });
 }

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void quantize_e4m3_kernel(const T* __restrict_
 
 }  // namespace kvm
 
-extern "C" int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, void* dst,
+static int kvm_quantize_e4m3_body(const void* src, int32_t src_dtype, int64_t n, void* dst,
                                  void* stream) {
   using namespace kvm;
   clear_error();
@@ -58,4 +58,11 @@ extern "C" int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, 
         reinterpret_cast<const uint16_t*>(src), n, reinterpret_cast<uint8_t*>(dst));
   KVM_HIP(hipGetLastError());
   return KVM_OK;
+}
+
+extern "C" int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, void* dst,
+                                 void* stream) {
+  return kvm::guarded([&] {
+    return kvm_quantize_e4m3_body(src, src_dtype, n, dst, stream);
+  });
 }

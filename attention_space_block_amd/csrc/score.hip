@@ -35,6 +35,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <memory>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1090,29 +1092,57 @@ static Plan make_plan(const kvm_dims* d, int32_t dtype, int32_t T, int64_t N, in
   return p;
 }
 
-// Cached per-thread side stream and events for the host-tiled form.
+// Side stream and events of one host-tiled scoring call. Sets are kept per
+// GPU and handed out one per call in progress (taken at the start of a call,
+// returned once its work is queued: later calls queue behind it on the same
+// side stream), so their number is bounded by the calls that overlap.
 struct TiledRes {
   hipStream_t side = nullptr;
   hipEvent_t h2d[2] = {nullptr, nullptr};
   hipEvent_t used[2] = {nullptr, nullptr};
   int device = -1;
 };
-static thread_local TiledRes g_tiled;
+static std::mutex g_tiled_mu;
+static std::vector<TiledRes*> g_tiled_free;
 
-static int tiled_res(TiledRes** out) {
+static int tiled_take(TiledRes** out) {
   int dev;
   KVM_HIP(hipGetDevice(&dev));
-  TiledRes& r = g_tiled;
-  if (r.device != dev) {
-    KVM_HIP(hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking));
-    for (int i = 0; i < 2; ++i) {
-      KVM_HIP(hipEventCreateWithFlags(&r.h2d[i], hipEventDisableTiming));
-      KVM_HIP(hipEventCreateWithFlags(&r.used[i], hipEventDisableTiming));
-    }
-    r.device = dev;
+  {
+    std::lock_guard<std::mutex> g(g_tiled_mu);
+    for (size_t i = 0; i < g_tiled_free.size(); ++i)
+      if (g_tiled_free[i]->device == dev) {
+        *out = g_tiled_free[i];
+        g_tiled_free.erase(g_tiled_free.begin() + (ptrdiff_t)i);
+        return KVM_OK;
+      }
   }
-  *out = &r;
+  std::unique_ptr<TiledRes> r(new TiledRes());
+  auto undo = [&r] {
+    for (int i = 0; i < 2; ++i) {
+      if (r->h2d[i]) (void)hipEventDestroy(r->h2d[i]);
+      if (r->used[i]) (void)hipEventDestroy(r->used[i]);
+    }
+    if (r->side) (void)hipStreamDestroy(r->side);
+  };
+  hipError_t e = hipStreamCreateWithFlags(&r->side, hipStreamNonBlocking);
+  for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+    e = hipEventCreateWithFlags(&r->h2d[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&r->used[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    undo();
+    set_error("host-tiled scoring resources: %s", hipGetErrorString(e));
+    return KVM_EHIP;
+  }
+  r->device = dev;
+  *out = r.release();
   return KVM_OK;
+}
+
+static void tiled_give_back(TiledRes* r) {
+  std::lock_guard<std::mutex> g(g_tiled_mu);
+  g_tiled_free.push_back(r);
 }
 
 template <typename T, int D>
@@ -1150,7 +1180,7 @@ static void stored_pass1(int32_t dtype, int32_t D, const StoredArgs& a, hipStrea
 
 }  // namespace kvm
 
-extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
+static size_t kvm_score_ws_bytes_body(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
                                      int64_t n_blocks, int32_t index_loc, int64_t tile_blocks) {
   using namespace kvm;
   if (check_dims(dims, dtype) || n_q_tokens < 1 || n_blocks < 1) return 0;
@@ -1159,7 +1189,16 @@ extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_
   return p.bytes;
 }
 
-extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q,
+extern "C" size_t kvm_score_ws_bytes(const kvm_dims* dims, int32_t dtype, int32_t n_q_tokens,
+                                     int64_t n_blocks, int32_t index_loc, int64_t tile_blocks) {
+  try {
+    return kvm_score_ws_bytes_body(dims, dtype, n_q_tokens, n_blocks, index_loc, tile_blocks);
+  } catch (...) {
+    return 0;
+  }
+}
+
+static int kvm_score_blocks_body(const kvm_dims* dims, int32_t dtype, const void* q,
                                 int32_t n_q_tokens, const void* index, int64_t index_cap_blocks,
                                 int64_t n_blocks, int32_t index_loc, int64_t tile_blocks,
                                 float* scores, void* ws, size_t ws_bytes, void* stream) {
@@ -1305,9 +1344,12 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
     stored_pass1(dtype, D, a, s);
     KVM_HIP(hipGetLastError());
   } else {
-    TiledRes* tr;
-    rc = tiled_res(&tr);
-    if (rc) return rc;
+    TiledRes* tr = nullptr;
+    KVM_TRY(tiled_take(&tr));
+    struct GiveBack {
+      TiledRes* r;
+      ~GiveBack() { tiled_give_back(r); }
+    } give_back{tr};
     const int64_t ntile = (n_blocks + tile_blocks - 1) / tile_blocks;
     const size_t tile_bytes = (size_t)nlg * tile_blocks * D * dtype_bytes(dtype);
     char* stage[2] = {w + p.off_stage, w + p.off_stage + tile_bytes};
@@ -1365,4 +1407,14 @@ extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void*
   }
   KVM_HIP(hipGetLastError());
   return KVM_OK;
+}
+
+extern "C" int kvm_score_blocks(const kvm_dims* dims, int32_t dtype, const void* q,
+                                int32_t n_q_tokens, const void* index, int64_t index_cap_blocks,
+                                int64_t n_blocks, int32_t index_loc, int64_t tile_blocks,
+                                float* scores, void* ws, size_t ws_bytes, void* stream) {
+  return kvm::guarded([&] {
+    return kvm_score_blocks_body(dims, dtype, q, n_q_tokens, index, index_cap_blocks, n_blocks,
+                                 index_loc, tile_blocks, scores, ws, ws_bytes, stream);
+  });
 }

@@ -354,12 +354,14 @@ extern "C" size_t kvm_select_ws_bytes(int64_t n_blocks) {
   return kvm::sel_ws_bytes(n_blocks > 0 ? n_blocks : 1);
 }
 
-extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
-                          int32_t budget_blocks, int32_t block_tokens, int32_t* sel,
-                          int32_t* n_sel, int32_t* base_pos, void* ws, size_t ws_bytes,
-                          void* stream) {
-  using namespace kvm;
-  clear_error();
+
+namespace kvm {
+namespace {
+
+// Argument checks shared by both entry points (no device work).
+int select_check(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
+                 int32_t budget_blocks, int32_t block_tokens, int32_t* sel, int32_t* n_sel,
+                 int32_t* base_pos) {
   KVM_CHECK_ARG(scores && sel && n_sel && base_pos, "null pointer");
   KVM_CHECK_ARG(n_blocks >= 1 && n_blocks < 0x7fffffffLL, "n_blocks out of range");
   KVM_CHECK_ARG(n_sink >= 0 && n_recent >= 0 && budget_blocks >= 1 && block_tokens >= 1,
@@ -374,21 +376,22 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
   KVM_CHECK_RANGE(sel, out_bytes, RANGE_DEVICE, "sel");
   KVM_CHECK_RANGE(base_pos, out_bytes, RANGE_DEVICE, "base_pos");
   KVM_CHECK_RANGE(n_sel, sizeof(int32_t), RANGE_DEVICE, "n_sel");
-  hipStream_t s = as_stream(stream);
+  return KVM_OK;
+}
+
+// The launches of one selection; `ws` holds at least sel_ws_bytes(n_blocks)
+// bytes of device memory (unused when n_blocks <= budget_blocks). sel_init
+// clears the control words and histograms, so `ws` needs no clearing.
+int select_launch(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
+                  int32_t budget_blocks, int32_t block_tokens, int32_t* sel, int32_t* n_sel,
+                  int32_t* base_pos, void* ws, hipStream_t s, bool timed) {
   if (n_blocks <= budget_blocks) {
-    KernelTimer tm("select", s);
+    KernelTimer tm(timed ? "select" : nullptr, s);
     select_all_kernel<<<1, 1024, 0, s>>>(scores, n_blocks, block_tokens, sel, n_sel, base_pos);
     KVM_HIP(hipGetLastError());
     return KVM_OK;
   }
-  const size_t need = sel_ws_bytes(n_blocks);
-  if (!ws || ws_bytes < need) {
-    set_error("select workspace %zu < %zu bytes", ws_bytes, need);
-    return KVM_ENOMEM;
-  }
-  KVM_CHECK_ARG((uintptr_t)ws % 256 == 0, "ws must be 256-byte aligned");
-  KVM_CHECK_RANGE(ws, need, RANGE_DEVICE, "ws");
-  KernelTimer tm("select", s);
+  KernelTimer tm(timed ? "select" : nullptr, s);
   const SelWs w = sel_ws(ws);
   const int64_t nwg = sel_nwg(n_blocks);
   const int64_t c0 = n_sink, c1 = n_blocks - n_recent;
@@ -406,4 +409,31 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
                                                               budget_blocks, sel, n_sel, base_pos);
   KVM_HIP(hipGetLastError());
   return KVM_OK;
+}
+
+}  // namespace
+}  // namespace kvm
+
+extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
+                          int32_t budget_blocks, int32_t block_tokens, int32_t* sel,
+                          int32_t* n_sel, int32_t* base_pos, void* ws, size_t ws_bytes,
+                          void* stream) {
+  using namespace kvm;
+  return guarded([&]() -> int {
+    clear_error();
+    int rc = select_check(scores, n_blocks, n_sink, n_recent, budget_blocks, block_tokens, sel,
+                          n_sel, base_pos);
+    if (rc) return rc;
+    if (n_blocks > budget_blocks) {
+      const size_t need = sel_ws_bytes(n_blocks);
+      if (!ws || ws_bytes < need) {
+        set_error("select workspace %zu < %zu bytes", ws_bytes, need);
+        return KVM_ENOMEM;
+      }
+      KVM_CHECK_ARG((uintptr_t)ws % 256 == 0, "ws must be 256-byte aligned");
+      KVM_CHECK_RANGE(ws, need, RANGE_DEVICE, "ws");
+    }
+    return select_launch(scores, n_blocks, n_sink, n_recent, budget_blocks, block_tokens, sel,
+                         n_sel, base_pos, ws, as_stream(stream), true);
+  });
 }

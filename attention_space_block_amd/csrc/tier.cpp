@@ -12,7 +12,7 @@
 #include <utility>
 #include <vector>
 
-#include "common.hpp"
+#include "host_common.hpp"
 
 namespace kvm {
 namespace {
@@ -82,7 +82,7 @@ int check_csr(int32_t n_steps, const int64_t* off, const int32_t* blk, int32_t* 
 }  // namespace
 }  // namespace kvm
 
-extern "C" int kvm_tier_simulate(const kvm_tier_policy* pol, int32_t n_steps,
+static int kvm_tier_simulate_body(const kvm_tier_policy* pol, int32_t n_steps,
                                  const int64_t* new_off, const int32_t* new_blk,
                                  const int64_t* sel_off, const int32_t* sel_blk,
                                  const int64_t* miss_off, const int32_t* miss_blk, int32_t* out) {
@@ -131,4 +131,14 @@ extern "C" int kvm_tier_simulate(const kvm_tier_policy* pol, int32_t n_steps,
     out[3 * t + 2] = dem;
   }
   return KVM_OK;
+}
+
+extern "C" int kvm_tier_simulate(const kvm_tier_policy* pol, int32_t n_steps,
+                                 const int64_t* new_off, const int32_t* new_blk,
+                                 const int64_t* sel_off, const int32_t* sel_blk,
+                                 const int64_t* miss_off, const int32_t* miss_blk, int32_t* out) {
+  return kvm::guarded([&] {
+    return kvm_tier_simulate_body(pol, n_steps, new_off, new_blk, sel_off, sel_blk, miss_off,
+                                  miss_blk, out);
+  });
 }

@@ -24,7 +24,8 @@
  *  - Return value: KVM_OK or a negative kvm_status. Argument validation is
  *    synchronous and leaves outputs untouched. HIP errors return KVM_EHIP;
  *    the text is in kvm_last_error() (thread-local). No C++ exception crosses
- *    this interface.
+ *    this interface: every entry point catches them; host allocation and
+ *    thread-creation failures return KVM_ENOMEM, anything else KVM_EINTERNAL.
  *  - Element types: KVM_F32 (IEEE binary32), KVM_BF16 (bfloat16 bit patterns)
  *    or KVM_FP8_E4M3 (OCP FP8 E4M3FN bytes: bias 7, 3 mantissa bits, largest
  *    finite 448, no infinities; the KV-cache format the pages' engine runs).
@@ -57,7 +58,10 @@ typedef enum {
   KVM_EHIP = -3,    /* a HIP runtime call failed; see kvm_last_error() */
   KVM_ERANGE = -4,  /* budget < sink + recent, block id out of range, block
                        without a source, NaN or negative score */
-  KVM_ENOTSUP = -5  /* valid but unsupported combination (dtype, head_dim) */
+  KVM_ENOTSUP = -5, /* valid but unsupported combination (dtype, head_dim) */
+  KVM_EINTERNAL = -6 /* unexpected host-side failure inside the library (an
+                        exception other than memory or thread exhaustion,
+                        which are KVM_ENOMEM); see kvm_last_error() */
 } kvm_status;
 
 typedef enum { KVM_F32 = 0, KVM_BF16 = 1, KVM_FP8_E4M3 = 2 } kvm_dtype;
@@ -76,7 +80,7 @@ typedef struct {
   int32_t block_tokens; /* B: tokens per logical block (32) */
 } kvm_dims;
 
-/* Version of this interface (major*100 + minor). */
+/* Version of this interface (major*100 + minor): 101. */
 int kvm_version(void);
 
 /* Text of the last error on the calling thread ("" if none). */

@@ -913,3 +913,100 @@ def test_device_backed_page_released_when_source_changes(k, dev):
     assert st["misses"] == 1 and st["hits"] == 10
     gc.check_view(wl, sel.cpu().numpy(), pool.page.cpu().numpy()[:11], pool)
     pool.ctx.close()
+
+
+# ----------------------------------- bounded pool: registration, rollback ----
+
+def _state(pool, blocks):
+    return {int(b): tuple(pool.ctx.kvm_ctx_block_state(int(b))) for b in blocks}
+
+
+def test_register_never_takes_pages_of_the_current_view(k, dev):
+    """A tight pool (the view plus three pages): freshly prefilled blocks take
+    free pages or pages of blocks outside the current view and never a page
+    of the view (KVMem Sec. 4.4); with only view pages left the registration
+    fails with KVM_ENOMEM and changes nothing. Hits, misses and evictions
+    follow the oracle's page-pool model; every view page holds its block."""
+    import torch
+    from oracle import PagePool
+    wl = synth.get_workload("tiny")
+    N, n_slots = 128, 14
+    pool, keep = _remat_setup(k, dev, wl, N, n_slots)
+    rk, rv = keep
+    model = PagePool(n_slots)
+
+    def update(blocks):
+        sel = torch.tensor(blocks, dtype=torch.int32, device=dev)
+        n_sel = torch.tensor([len(blocks)], dtype=torch.int32, device=dev)
+        st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+        torch.cuda.synchronize()
+        r = model.update(blocks)
+        assert (st["hits"], st["misses"], st["evicted"]) == (
+            len(r["hits"]), len(r["misses"]), len(r["evicted"]))
+        gc.check_view(wl, np.array(blocks), pool.page.cpu().numpy()[:len(blocks)], pool)
+        return sel, n_sel
+
+    def register(b):
+        pool.ctx.kvm_ctx_register_resident(b, 1, rk[b], rv[b], wl.block_bytes)
+        torch.cuda.synchronize()
+        model.register([b])
+
+    view1 = list(range(0, 11))
+    update(view1)
+    for b in (100, 101, 102):                       # the three free pages
+        register(b)
+    before = _state(pool, range(N))
+    with pytest.raises(k.KvmError) as e:             # only pages of the current view remain
+        pool.ctx.kvm_ctx_register_resident(103, 1, rk[103], rv[103], wl.block_bytes)
+    assert e.value.code == k.api._abi.KVM_ENOMEM
+    assert _state(pool, range(N)) == before
+    gc.check_view(wl, np.array(view1), pool.page.cpu().numpy()[:11], pool)
+    view2 = [0, 1, 3, 5, 7, 9, 100, 110, 111, 126, 127]
+    update(view2)                                   # 2, 4, ... 101, 102 leave the view
+    for b in (103, 104):                            # LRU pages outside the view
+        register(b)
+    resident = {b for b in range(N) if pool.ctx.kvm_ctx_block_state(b)[0] >= 0}
+    assert resident == model.resident
+    gc.check_view(wl, np.array(view2), pool.page.cpu().numpy()[:11], pool)
+    update([0, 1, 3, 103, 104, 110, 111, 120, 121, 126, 127])
+    pool.ctx.close()
+
+
+def test_failed_gather_rolls_back_and_a_retry_is_exact(k, dev):
+    """The gather callback fails on the second staging batch: the call returns
+    an error after the first batch was queued. Blocks whose pages were
+    completed stay resident; the others are released. Retrying the same
+    selection stages only the released blocks, and every page of the view
+    matches the oracle (K re-RoPE'd, V bit-exact)."""
+    import ctypes
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, budget_blocks=96, n_recent=8)
+    N = 400
+    pool = gc.Pool(k, wl, 130, N, wl.budget_blocks * wl.block_tokens, dev, 16, 32)
+    R = synth.scores_f32(21, N)
+    sel, n_sel, base = gc.select_dev(k, gc.to_dev(R, dev), N, wl.n_sink, wl.n_recent,
+                                     wl.budget_blocks, dev)
+    s = sel.cpu().numpy()[:96]
+    bad = {int(b) for b in s[16:32]}                 # the second batch of 16
+    fail = [True]
+
+    def gather(block, which, dst):
+        if fail[0] and block in bad:
+            return 1
+        buf = (ctypes.c_char * wl.block_bytes).from_address(dst)
+        arr = np.frombuffer(buf, dtype=gc.np_elem(wl))
+        synth.kv_blocks(wl, "K" if which == 0 else "V", block, 1, out=arr, nthreads=1)
+        return 0
+    pool.ctx.kvm_ctx_set_gather(0, N, gather)
+    with pytest.raises(k.KvmError) as e:
+        pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    assert e.value.code == k.api._abi.KVM_ERANGE
+    torch.cuda.synchronize()
+    resident = [pool.ctx.kvm_ctx_block_state(int(b))[0] >= 0 for b in s]
+    assert all(resident[:16]) and not any(resident[16:])
+    fail[0] = False
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    assert st["hits"] == 16 and st["misses"] == 80
+    gc.check_view(wl, s, pool.page.cpu().numpy()[:96], pool)
+    pool.ctx.close()

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import compact_positions
+from oracle import compact_positions, select_blocks
 from oracle.pipeline import as_f64
 from tests import gpu_common as gc
 
@@ -64,34 +64,48 @@ def test_ws1m_full_step(k, dev):
     n = int(n_sel.item())
     s = sel.cpu().numpy()[:n]
     assert n == wl.budget_blocks
+    # bit-exact against the oracle's selector on the same fp32 scores
+    assert np.array_equal(s, select_blocks(R, wl.n_sink, wl.n_recent, wl.budget_blocks))
     if float(g["margin"]) > 2e-5:
         assert np.array_equal(s, g["sel"])
     nband = gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
     say("blocks within the cutoff band", nband)
     assert np.array_equal(base.cpu().numpy()[:n], compact_positions(n))
     del index
-    say("ws1m: rematerializing (half resident, half from HBM sources)")
+    say("ws1m: rematerializing (half resident, half fetched H2D from pinned host memory)")
     hits, misses = s[0::2], s[1::2]
     pool = gc.Pool(k, wl, n + 64, N, (n + wl.reserve_blocks) * B, dev)
     hk = gc.raw_blocks_to_device(wl, "K", hits, dev)
     hv = gc.raw_blocks_to_device(wl, "V", hits, dev)
     for i, b in enumerate(hits):
         pool.ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv[i], wl.block_bytes)
+    torch.cuda.synchronize()
     del hk, hv
-    mk = gc.raw_blocks_to_device(wl, "K", misses, dev)
-    mv = gc.raw_blocks_to_device(wl, "V", misses, dev)
+    # the lower tier of the other half: raw K and V in pinned host memory
+    mk = torch.empty((len(misses), wl.block_elems), dtype=torch.int16).pin_memory()
+    mv = torch.empty((len(misses), wl.block_elems), dtype=torch.int16).pin_memory()
+    for t, which in ((mk, "K"), (mv, "V")):
+        view = t.numpy().view(np.uint16)
+        for i, b in enumerate(misses):
+            synth.kv_blocks(wl, which, int(b), 1, out=view[i:i + 1])
     for i, b in enumerate(misses):
-        pool.ctx.kvm_ctx_set_source(int(b), 1, mk[i], mv[i], wl.block_bytes, k.KVM_SRC_DEVICE)
+        pool.ctx.kvm_ctx_set_source(int(b), 1, mk[i], mv[i], wl.block_bytes,
+                                    k.KVM_SRC_HOST_PINNED)
     st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
     torch.cuda.synchronize()
+    pool.ctx.kvm_ctx_sync()
+    say(f"remat stats {st}")
     assert st["hits"] == len(hits) and st["misses"] == len(misses) and st["rotated"] == n
+    assert st["h2d_bytes"] == 2 * len(misses) * wl.block_bytes
     pg = pool.page.cpu().numpy()[:n]
     assert len(set(pg.tolist())) == n
     rng = np.random.default_rng(3)
-    check = sorted(set(rng.choice(n, 24, replace=False).tolist()) | {0, n - 1})
+    check = sorted(set(rng.choice(n, 24, replace=False).tolist()) | {0, 1, n - 2, n - 1})
     worst = gc.check_view(wl, s, pg, pool, blocks=check)
     say("worst K error", worst)
     pool.ctx.close()
+    del mk, mv
+    torch._C._host_emptyCache()       # give the 16 GiB of pinned memory back
 
 
 @pytest.mark.timeout(600)
@@ -126,6 +140,8 @@ def test_ws10m_scores_resident_match_oracle(k, dev):
     n = int(n_sel.item())
     assert n == wl.budget_blocks
     s = sel.cpu().numpy()[:n]
+    assert np.array_equal(s, select_blocks(res.astype(np.float64), wl.n_sink, wl.n_recent,
+                                           wl.budget_blocks))
     if float(g["margin"]) > 2e-5:
         assert np.array_equal(s, g["sel"])
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
@@ -171,6 +187,8 @@ def test_ws10m_scores_resident_and_host_tiled(k, dev):
     n = int(n_sel.item())
     assert n == wl.budget_blocks
     s = sel.cpu().numpy()[:n]
+    assert np.array_equal(s, select_blocks(res.astype(np.float64), wl.n_sink, wl.n_recent,
+                                           wl.budget_blocks))
     if float(g["margin"]) > 2e-5:
         assert np.array_equal(s, g["sel"])
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
