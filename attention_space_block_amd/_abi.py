@@ -21,7 +21,7 @@ KVM_TIER_LRU, KVM_TIER_LRFU = 0, 1
 
 EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
-    "kvm_select_ws_bytes", "kvm_select", "kvm_ctx_create", "kvm_ctx_destroy",
+    "kvm_select_ws_bytes", "kvm_select", "kvm_select_noalloc", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
     "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
     "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_quantize_e4m3",
@@ -96,6 +96,7 @@ def lib():
                                                 vp, sz, vp]),
             "kvm_select_ws_bytes": (sz, [i64]),
             "kvm_select": (ctypes.c_int, [f32p, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]),
+            "kvm_select_noalloc": (ctypes.c_int, [f32p, i64, i32, i32, i32, i32, vp, vp, vp, vp]),
             "kvm_ctx_create": (ctypes.c_int, [ctypes.POINTER(CtxDesc), ctypes.POINTER(vp)]),
             "kvm_ctx_destroy": (None, [vp]),
             "kvm_ctx_set_source": (ctypes.c_int, [vp, i64, i64, vp, vp, i64, i32]),

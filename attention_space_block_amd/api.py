@@ -83,6 +83,14 @@ def kvm_select(scores, n_blocks: int, n_sink: int, n_recent: int, budget_blocks:
     _abi.check(rc, "kvm_select")
 
 
+def kvm_select_noalloc(scores, n_blocks: int, n_sink: int, n_recent: int, budget_blocks: int,
+                       block_tokens: int, sel, n_sel, base_pos, stream=None) -> None:
+    rc = _abi.lib().kvm_select_noalloc(_ptr(scores), n_blocks, n_sink, n_recent, budget_blocks,
+                                       block_tokens, _ptr(sel), _ptr(n_sel), _ptr(base_pos),
+                                       _stream(stream))
+    _abi.check(rc, "kvm_select_noalloc")
+
+
 def kvm_tier_simulate(policy: int, host_blocks: int, lam: float, steps) -> list:
     """Host-tier admission over a trace; steps = [(new, sel, miss), ...], each an
     ascending list of block ids. Returns [(host_hits, nvme_reads, demotions)]."""

@@ -28,6 +28,7 @@
 //     output is ascending without a sort.
 // With n_blocks <= budget every block is selected (select_all_kernel).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "profile.hpp"
@@ -411,6 +412,37 @@ int select_launch(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t
   return KVM_OK;
 }
 
+// Workspace of kvm_select_noalloc: one array per GPU, held until the process
+// ends. Host code must use the address hipGetSymbolAddress returns for the
+// current device (select_scratch), never the array's name.
+static __device__ __align__(256) unsigned char scratch[KVM_SELECT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current GPU (looked up once per GPU).
+int select_scratch(void** out) {
+  int dev = -1;
+  KVM_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    set_error("device %d outside the scratch table (%d devices)", dev, MAX_DEVICES);
+    return KVM_ENOTSUP;
+  }
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    KVM_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) {
+      set_error("hipGetSymbolAddress returned no address for the select scratch");
+      return KVM_EHIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KVM_OK;
+}
+
 }  // namespace
 }  // namespace kvm
 
@@ -435,5 +467,29 @@ extern "C" int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink,
     }
     return select_launch(scores, n_blocks, n_sink, n_recent, budget_blocks, block_tokens, sel,
                          n_sel, base_pos, ws, as_stream(stream), true);
+  });
+}
+
+extern "C" int kvm_select_noalloc(const float* scores, int64_t n_blocks, int32_t n_sink,
+                                  int32_t n_recent, int32_t budget_blocks, int32_t block_tokens,
+                                  int32_t* sel, int32_t* n_sel, int32_t* base_pos, void* stream) {
+  using namespace kvm;
+  return guarded([&]() -> int {
+    clear_error();
+    if (n_blocks > KVM_SELECT_NOALLOC_MAX_BLOCKS) {
+      set_error("n_blocks %lld exceeds the %lld blocks the built-in select scratch covers",
+                (long long)n_blocks, (long long)KVM_SELECT_NOALLOC_MAX_BLOCKS);
+      return KVM_ENOMEM;
+    }
+    int rc = select_check(scores, n_blocks, n_sink, n_recent, budget_blocks, block_tokens, sel,
+                          n_sel, base_pos);
+    if (rc) return rc;
+    void* ws = nullptr;
+    if (n_blocks > budget_blocks) {
+      rc = select_scratch(&ws);
+      if (rc) return rc;
+    }
+    return select_launch(scores, n_blocks, n_sink, n_recent, budget_blocks, block_tokens, sel,
+                         n_sel, base_pos, ws, as_stream(stream), false);
   });
 }

@@ -184,6 +184,25 @@ int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_
                int32_t budget_blocks, int32_t block_tokens, int32_t* sel, int32_t* n_sel,
                int32_t* base_pos, void* ws, size_t ws_bytes, void* stream);
 
+/* kvm_select without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, results and errors as kvm_select,
+ * minus ws/ws_bytes: the selection's scratch (control words, digit
+ * histograms, per-chunk counts) is a fixed array of
+ * KVM_SELECT_NOALLOC_SCRATCH_BYTES in the library's device code, one per GPU,
+ * held until the process ends, so n_blocks is limited to
+ * KVM_SELECT_NOALLOC_MAX_BLOCKS (larger: KVM_ENOMEM, nothing enqueued). The
+ * call allocates nothing. Every call on one GPU shares that GPU's array (the
+ * kernels reset what must start at zero): calls that overlap on one GPU, on
+ * different streams or threads, race and give undefined selections; order
+ * them on one stream. Not timed by kvm_profile_*. */
+#define KVM_SELECT_NOALLOC_SCRATCH_BYTES 65536
+#define KVM_SELECT_NOALLOC_MAX_BLOCKS 31326208LL   /* 7648 chunks of 4096 blocks */
+
+int kvm_select_noalloc(const float* scores, int64_t n_blocks, int32_t n_sink,
+                       int32_t n_recent, int32_t budget_blocks, int32_t block_tokens,
+                       int32_t* sel, int32_t* n_sel, int32_t* base_pos, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Working-set context: block records, the bounded GPU page pool and the
  * rematerialization data plane (KVMem Sec. 4.4, Sec. 5, Fig. 3).
