@@ -147,12 +147,16 @@ def test_ws10m_scores_resident_match_oracle(k, dev):
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
 
 
-@pytest.mark.skip(reason="with this test earlier in the same process, the next kvm_ctx_create "
-                         "ended in a host segmentation fault (after 41 GB of pinned host "
-                         "memory for the tiled index); the cause is not found, so the test "
-                         "stays off until it is")
+@pytest.mark.skipif(not os.environ.get("KVM_HOST_TILED_10M_ALONE"),
+                    reason="runs only alone in its own process (KVM_HOST_TILED_10M_ALONE=1): "
+                           "with it earlier in the same process a later kvm_ctx_create once "
+                           "ended in a host segmentation fault whose cause is not found")
 @pytest.mark.timeout(600)
 def test_ws10m_scores_resident_and_host_tiled(k, dev):
+    """KVMem Sec. 5: scoring with the index streamed from pinned host memory in
+    64 MiB tiles (611 tiles at 10M tokens) keeps the global softmax, so it
+    equals scoring the resident index: bit-identical here, and within 1e-5 of
+    the oracle."""
     import torch
     g = golden("ws10m")
     wl = synth.get_workload("ws10m")
@@ -192,3 +196,5 @@ def test_ws10m_scores_resident_and_host_tiled(k, dev):
     if float(g["margin"]) > 2e-5:
         assert np.array_equal(s, g["sel"])
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
+    del host, hv
+    torch._C._host_emptyCache()
