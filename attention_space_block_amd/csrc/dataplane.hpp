@@ -38,8 +38,9 @@ class Engine {
   virtual int wait(int stream, int event) = 0;         // `stream` waits for `event`
   virtual int host_wait(int event) = 0;                // the host waits for `event`
   virtual int sync_all() = 0;                          // the host waits for all three streams
-  // Remat kernel over jobs [first, first + n) of the device job list, on MAIN.
-  virtual int launch(int32_t first, int32_t n, bool delta) = 0;
+  // Remat kernel over jobs [first, first + n) of the device job list, on MAIN;
+  // jobs that copy V (JOB_COPY_V) only in launches with copy_v.
+  virtual int launch(int32_t first, int32_t n, bool delta, bool copy_v) = 0;
 };
 
 // Host workers that run the gather callbacks of one batch concurrently.

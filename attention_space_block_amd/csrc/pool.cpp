@@ -279,6 +279,7 @@ int BlockPool::plan(const int32_t* sel, int32_t n, RematPlan* p) {
         p->undo.push_back(undo[j]);
         ++count[k];
       }
+  p->n_reencode = count[JK_REENCODE];
   p->n_full = count[JK_REENCODE] + count[JK_DEVICE_MISS];
   p->n_delta = count[JK_DELTA];
   p->n_dma = count[JK_DMA];

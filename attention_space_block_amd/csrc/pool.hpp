@@ -85,6 +85,7 @@ struct RematPlan {
   std::vector<int64_t> job_block;      // block of each job
   std::vector<int8_t> job_kind;        // JobKind of each job
   int32_t n_full = 0, n_delta = 0, n_dma = 0, n_gather = 0;
+  int32_t n_reencode = 0;              // the first n_full jobs: re-encodes, then device misses
   std::vector<int32_t> page;           // page table [n]
   kvm_remat_stats st{};
   struct Undo {
@@ -131,8 +132,9 @@ class BlockPool {
   // jobs [0, done) completed, jobs [done, done + unknown) may or may not have
   // run, the rest never started. Hits whose page was not written get their
   // old record back; hits whose page may have been written are marked stale
-  // (or, in delta mode, due for a rebuild from raw K); misses and staged
-  // blocks that did not complete lose their page.
+  // (their raw K is intact), or in delta mode, where the page itself was
+  // being rotated, lose their page; misses and staged blocks that did not
+  // complete lose their page.
   void rollback(const RematPlan& p, int32_t done, int32_t unknown);
 
  private:

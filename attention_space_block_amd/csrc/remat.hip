@@ -117,7 +117,7 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
 // LAYOUT 1 (pairs (t, t+d/2)): pieces [t0, t0+P) and [t0+d/2, t0+d/2+P).
 // All loads of a workgroup's rows are issued before the first store; loads and
 // stores are plain (cached) ones, faster here than the non-temporal forms.
-template <typename T, int D, int LAYOUT, bool DELTA>
+template <typename T, int D, int LAYOUT, bool DELTA, bool COPYV>
 __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
   constexpr int TPR = D / (2 * P);               // threads per row
@@ -154,7 +154,9 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   }
   const int64_t page = (int64_t)job.slot * a.page_bytes;
   const int64_t row0 = (int64_t)wpart * ROWS;
-  const bool copyv = (job.flags & JOB_COPY_V) != 0;
+  // launches of K-only jobs compile the V copy out (fewer registers, more
+  // waves per SIMD); launches that may copy V test each job's flag
+  const bool copyv = COPYV && (job.flags & JOB_COPY_V) != 0;
   uint4 k0[NR], k1[NR], v0[NR], v1[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   }
 }
 
-static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta,
+static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, bool copy_v,
                          const RematArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.n_jobs * a.wg_per_job;
   if (grid <= 0) return;
@@ -212,8 +214,9 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta,
   KernelTimer tm("remat", s);
 #define KVM_REMAT(T, D, LAY)                                                 \
   do {                                                                       \
-    if (delta) remat_kernel<T, D, LAY, true><<<g, b, 0, s>>>(a);             \
-    else remat_kernel<T, D, LAY, false><<<g, b, 0, s>>>(a);                  \
+    if (delta) remat_kernel<T, D, LAY, true, false><<<g, b, 0, s>>>(a);      \
+    else if (copy_v) remat_kernel<T, D, LAY, false, true><<<g, b, 0, s>>>(a); \
+    else remat_kernel<T, D, LAY, false, false><<<g, b, 0, s>>>(a);          \
   } while (0)
   if (dtype == KVM_FP8_E4M3) {
     if (d == 128) { if (layout == 0) KVM_REMAT(uint8_t, 128, 0); else KVM_REMAT(uint8_t, 128, 1); }
@@ -327,12 +330,12 @@ class HipEngine final : public Engine {
     const hipError_t v = hipStreamSynchronize(c_->side_v);
     return a == hipSuccess && b == hipSuccess && v == hipSuccess ? KVM_OK : KVM_EHIP;
   }
-  int launch(int32_t first, int32_t n, bool delta) override {
+  int launch(int32_t first, int32_t n, bool delta, bool copy_v) override {
     RematArgs a = a_;
     a.jobs = c_->d_jobs + first;
     a.n_jobs = n;
     const kvm_dims& dm = c_->d.dims;
-    launch_remat(c_->d.dtype, dm.head_dim, c_->d.rope_layout, delta, a, s_);
+    launch_remat(c_->d.dtype, dm.head_dim, c_->d.rope_layout, delta, copy_v, a, s_);
     KVM_HIP(hipGetLastError());
     return KVM_OK;
   }

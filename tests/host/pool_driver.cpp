@@ -92,6 +92,7 @@ struct Op {
   uint64_t rid = 0;        // RECORD: its id; WAIT: the record it waits for (0: none)
   int32_t first = 0, n = 0;
   bool delta = false;
+  bool copy_v = false;      // LAUNCH: the launch may copy V
   std::vector<RematJob> jobs;   // UPLOAD: the job list as queued
   std::function<void()> call;   // CALL: the caller's later work on MAIN
 };
@@ -160,7 +161,7 @@ class FakeEngine final : public Engine {
       }
     return KVM_OK;
   }
-  int launch(int32_t first, int32_t n, bool delta) override {
+  int launch(int32_t first, int32_t n, bool delta, bool copy_v) override {
     if (fail_launch > 0 && --fail_launch == 0) {
       set_error("injected launch failure");
       return KVM_EHIP;
@@ -170,6 +171,7 @@ class FakeEngine final : public Engine {
     o.first = first;
     o.n = n;
     o.delta = delta;
+    o.copy_v = copy_v;
     push(MAIN, std::move(o));
     return KVM_OK;
   }
@@ -268,7 +270,7 @@ class FakeEngine final : public Engine {
         memcpy(o.dst, o.src, o.bytes);
         break;
       case Op::LAUNCH:
-        for (int32_t j = o.first; j < o.first + o.n; ++j) kernel(dev_jobs_.at((size_t)j), o.delta);
+        for (int32_t j = o.first; j < o.first + o.n; ++j) kernel(dev_jobs_.at((size_t)j), o.delta, o.copy_v);
         break;
     }
   }
@@ -280,7 +282,8 @@ class FakeEngine final : public Engine {
     return false;
   }
   // The remat kernel on tagged pages.
-  void kernel(const RematJob& jb, bool delta) {
+  void kernel(const RematJob& jb, bool delta, bool copy_v) {
+    if ((jb.flags & JOB_COPY_V) && !copy_v) error("a job that copies V in a K-only launch");
     char* kv = L_.k_view + (int64_t)jb.slot * PAGE;
     char* vv = L_.v_view + (int64_t)jb.slot * PAGE;
     if (copy_pending_into(jb.src_k, PAGE) || ((jb.flags & JOB_COPY_V) && copy_pending_into(jb.src_v, PAGE)))
