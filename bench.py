@@ -869,7 +869,9 @@ def write_traffic_profile(value_dir: str, delta_dir: str, out_path: str) -> dict
     dl = json.load(open(os.path.join(delta_dir, "summary.json")))
     traffic = dict(v["traffic"])
     for k, x in dl["traffic"].items():
-        if k.endswith("true>"):                   # the delta-mode remat kernel
+        # the delta-mode remat kernel: remat_kernel<T, D, LAYOUT, DELTA = true, COPYV>
+        args = k.split("<", 1)[-1].rstrip(">").split(", ")
+        if k.startswith("kvm::remat_kernel") and len(args) > 3 and args[3] == "true":
             traffic[k] = x
     per = {}
     for k, x in traffic.items():
