@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--pcie-steps", type=int, default=2,
+    ap.add_argument("--pcie-steps", type=int, default=3,
                     help="steps of the pinned-host leg (0 to skip)")
     ap.add_argument("--delta-steps", type=int, default=4,
                     help="rematerializations timed in bounded delta re-RoPE mode (0: skip)")
@@ -1048,8 +1048,10 @@ def main():
         run(1, False)          # untimed: the first DMA from the pinned store pays one-time costs
         ptimes, pst = run(args.pcie_steps, False)
         pms = 1e3 * sum(ptimes) / len(ptimes)
+        log("pcie leg steps (ms): " + ", ".join(f"{1e3 * t:.1f}" for t in ptimes))
         rc_s = timed_remat_call(k, ws)
         pcie = {"ms_per_step": pms, "blocks_per_s": N / (pms * 1e-3),
+                "step_ms": [1e3 * t for t in ptimes],
                 "remat_call_ms": rc_s * 1e3,
                 "delivered_view_GBps": view_bytes(ws) / rc_s / 1e9,
                 "h2d_bytes": pst["h2d_bytes"], "batches": pst["batches"],
