@@ -34,6 +34,11 @@ if ROOT not in sys.path:
 METRIC = ("history blocks scored/s + rematerialized KV GB/s (fraction of HBM peak), 1M-tok")
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# VALU issue bound of a score pass: per score element one fused scale-and-shift,
+# one v_exp_f32 (half the fp32 issue rate, measured 1.4e13/s over the chip) and
+# one add, i.e. 4 wave issue slots of 4 cycles per 64 elements on each of the
+# 1024 SIMDs at 2.4 GHz: 1024 * 2.4e9 * 64 / 16 score elements per second.
+VALU_SCORE_PEAK_GELEMS = 1024 * 2.4e9 * 64 / 16 / 1e9
 MFMA_FP8_PEAK_TFLOPS = 5000.0
 
 
@@ -977,9 +982,17 @@ def main():
     dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
     roof = roofline(*dom)
     others = [roofline(n, i) for n, i in kern.items() if n != dom[0] and roofline(n, i)]
+    # the score passes against their VALU issue bound (exps and sums of every score)
+    elems = float(L * Hq * T * N)
+    for n_ in ("score_pass1_mfma", "score_pass2_mfma"):
+        if n_ in kern:
+            ach = elems / (kern[n_]["avg_ms"] * 1e-3) / 1e9
+            others.append({"kernel": n_, "bound": "alu", "achieved": ach,
+                           "peak": VALU_SCORE_PEAK_GELEMS, "unit": "Gscores/s",
+                           "frac": ach / VALU_SCORE_PEAK_GELEMS, "traffic": None})
     peaks = measured_peaks(dev)
     for r in [roof] + others:
-        if r is not None:
+        if r is not None and r["bound"] in ("mfma", "hbm"):
             mp = peaks["bf16_gemm_TFLOPs"] if r["bound"] == "mfma" else peaks["hbm_copy_GBps"]
             r["frac_of_measured"] = r["achieved"] / mp
     log(f"measured peaks: {peaks['hbm_copy_GBps']:.0f} GB/s copy, "
