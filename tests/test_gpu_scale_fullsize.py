@@ -9,6 +9,7 @@ import pytest
 
 import synth
 from oracle import compact_positions, select_blocks
+from oracle import pipeline as op
 from oracle.pipeline import as_f64
 from tests import gpu_common as gc
 
@@ -198,3 +199,54 @@ def test_ws10m_scores_resident_and_host_tiled(k, dev):
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
     del host, hv
     torch._C._host_emptyCache()
+
+
+@pytest.mark.timeout(600)
+def test_ws1m_fp8_pages_view(k, dev):
+    """FP8 E4M3 K/V pages (the pages' engine runs an FP8 KV cache, KVMem Sec. 6.1)
+    at the 1M-token view: Mean-K of sampled blocks from FP8 K bit-exact against
+    the oracle, then the 4096-block view of the oracle's bf16 selection with
+    half of it resident and half re-RoPE'd from HBM-resident lower-tier copies;
+    sampled K pages within half an E4M3 spacing of the exact rotation, V
+    byte-exact."""
+    import torch
+    from oracle.numerics import bf16_bits
+    g = golden("ws1m")
+    wl = synth.get_workload("ws1m_fp8")
+    N, B = wl.n_blocks, wl.block_tokens
+    blocks = [int(b) for b in g["sample_blocks"]]
+    raw = gc.raw_blocks_to_device(wl, "K", blocks, dev)
+    idx = torch.zeros((wl.n_layers, wl.n_kv_heads, len(blocks), wl.head_dim), dtype=torch.int16,
+                      device=dev)
+    k.kvm_build_index(k.dims_for(wl), k.KVM_FP8_E4M3, raw, wl.block_bytes, 0, len(blocks), idx,
+                      len(blocks))
+    want = np.concatenate([bf16_bits(op.index_rows(wl, b, 1)) for b in blocks], axis=2)
+    assert np.array_equal(gc.to_host_bits(idx), want)
+    del raw, idx
+    s = g["sel"].astype(np.int64)
+    n = len(s)
+    sel = torch.as_tensor(s.astype(np.int32), device=dev)
+    n_sel = torch.tensor([n], dtype=torch.int32, device=dev)
+    hits, misses = s[0::2], s[1::2]
+    pool = gc.Pool(k, wl, n + 64, N, (n + wl.reserve_blocks) * B, dev)
+    hk = gc.raw_blocks_to_device(wl, "K", hits, dev)
+    hv = gc.raw_blocks_to_device(wl, "V", hits, dev)
+    for i, b in enumerate(hits):
+        pool.ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv[i], wl.block_bytes)
+    torch.cuda.synchronize()
+    del hk, hv
+    mk = gc.raw_blocks_to_device(wl, "K", misses, dev)
+    mv = gc.raw_blocks_to_device(wl, "V", misses, dev)
+    for i, b in enumerate(misses):
+        pool.ctx.kvm_ctx_set_source(int(b), 1, mk[i], mv[i], wl.block_bytes, k.KVM_SRC_DEVICE)
+    st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+    torch.cuda.synchronize()
+    say(f"fp8 remat stats {st}")
+    assert st["hits"] == len(hits) and st["misses"] == len(misses) and st["rotated"] == n
+    pg = pool.page.cpu().numpy()[:n]
+    assert len(set(pg.tolist())) == n
+    rng = np.random.default_rng(4)
+    check = sorted(set(rng.choice(n, 24, replace=False).tolist()) | {0, 1, n - 2, n - 1})
+    worst = gc.check_view(wl, s, pg, pool, blocks=check)
+    say("worst K error", worst)
+    pool.ctx.close()
