@@ -283,7 +283,12 @@ int kvm_ctx_set_gather(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks, kvm_
 /* Register freshly prefilled blocks as GPU-resident (KVMem Sec. 5: new blocks
  * start in their original frame; here their K page is marked stale so the next
  * selection encodes it). Copies raw K and V (device, block stride as above)
- * into free pool pages on `stream`. KVM_ENOMEM if no free page remains. */
+ * into pool pages on `stream`: a free page, else the page of the least recently
+ * used resident block outside the current view (the last selection and the
+ * blocks registered since), ties to the lower block id; a page of the current
+ * view is never taken. All or nothing: KVM_ENOMEM, with nothing changed, when
+ * the blocks do not fit. A block already resident is refreshed in its page.
+ * If a copy cannot be queued, the call's blocks lose their pages (KVM_EHIP). */
 int kvm_ctx_register_resident(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks,
                               const void* k_raw, const void* v_raw, int64_t block_stride,
                               void* stream);
@@ -306,16 +311,22 @@ int kvm_ctx_build_index_rope(kvm_ctx* ctx, const void* k_rope, int64_t block_str
 
 /* Make the execution view for a selection (KVMem Sec. 4.4, Sec. 5, Fig. 3):
  * reads n_sel/sel from the device (one small copy, then waits for `stream`),
- * plans hits / misses / evictions against the pool, stages misses H2D on the
- * side stream in event-tracked batches, and enqueues on `stream` the kernels
- * that write k_view = RoPE(raw K, compact position) for misses and for hits
- * whose position changed, and v_view = raw V for misses. page_table_dev
- * (device int32[n_sel]) receives the pool page of sel[i]. Selected block i
- * occupies positions [i*B, i*B + B). Returns once everything is enqueued;
- * later work on `stream` sees the finished view. stats_host may be NULL.
- * Errors: KVM_ERANGE (selection invalid or a miss without a source; n_sel
- * reported as KVM_ERANGE by kvm_select), KVM_ENOMEM (pool smaller than the
- * view), KVM_EHIP. */
+ * plans hits / misses / evictions against the pool (a miss takes a free page,
+ * else the page of the least recently used resident block outside the new
+ * view, ties to the lower block id), stages misses H2D on the side streams in
+ * event-tracked batches, and enqueues on `stream` the kernels that write
+ * k_view = RoPE(raw K, compact position) for misses and for hits whose
+ * position changed, and v_view = raw V for misses. page_table_dev (device
+ * int32[n_sel]) receives the pool page of sel[i]. Selected block i occupies
+ * positions [i*B, i*B + B). Returns once everything is enqueued; later work on
+ * `stream` sees the finished view. stats_host may be NULL.
+ * Errors: KVM_ERANGE (selection invalid, a miss without a source, or a gather
+ * callback that failed; n_sel reported as KVM_ERANGE by kvm_select), KVM_ENOMEM
+ * (pool smaller than the view), KVM_EHIP, KVM_EINTERNAL. An error after
+ * planning drains the ctx's streams and `stream` and rolls the block records
+ * back: every resident block then holds what its record says (blocks whose
+ * pages were not completed are no longer resident), and a retry with the same
+ * selection stages only what is missing. */
 int kvm_rematerialize(kvm_ctx* ctx, const int32_t* sel_dev, const int32_t* n_sel_dev,
                       int32_t* page_table_dev, kvm_remat_stats* stats_host, void* stream);
 
