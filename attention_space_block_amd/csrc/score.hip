@@ -106,18 +106,21 @@ struct MfmaShape {
     else
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // a stationary operand row from global memory: the lane's pieces of each k-step
+  // an operand row from global memory: the lane's pieces of k-step ks (zero
+  // when !ok, without a load)
+  static __device__ __forceinline__ Op load_op(const char* row, bool ok, int half, int ks) {
+    uint4 u[PPK];
+#pragma unroll
+    for (int j = 0; j < PPK; ++j)
+      u[j] = ok ? *reinterpret_cast<const uint4*>(row + piece(ks, half, j) * 16)
+                : make_uint4(0, 0, 0, 0);
+    return make_op(u);
+  }
+  // a stationary operand row: the lane's pieces of every k-step
   static __device__ __forceinline__ void load_row(const char* row, bool ok, int half,
                                                   Op (&op)[KS]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 u[PPK];
-#pragma unroll
-      for (int j = 0; j < PPK; ++j)
-        u[j] = ok ? *reinterpret_cast<const uint4*>(row + piece(ks, half, j) * 16)
-                  : make_uint4(0, 0, 0, 0);
-      op[ks] = make_op(u);
-    }
+    for (int ks = 0; ks < KS; ++ks) op[ks] = load_op(row, ok, half, ks);
   }
 };
 
@@ -254,15 +257,18 @@ __device__ __forceinline__ float exp_sum16(const f32x16& acc, float scale, float
   return e[0];
 }
 
-// Online (shift, sum-exp) update of one lane's query row with 16 new scores
-// (raw dot products; x = acc * scale). The shift m_run is a running maximum
-// that is refreshed lazily: the 16 exps are taken against the current shift
-// (tsum = exp_sum16(acc, scale, m_run)), and only a lane whose tile sum
-// exceeds 2^32 (a new score more than 32 log2-units above the shift), or that
-// has no shift yet (-inf), or that produced inf/NaN, takes the exact path:
-// tile max, new shift, rescale. Any shift gives the same log-sum-exp, and sums
-// stay below 2^32 per term, so the fp64 running sum loses nothing. A lane that
-// has seen only -inf keeps m = -inf and s = 0.
+// Online (shift, sum-exp) state of one lane's query row. The exps are taken
+// against a running shift m_run (log2 units) that is refreshed lazily: scores
+// are summed against the current shift, and only when a sum is not at most
+// LAZY_MAX (some score more than 64 log2-units above the shift, no shift yet
+// (-inf), or an inf/NaN) are the same scores taken again exactly: tile max, new
+// shift, rescale of the running sum. Any shift gives the same log-sum-exp; a
+// sum that passes the test holds no term above 2^64, so no fp32 exp or partial
+// sum can overflow, and the fp64 running sum keeps every term. A lane that has
+// seen only -inf keeps m = -inf and s = 0.
+static constexpr float LAZY_MAX = 18446744073709551616.0f;   // 2^64
+
+// The exact path for 16 new scores (raw dot products; x = acc * scale).
 __device__ __forceinline__ void lse_exact(const f32x16& acc, float scale, float& m_run,
                                           double& s_run) {
   float mx = acc[0];
@@ -275,27 +281,12 @@ __device__ __forceinline__ void lse_exact(const f32x16& acc, float scale, float&
   m_run = m_new;
 }
 
-__device__ __forceinline__ void lse_commit(const f32x16& acc, float scale, float tsum,
-                                           float& m_run, double& s_run) {
-  if (tsum <= 4294967296.0f) s_run += (double)tsum;
-  else lse_exact(acc, scale, m_run, s_run);
-}
-
+// One lazy update with 16 new scores.
 __device__ __forceinline__ void lse_update(const f32x16& acc, float scale, float& m_run,
                                            double& s_run) {
-  lse_commit(acc, scale, exp_sum16(acc, scale, m_run), m_run, s_run);
-}
-
-// lse_commit of both accumulators, with both tile sums consumed before any
-// branch (a select adds 0 on the exact path, which then starts from the
-// unchanged sum).
-__device__ __forceinline__ void lse_commit2(const f32x16 (&acc)[2], float scale, float ts0,
-                                            float ts1, float (&m_run)[2], double (&s_run)[2]) {
-  const bool ok0 = ts0 <= 4294967296.0f, ok1 = ts1 <= 4294967296.0f;
-  s_run[0] += (double)(ok0 ? ts0 : 0.0f);
-  s_run[1] += (double)(ok1 ? ts1 : 0.0f);
-  if (!ok0) lse_exact(acc[0], scale, m_run[0], s_run[0]);
-  if (!ok1) lse_exact(acc[1], scale, m_run[1], s_run[1]);
+  const float tsum = exp_sum16(acc, scale, m_run);
+  if (tsum <= LAZY_MAX) s_run += (double)tsum;
+  else lse_exact(acc, scale, m_run, s_run);
 }
 
 __device__ __forceinline__ void mask_rows(f32x16 (&acc)[2], int half, int32_t nvalid) {
@@ -379,14 +370,43 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
   uint32_t aoff[S::KS][S::PPK];
   operand_offsets<S>(aoff, half, col);
 
+  // Exact recomputation of subtiles [j0, j1) (j0 >= 0): their scores again,
+  // with the index rows read from global memory straight into the A operand
+  // (the stage buffers may already hold later rows), then the exact update.
+  auto replay = [&](int j0, int j1) {
+    for (int j = j0; j < j1; ++j) {
+      const int32_t r0 = b_begin + 32 * j;
+      const int32_t b = r0 + col;
+      const bool ok = b < b_end;
+      const char* row = kb + (int64_t)(ok ? b : 0) * S::ROW_B;
+      f32x16 acc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const typename S::Op av = S::load_op(row, ok, half, ks);
+        acc[0] = S::mma(av, bq[0][ks], acc[0]);
+        acc[1] = S::mma(av, bq[1][ks], acc[1]);
+      }
+      if (b_end - r0 < 32) mask_rows(acc, half, b_end - r0);
+      lse_exact(acc[0], a.scale, m_run[0], s_run[0]);
+      lse_exact(acc[1], a.scale, m_run[1], s_run[1]);
+    }
+  };
+
   // Software pipeline over 32-block subtiles: while the MFMAs of subtile j
   // run, the wave takes the exps of subtile j-1 (its scores sit in the other
   // accumulator set). ab[j & 1] holds subtile j; before the first subtile the
-  // other set holds -inf scores, which leave (m, s) = (-inf, 0) unchanged.
-  // The order of the updates, and so every rounding, is that of the plain
-  // loop. A stage holds SUB (even) subtiles; the next stage's global loads are
-  // in flight while they are multiplied and reduced.
-  static_assert(S::SUB % 2 == 0, "subtile slots alternate within a stage");
+  // other set holds -inf scores. A stage holds SUB (even) subtiles; the next
+  // stage's global loads are in flight while they are multiplied and reduced.
+  // The exps a stage takes (subtiles 4it-1 .. 4it+2) are summed in fp32
+  // against the shift the stage started with, without a branch; at the end of
+  // the stage the sums enter the fp64 running sums, unless some lane's sum
+  // fails the lazy test (always so in the first stage, where there is no shift
+  // yet): then the wave takes those subtiles again on the exact path.
+  static_assert(S::SUB == 4, "a stage's exps cover subtiles 4it-1 .. 4it+2");
   f32x16 ab[2][2];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -399,17 +419,27 @@ __global__ __launch_bounds__(256, 2) void score_pass1_mfma(Pass1Args a) {
     constexpr int BUF = decltype(bufc)::value;
     const int32_t t0 = b_begin + it * S::TILE;
     if (it + 1 < ntiles) dma_stage(it + 1, std::integral_constant<int, BUF ^ 1>{});
+    float g_sum[2] = {0.0f, 0.0f};
+    const float m0 = m_run[0], m1 = m_run[1];
 #pragma unroll
     for (int sub = 0; sub < S::SUB; ++sub) {
       f32x16 (&cur)[2] = ab[sub & 1];
       f32x16 (&prv)[2] = ab[(sub & 1) ^ 1];
       float t[2][8];
-      const float m0 = m_run[0], m1 = m_run[1];
       mfma_subtile_woven<S>(cur, &lds[BUF][sub * 32 * S::ROW_B], aoff, bq, prv, a.scale,
                             [&](int c, int) { return c ? m1 : m0; }, t, [] {});
-      lse_commit2(prv, a.scale, tree8(t[0]), tree8(t[1]), m_run, s_run);
+      g_sum[0] += tree8(t[0]);
+      g_sum[1] += tree8(t[1]);
+      asm volatile("" : "+v"(g_sum[0]), "+v"(g_sum[1]));   // sum each subtile here
       const int32_t nvalid = b_end - (t0 + 32 * sub);
       if (nvalid < 32) mask_rows(cur, half, nvalid);   // uniform: only a split's last stage
+    }
+    const bool good = g_sum[0] <= LAZY_MAX && g_sum[1] <= LAZY_MAX;
+    if (__builtin_amdgcn_ballot_w64(!good) == 0) {
+      s_run[0] += (double)g_sum[0];
+      s_run[1] += (double)g_sum[1];
+    } else {
+      replay(it > 0 ? 4 * it - 1 : 0, 4 * it + 3);
     }
     wait_dma();
     __syncthreads();
