@@ -413,6 +413,14 @@ def counter_traffic() -> dict:
     return out
 
 
+# Kernels whose counter traffic the bench line reports, as (name, template
+# arguments): remat_kernel<element, head dim, pair layout, delta mode, V copy>
+# for the view (full re-encodes and device misses) and for in-place shifts.
+SCORE_KERNEL_TAIL = "<unsigned short, 128>"
+REMAT_VIEW_KERNEL = ("remat_kernel", "<unsigned short, 128, 0, false, true>")
+REMAT_DELTA_KERNEL = ("remat_kernel", "<unsigned short, 128, 0, true, false>")
+
+
 def traffic_for(traffic: dict, short: str, tail: str | None = None):
     for name, val in traffic.items():
         if name.split("<")[0].endswith(short) and (tail is None or name.endswith(tail)):
@@ -972,11 +980,11 @@ def main():
             return {"kernel": name, "bound": "mfma", "achieved": ach,
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                    "traffic": traffic_for(traffic, name, "<unsigned short, 128>")}
+                    "traffic": traffic_for(traffic, name, SCORE_KERNEL_TAIL)}
         if name == "remat":
             return {"kernel": name, "bound": "hbm", "achieved": remat_gbps,
                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": remat_gbps / HBM_PEAK_GBPS,
-                    "traffic": traffic_for(traffic, "remat_kernel", "<unsigned short, 128, 0, false>")}
+                    "traffic": traffic_for(traffic, *REMAT_VIEW_KERNEL)}
         return None
 
     dom = max(kern.items(), key=lambda kv: kv[1]["avg_ms"] * kv[1]["launches"])
@@ -1049,7 +1057,7 @@ def main():
         delta = {"avg_ms": d_ms, "deltas_per_call": dst["deltas"], "bytes": d_bytes,
                  "GBps": d_bytes / (d_ms * 1e-3) / 1e9,
                  "hbm_frac": d_bytes / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                 "traffic": traffic_for(traffic, "remat_kernel", "<unsigned short, 128, 0, true>")}
+                 "traffic": traffic_for(traffic, *REMAT_DELTA_KERNEL)}
         log(f"delta leg: {d_ms:.2f} ms per remat, {dst['deltas']} blocks shifted in place")
         ws.reset_pool()
     fp8 = fp8_leg(k, ws, wl, dev, args.steps) if args.fp8 else None

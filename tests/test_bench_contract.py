@@ -39,3 +39,22 @@ def test_workload_description_follows_the_workload():
     assert "512 query tokens, budget 4096 blocks (sink 1, recent 64)" in d
     d64 = bench.workload_desc(synth.get_workload("ctx64k"))
     assert d64.startswith("64K-token history: 2048 blocks") and "256 query tokens" in d64
+
+
+def test_traffic_lookups_name_profiled_kernels():
+    """Every kernel the bench line attaches counter traffic to names an entry of
+    the committed counter summary, and its template arguments name a kernel the
+    library launches (a renamed instantiation would silently report null)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    per = json.load(open(os.path.join(ROOT, "profiles", "ws1m_traffic.json")))["per_dispatch"]
+    looks = [("score_pass1_mfma", bench.SCORE_KERNEL_TAIL),
+             ("score_pass2_mfma", bench.SCORE_KERNEL_TAIL),
+             bench.REMAT_VIEW_KERNEL, bench.REMAT_DELTA_KERNEL]
+    for short, tail in looks:
+        hits = [n for n in per if n.split("<")[0].endswith(short) and n.endswith(tail)]
+        assert len(hits) == 1, (short, tail)
+    src = open(os.path.join(ROOT, "attention_space_block_amd", "csrc", "remat.hip")).read()
+    for _, tail in (bench.REMAT_VIEW_KERNEL, bench.REMAT_DELTA_KERNEL):
+        delta, copy_v = tail.strip("<>").split(", ")[3:]
+        assert f"remat_kernel<T, D, LAY, {delta}, {copy_v}>" in src
