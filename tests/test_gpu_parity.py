@@ -332,8 +332,11 @@ def test_fp8_scores_unsupported_forms(k, dev):
 
 def test_scores_steep_ramp_match_oracle(k, dev):
     """Scores that climb (or fall) by more than 32 log2-units along the block
-    axis: rows facing the ramp must refresh their softmax shift in pass 1, rows
-    facing away see most terms vanish; both must match the float64 softmax."""
+    axis: rows facing away see most terms vanish, rows facing the ramp put
+    their mass on its far end; both must match the float64 softmax. At this
+    size pass 1 splits the blocks eight ways, so every workgroup streams 256
+    of them and sets its shift on the exact path of its first stage; shift
+    refreshes in later stages are the next test's subject."""
     wl = synth.get_workload("ctx64k").scaled(n_layers=2, n_q_tokens=77)
     N, d = 2048, wl.head_dim
     import torch
