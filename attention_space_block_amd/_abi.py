@@ -23,6 +23,7 @@ EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
     "kvm_select_ws_bytes", "kvm_select", "kvm_select_noalloc", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
+    "kvm_ctx_register_resident_list",
     "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
     "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_quantize_e4m3",
     "kvm_profile_enable", "kvm_profile_read",
@@ -102,6 +103,7 @@ def lib():
             "kvm_ctx_set_source": (ctypes.c_int, [vp, i64, i64, vp, vp, i64, i32]),
             "kvm_ctx_set_gather": (ctypes.c_int, [vp, i64, i64, GATHER_FN, vp]),
             "kvm_ctx_register_resident": (ctypes.c_int, [vp, i64, i64, vp, vp, i64, vp]),
+            "kvm_ctx_register_resident_list": (ctypes.c_int, [vp, vp, i64, vp, vp, i64, vp]),
             "kvm_ctx_build_index_rope": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
             "kvm_rematerialize": (ctypes.c_int, [vp, vp, vp, vp, ctypes.POINTER(RematStats), vp]),
             "kvm_ctx_sync": (ctypes.c_int, [vp]),

@@ -3,6 +3,8 @@ from __future__ import annotations
 
 import ctypes
 
+import numpy as np
+
 from . import _abi
 from ._abi import (  # noqa: F401
     Dims, KvmError, RematStats, KVM_F32, KVM_BF16, KVM_FP8_E4M3, KVM_INDEX_DEVICE,
@@ -94,7 +96,6 @@ def kvm_select_noalloc(scores, n_blocks: int, n_sink: int, n_recent: int, budget
 def kvm_tier_simulate(policy: int, host_blocks: int, lam: float, steps) -> list:
     """Host-tier admission over a trace; steps = [(new, sel, miss), ...], each an
     ascending list of block ids. Returns [(host_hits, nvme_reads, demotions)]."""
-    import numpy as np
 
     def csr(lists):
         off = np.zeros(len(lists) + 1, dtype=np.int64)
@@ -192,6 +193,16 @@ class KvmCtx:
         rc = _abi.lib().kvm_ctx_register_resident(self._h, first_block, n_blocks, _ptr(k_raw),
                                                   _ptr(v_raw), block_stride, _stream(stream))
         _abi.check(rc, "kvm_ctx_register_resident")
+
+    def kvm_ctx_register_resident_list(self, blocks, k_raw, v_raw, block_stride: int,
+                                       stream=None) -> None:
+        """blocks: strictly ascending block ids (any int sequence); the raw K/V
+        of blocks[i] at k_raw / v_raw + i * block_stride."""
+        ids = np.ascontiguousarray(np.asarray(blocks, dtype=np.int64))
+        rc = _abi.lib().kvm_ctx_register_resident_list(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.size, _ptr(k_raw), _ptr(v_raw),
+            block_stride, _stream(stream))
+        _abi.check(rc, "kvm_ctx_register_resident_list")
 
     def kvm_ctx_build_index_rope(self, k_rope, block_stride: int, first_block: int,
                                  n_blocks: int, pos0: int, index, index_cap_blocks: int,

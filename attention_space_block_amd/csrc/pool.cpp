@@ -98,16 +98,16 @@ int BlockPool::set_gather(int64_t first, int64_t n, kvm_gather_fn fn, void* user
   return KVM_OK;
 }
 
-int BlockPool::register_blocks(int64_t first, int64_t n, std::vector<int32_t>* slots) {
+int BlockPool::register_list(const int64_t* ids, int64_t n, std::vector<int32_t>* slots) {
   slots->assign((size_t)n, -1);
   if (n <= 0) return KVM_OK;
   // Room: free pages plus pages of resident blocks outside the current view
-  // (blocks of this range are being refreshed, not evicted).
+  // (blocks of this list are being refreshed, not evicted).
   std::vector<std::pair<int64_t, int64_t>> lru;
   for (const auto& e : lru_outside_view())
-    if (e.second < first || e.second >= first + n) lru.push_back(e);
+    if (!std::binary_search(ids, ids + n, e.second)) lru.push_back(e);
   int64_t need = 0;
-  for (int64_t b = first; b < first + n; ++b) need += rec_[(size_t)b].slot < 0;
+  for (int64_t i = 0; i < n; ++i) need += rec_[(size_t)ids[i]].slot < 0;
   if (need > (int64_t)free_slots_.size() + (int64_t)lru.size()) {
     set_error("registering %lld blocks needs %lld free pages; %zu are free and %zu hold blocks "
               "outside the current view",
@@ -118,7 +118,7 @@ int BlockPool::register_blocks(int64_t first, int64_t n, std::vector<int32_t>* s
   int32_t evicted = 0;
   const bool delta = L_.delta_limit > 0;
   for (int64_t i = 0; i < n; ++i) {
-    const int64_t b = first + i;
+    const int64_t b = ids[i];
     BlockRec& r = rec_[(size_t)b];
     if (r.slot < 0) {
       const int32_t sl = take_slot(lru, pos, &evicted);
@@ -133,6 +133,16 @@ int BlockPool::register_blocks(int64_t first, int64_t n, std::vector<int32_t>* s
     (*slots)[(size_t)i] = r.slot;
   }
   return KVM_OK;
+}
+
+int BlockPool::register_blocks(int64_t first, int64_t n, std::vector<int32_t>* slots) {
+  std::vector<int64_t> ids((size_t)(n > 0 ? n : 0));
+  for (int64_t i = 0; i < n; ++i) ids[(size_t)i] = first + i;
+  return register_list(ids.data(), n, slots);
+}
+
+void BlockPool::release_list(const int64_t* ids, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) free_slot_of(rec_[(size_t)ids[i]]);
 }
 
 void BlockPool::release(int64_t first, int64_t n) {

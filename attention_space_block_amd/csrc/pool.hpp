@@ -111,13 +111,17 @@ class BlockPool {
                  int64_t stride, int32_t loc);
   int set_gather(int64_t first, int64_t n, kvm_gather_fn fn, void* user);
 
-  // Freshly prefilled blocks [first, first + n) become resident at the
-  // current step: a free page, else the page of the least recently used block
-  // outside the current view. All or nothing: KVM_ENOMEM and no change when
-  // they do not fit. slots[i] receives block first+i's page.
+  // Freshly prefilled blocks ids[0..n) (strictly ascending, checked by the
+  // caller) become resident at the current step: a free page, else the page
+  // of the least recently used block outside the current view. All or
+  // nothing: KVM_ENOMEM and no change when they do not fit. slots[i] receives
+  // block ids[i]'s page.
+  int register_list(const int64_t* ids, int64_t n, std::vector<int32_t>* slots);
+  // The same for the range [first, first + n).
   int register_blocks(int64_t first, int64_t n, std::vector<int32_t>* slots);
-  // Undo register_blocks after its copies could not be queued: the blocks
+  // Undo a registration after its copies could not be queued: the blocks
   // lose their pages (the pages' contents are unknown).
+  void release_list(const int64_t* ids, int64_t n);
   void release(int64_t first, int64_t n);
 
   int evict(int64_t first, int64_t n);

@@ -232,6 +232,56 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, b
 }
 
 
+// Registration copies: the raw K of listed block i (k_src + i * stride) into
+// the K-side page of slot[i] (the shadow page, or the K view page in delta
+// mode) and its V into the V view page, byte for byte. A launch takes up to
+// REG_MAX blocks; their pages travel in the kernel arguments, so a launch
+// needs no upload and leaves no buffer behind whose reuse would have to wait
+// for it. Each workgroup copies one REG_CHUNK of K and of V of one block,
+// every thread sixteen 16-byte pieces of each, all loads before the stores.
+static constexpr int REG_MAX = 448;
+static constexpr int64_t REG_CHUNK = 64 * 1024;
+
+struct RegCopyArgs {
+  const char* k_src;
+  const char* v_src;
+  char* k_dst;
+  char* v_dst;
+  int64_t stride;
+  int64_t page_bytes;        // a multiple of 16
+  int32_t wg_per_page;       // ceil(page_bytes / REG_CHUNK)
+  int32_t n;
+  int32_t slot[REG_MAX];
+};
+
+__global__ __launch_bounds__(256) void register_copy_kernel(RegCopyArgs a) {
+  constexpr int PER = (int)(REG_CHUNK / (256 * 16));
+  const int32_t i = blockIdx.x / a.wg_per_page;
+  if (i >= a.n) return;
+  const int64_t base = (int64_t)(blockIdx.x % a.wg_per_page) * REG_CHUNK;
+  const char* ks = a.k_src + (int64_t)i * a.stride;
+  const char* vs = a.v_src + (int64_t)i * a.stride;
+  char* kd = a.k_dst + (int64_t)a.slot[i] * a.page_bytes;
+  char* vd = a.v_dst + (int64_t)a.slot[i] * a.page_bytes;
+  uint4 k[PER], v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t off = base + ((int64_t)u * 256 + threadIdx.x) * 16;
+    if (off < a.page_bytes) {
+      k[u] = ld_plain(ks + off);
+      v[u] = ld_plain(vs + off);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int64_t off = base + ((int64_t)u * 256 + threadIdx.x) * 16;
+    if (off < a.page_bytes) {
+      st_plain(kd + off, k[u]);
+      st_plain(vd + off, v[u]);
+    }
+  }
+}
+
 // Run f(w) for w in [0, n) on up to n threads; a share whose thread cannot be
 // started runs on the calling thread.
 template <class F>
@@ -505,40 +555,87 @@ static int ctx_set_gather(kvm_ctx* c, int64_t first_block, int64_t n_blocks, kvm
   return c->pool->set_gather(first_block, n_blocks, fn, user);
 }
 
-static int ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_t n_blocks,
-                                 const void* k_raw, const void* v_raw, int64_t block_stride,
-                                 void* stream) {
-  clear_error();
-  KVM_CHECK_ARG(c && k_raw && v_raw, "null pointer");
-  KVM_CHECK_ARG(first_block >= 0 && n_blocks >= 0 && first_block + n_blocks <= c->d.max_blocks,
-                "block range outside the record capacity");
+// Registration of blocks ids[0..n) (strictly ascending) whose raw K and V
+// sit at k_raw / v_raw + i * block_stride (device): pages by the pool's rule,
+// then the copies on `stream` (one kernel launch per REG_MAX blocks when
+// sources, stride and pages are 16-byte aligned, else one copy per page).
+static int ctx_register(kvm_ctx* c, const int64_t* ids, int64_t n, const void* k_raw,
+                        const void* v_raw, int64_t block_stride, void* stream) {
+  KVM_CHECK_ARG(k_raw && v_raw, "null pointer");
   KVM_CHECK_ARG(block_stride >= c->page_bytes, "block_stride");
-  if (n_blocks == 0) return KVM_OK;
-  const size_t span = (size_t)((n_blocks - 1) * block_stride + c->page_bytes);
+  for (int64_t i = 0; i < n; ++i)
+    KVM_CHECK_ARG(ids[i] >= 0 && ids[i] < c->d.max_blocks && (i == 0 || ids[i] > ids[i - 1]),
+                  "block list entry %lld (block %lld): out of range or not ascending",
+                  (long long)i, (long long)ids[i]);
+  if (n == 0) return KVM_OK;
+  const size_t span = (size_t)((n - 1) * block_stride + c->page_bytes);
   KVM_CHECK_RANGE(k_raw, span, RANGE_DEVICE, "k_raw");
   KVM_CHECK_RANGE(v_raw, span, RANGE_DEVICE, "v_raw");
   hipStream_t s = as_stream(stream);
   std::vector<int32_t> slots;
-  KVM_TRY(c->pool->register_blocks(first_block, n_blocks, &slots));
-  const bool delta = c->d.delta_limit > 0;
+  KVM_TRY(c->pool->register_list(ids, n, &slots));
   // raw K lands in the shadow page (in delta mode in the K page, rotated at
   // the block's first selection); V in the V page
-  for (int64_t i = 0; i < n_blocks; ++i) {
-    const int64_t off = (int64_t)slots[(size_t)i] * c->page_bytes;
-    char* kdst = (char*)(delta ? c->d.k_view : c->d.k_shadow) + off;
-    hipError_t e = hipMemcpyAsync(kdst, (const char*)k_raw + i * block_stride, c->page_bytes,
-                                  hipMemcpyDeviceToDevice, s);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync((char*)c->d.v_view + off, (const char*)v_raw + i * block_stride,
-                         c->page_bytes, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) {
-      c->pool->release(first_block, n_blocks);
-      set_error("registering block %lld: %s", (long long)(first_block + i),
-                hipGetErrorString(e));
-      return KVM_EHIP;
+  char* kdst = (char*)(c->d.delta_limit > 0 ? c->d.k_view : c->d.k_shadow);
+  char* vdst = (char*)c->d.v_view;
+  const bool aligned = ((uintptr_t)k_raw % 16 == 0) && ((uintptr_t)v_raw % 16 == 0) &&
+                       block_stride % 16 == 0 && c->page_bytes % 16 == 0;
+  hipError_t e = hipSuccess;
+  int64_t at = 0;
+  if (aligned) {
+    RegCopyArgs a{};
+    a.k_dst = kdst;
+    a.v_dst = vdst;
+    a.stride = block_stride;
+    a.page_bytes = c->page_bytes;
+    a.wg_per_page = (int32_t)((c->page_bytes + REG_CHUNK - 1) / REG_CHUNK);
+    KernelTimer tm("register_copy", s);
+    for (; at < n && e == hipSuccess; at += REG_MAX) {
+      a.n = (int32_t)std::min<int64_t>(REG_MAX, n - at);
+      a.k_src = (const char*)k_raw + at * block_stride;
+      a.v_src = (const char*)v_raw + at * block_stride;
+      for (int32_t j = 0; j < a.n; ++j) a.slot[j] = slots[(size_t)(at + j)];
+      register_copy_kernel<<<dim3((uint32_t)a.n * (uint32_t)a.wg_per_page), dim3(256), 0, s>>>(a);
+      e = hipGetLastError();
+    }
+  } else {
+    for (; at < n && e == hipSuccess; ++at) {
+      const int64_t off = (int64_t)slots[(size_t)at] * c->page_bytes;
+      e = hipMemcpyAsync(kdst + off, (const char*)k_raw + at * block_stride, c->page_bytes,
+                         hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(vdst + off, (const char*)v_raw + at * block_stride, c->page_bytes,
+                           hipMemcpyDeviceToDevice, s);
     }
   }
+  if (e != hipSuccess) {
+    c->pool->release_list(ids, n);
+    set_error("registering %lld blocks: %s", (long long)n, hipGetErrorString(e));
+    return KVM_EHIP;
+  }
   return KVM_OK;
+}
+
+static int ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_t n_blocks,
+                                 const void* k_raw, const void* v_raw, int64_t block_stride,
+                                 void* stream) {
+  clear_error();
+  KVM_CHECK_ARG(c, "ctx is NULL");
+  KVM_CHECK_ARG(first_block >= 0 && n_blocks >= 0 && first_block + n_blocks <= c->d.max_blocks,
+                "block range outside the record capacity");
+  std::vector<int64_t> ids((size_t)n_blocks);
+  for (int64_t i = 0; i < n_blocks; ++i) ids[(size_t)i] = first_block + i;
+  return ctx_register(c, ids.data(), n_blocks, k_raw, v_raw, block_stride, stream);
+}
+
+static int ctx_register_resident_list(kvm_ctx* c, const int64_t* blocks, int64_t n_blocks,
+                                      const void* k_raw, const void* v_raw, int64_t block_stride,
+                                      void* stream) {
+  clear_error();
+  KVM_CHECK_ARG(c, "ctx is NULL");
+  KVM_CHECK_ARG(n_blocks >= 0 && n_blocks <= c->d.max_blocks && (blocks || n_blocks == 0),
+                "block list");
+  return ctx_register(c, blocks, n_blocks, k_raw, v_raw, block_stride, stream);
 }
 
 static int rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32_t* n_sel_dev,
@@ -632,6 +729,16 @@ extern "C" int kvm_ctx_register_resident(kvm_ctx* c, int64_t first_block, int64_
   return kvm::guarded([&] {
     return kvm::ctx_register_resident(c, first_block, n_blocks, k_raw, v_raw, block_stride,
                                       stream);
+  });
+}
+
+extern "C" int kvm_ctx_register_resident_list(kvm_ctx* c, const int64_t* blocks,
+                                              int64_t n_blocks, const void* k_raw,
+                                              const void* v_raw, int64_t block_stride,
+                                              void* stream) {
+  return kvm::guarded([&] {
+    return kvm::ctx_register_resident_list(c, blocks, n_blocks, k_raw, v_raw, block_stride,
+                                           stream);
   });
 }
 

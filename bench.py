@@ -206,9 +206,8 @@ class Workspace:
         registered again as freshly prefilled (K page stale)."""
         wl = self.wl
         self.ctx.kvm_ctx_evict(0, wl.final_blocks)
-        for i, b in enumerate(self.hits):
-            self.ctx.kvm_ctx_register_resident(int(b), 1, self.hit_k[i], self.hit_v[i],
-                                               wl.block_bytes)
+        self.ctx.kvm_ctx_register_resident_list(self.hits, self.hit_k, self.hit_v,
+                                                wl.block_bytes)
 
     def step(self):
         """The timed hot path of one agent step."""
@@ -306,8 +305,7 @@ def fp8_leg(k, ws, wl, dev, steps: int) -> dict:
 
     def one():
         ctx.kvm_ctx_evict(0, wl.final_blocks)
-        for i, b in enumerate(ws.hits):
-            ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv_[i], page)
+        ctx.kvm_ctx_register_resident_list(ws.hits, hk, hv_, page)
         torch.cuda.synchronize()
         return ctx.kvm_rematerialize(ws.sel, ws.n_sel, ws.page)
     one()

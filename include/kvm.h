@@ -80,7 +80,7 @@ typedef struct {
   int32_t block_tokens; /* B: tokens per logical block (32) */
 } kvm_dims;
 
-/* Version of this interface (major*100 + minor): 101. */
+/* Version of this interface (major*100 + minor): 102. */
 int kvm_version(void);
 
 /* Text of the last error on the calling thread ("" if none). */
@@ -292,6 +292,20 @@ int kvm_ctx_set_gather(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks, kvm_
 int kvm_ctx_register_resident(kvm_ctx* ctx, int64_t first_block, int64_t n_blocks,
                               const void* k_raw, const void* v_raw, int64_t block_stride,
                               void* stream);
+
+/* The same for a set of blocks that need not be consecutive (KVMem Sec. 4.4:
+ * blocks staged back into the GPU tier, or prefilled blocks of several
+ * chunks): blocks (host int64[n_blocks], strictly ascending, each below
+ * max_blocks) name the blocks; the raw K and V of blocks[i] sit at
+ * k_raw / v_raw + i * block_stride (device). Same page rule, all or nothing.
+ * Both registration calls copy with one kernel launch per 448 blocks when
+ * k_raw, v_raw and block_stride are multiples of 16 bytes (else one copy per
+ * page). Errors: KVM_EINVAL (a list entry out of range or not ascending,
+ * block_stride below the page size, or sources that are not device memory of
+ * the needed size), KVM_ENOMEM and KVM_EHIP as above. */
+int kvm_ctx_register_resident_list(kvm_ctx* ctx, const int64_t* blocks, int64_t n_blocks,
+                                   const void* k_raw, const void* v_raw, int64_t block_stride,
+                                   void* stream);
 
 /* Mean-K index rows from K that already carries RoPE (KVMem Sec. 5: during
  * prefill RoPE is removed from the K of completed blocks and their Mean-K is

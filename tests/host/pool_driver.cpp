@@ -505,6 +505,22 @@ int main() {
         }
       }
       printf("reg %d\n", rc);
+    } else if (cmd == "regl") {
+      int64_t n;
+      in >> n;
+      std::vector<int64_t> ids((size_t)n);
+      for (auto& x : ids) in >> x;
+      std::vector<int32_t> slots;
+      const int rc = w.pool->register_list(ids.data(), n, &slots);
+      if (rc == KVM_OK) {
+        const bool delta = w.L.delta_limit > 0;
+        for (int64_t i = 0; i < n; ++i) {
+          char* kd = (delta ? w.L.k_view : w.L.k_shadow) + (int64_t)slots[(size_t)i] * PAGE;
+          make_page(kd, RAWK, ids[(size_t)i], -1);
+          make_page(w.L.v_view + (int64_t)slots[(size_t)i] * PAGE, RAWV, ids[(size_t)i], -1);
+        }
+      }
+      printf("regl %d\n", rc);
     } else if (cmd == "evict") {
       int64_t first, n;
       in >> first >> n;

@@ -1027,6 +1027,108 @@ def test_register_never_takes_pages_of_the_current_view(k, dev):
     pool.ctx.close()
 
 
+def test_register_list_matches_per_block_registration(k, dev):
+    """kvm_ctx_register_resident_list: non-consecutive blocks whose raw K/V are
+    packed in one buffer take the same pages as one-block registrations (the
+    page rule of the oracle's pool model), their shadow and V pages hold the
+    raw bytes, and the next view built from them matches the oracle. Also the
+    copy launches in groups of 448 blocks (a 500-block list), the per-page copy
+    path for sources that are not 16-byte aligned, a list that does not fit
+    (KVM_ENOMEM, nothing changed) and malformed lists (KVM_EINVAL)."""
+    import torch
+    from oracle import PagePool
+    wl = synth.get_workload("tiny")                 # 16 KiB pages
+    N, n_slots = 1000, 600
+    a, keep = _remat_setup(k, dev, wl, N, n_slots)
+    b, _ = _remat_setup(k, dev, wl, N, n_slots)
+    rk, rv = keep
+    model = PagePool(n_slots)
+    view = list(range(0, 11))
+    sel = torch.tensor(view, dtype=torch.int32, device=dev)
+    n_sel = torch.tensor([len(view)], dtype=torch.int32, device=dev)
+    for p in (a, b):
+        p.ctx.kvm_rematerialize(sel, n_sel, p.page)
+    model.update(view)
+    torch.cuda.synchronize()
+
+    def packed(ids):
+        return rk[ids].contiguous(), rv[ids].contiguous()
+
+    def same_bytes(x, y):
+        return torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
+
+    ids = [3, 20, 33, 57, 90, 91, 120, 999]          # 3 is in the view: refreshed in place
+    pk, pv = packed(ids)
+    a.ctx.kvm_ctx_register_resident_list(ids, pk, pv, wl.block_bytes)
+    for i in ids:
+        b.ctx.kvm_ctx_register_resident(i, 1, rk[i], rv[i], wl.block_bytes)
+    model.register(ids)
+    torch.cuda.synchronize()
+    assert _state(a, range(N)) == _state(b, range(N))
+    resident = {i for i in range(N) if a.ctx.kvm_ctx_block_state(i)[0] >= 0}
+    assert resident == model.resident
+    for i in ids:
+        slot = a.ctx.kvm_ctx_block_state(i)[0]
+        assert same_bytes(a.k_shadow[slot], rk[i]) and same_bytes(a.v_view[slot], rv[i])
+    # 500 more blocks in one list: two copy launches (448 + 52)
+    big = list(range(300, 800))
+    bk, bv = packed(big)
+    a.ctx.kvm_ctx_register_resident_list(big, bk, bv, wl.block_bytes)
+    model.register(big)
+    torch.cuda.synchronize()
+    for i in big[::7] + [big[447], big[448], big[-1]]:
+        slot = a.ctx.kvm_ctx_block_state(i)[0]
+        assert slot >= 0
+        assert same_bytes(a.k_shadow[slot], rk[i]) and same_bytes(a.v_view[slot], rv[i])
+    # sources 4 bytes off 16-byte alignment, stride a page plus 4 bytes: per-page copies
+    odd = [40, 41, 700]
+    stride = wl.block_bytes + 4
+    raw = torch.zeros(len(odd) * stride + 16, dtype=torch.uint8, device=dev)
+    rawv = torch.zeros_like(raw)
+    for j, i in enumerate(odd):
+        raw[4 + j * stride:4 + j * stride + wl.block_bytes] = rk[i].view(torch.uint8)
+        rawv[4 + j * stride:4 + j * stride + wl.block_bytes] = rv[i].view(torch.uint8)
+    a.ctx.kvm_ctx_register_resident_list(odd, raw[4:], rawv[4:], stride)
+    model.register(odd)
+    torch.cuda.synchronize()
+    for i in odd:
+        slot = a.ctx.kvm_ctx_block_state(i)[0]
+        assert same_bytes(a.k_shadow[slot], rk[i]) and same_bytes(a.v_view[slot], rv[i])
+    resident = {i for i in range(N) if a.ctx.kvm_ctx_block_state(i)[0] >= 0}
+    assert resident == model.resident
+    # the next view is built from the registered raw K
+    view2 = [0, 3, 20, 33, 41, 57, 90, 120, 300, 747, 999]
+    sel2 = torch.tensor(view2, dtype=torch.int32, device=dev)
+    st = a.ctx.kvm_rematerialize(sel2, n_sel, a.page)
+    torch.cuda.synchronize()
+    r = model.update(view2)
+    assert (st["hits"], st["misses"], st["evicted"]) == (
+        len(r["hits"]), len(r["misses"]), len(r["evicted"]))
+    gc.check_view(wl, np.array(view2), a.page.cpu().numpy()[:11], a)
+    # a list that does not fit changes nothing: the second pool holds 18
+    # blocks, all in its current view (the last selection and the blocks
+    # registered since), so 582 free pages are all that can be had
+    before = _state(b, range(N))
+    many = [i for i in range(N) if before[i][0] < 0][:583]
+    mk, mv = packed(many)
+    with pytest.raises(k.KvmError) as e:
+        b.ctx.kvm_ctx_register_resident_list(many, mk, mv, wl.block_bytes)
+    assert e.value.code == k.api._abi.KVM_ENOMEM
+    assert _state(b, range(N)) == before
+    b.ctx.kvm_ctx_register_resident_list(many[:582], mk[:582], mv[:582], wl.block_bytes)
+    torch.cuda.synchronize()
+    assert all(b.ctx.kvm_ctx_block_state(i)[0] >= 0 for i in many[:582] + view + ids)
+    before = _state(a, range(N))
+    for bad in ([5, 5], [7, 6], [-1], [N]):
+        bk_, bv_ = packed([0] * len(bad))
+        with pytest.raises(k.KvmError) as e:
+            a.ctx.kvm_ctx_register_resident_list(bad, bk_, bv_, wl.block_bytes)
+        assert e.value.code == k.api._abi.KVM_EINVAL
+    assert _state(a, range(N)) == before
+    a.ctx.close()
+    b.ctx.close()
+
+
 def test_failed_gather_rolls_back_and_a_retry_is_exact(k, dev):
     """The gather callback fails on the second staging batch: the call returns
     an error after the first batch was queued. Blocks whose pages were

@@ -231,8 +231,8 @@ def test_ws1m_fp8_pages_view(k, dev):
     pool = gc.Pool(k, wl, n + 64, N, (n + wl.reserve_blocks) * B, dev)
     hk = gc.raw_blocks_to_device(wl, "K", hits, dev)
     hv = gc.raw_blocks_to_device(wl, "V", hits, dev)
-    for i, b in enumerate(hits):
-        pool.ctx.kvm_ctx_register_resident(int(b), 1, hk[i], hv[i], wl.block_bytes)
+    # one call for the whole resident half (copies in groups of 448 blocks)
+    pool.ctx.kvm_ctx_register_resident_list(hits, hk, hv, wl.block_bytes)
     torch.cuda.synchronize()
     del hk, hv
     mk = gc.raw_blocks_to_device(wl, "K", misses, dev)

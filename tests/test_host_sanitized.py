@@ -114,6 +114,10 @@ def random_scenario(seed, delta, sources, fail_rate):
         if rng.random() < 0.1:
             b = int(rng.integers(0, nb))
             steps.append(("evict", [b]))
+        if rng.random() < 0.2:
+            # blocks staged back, not consecutive (some may be resident)
+            ids = sorted(rng.choice(nb, int(rng.integers(1, 5)), replace=False).tolist())
+            steps.append(("regl", ids))
         k = int(rng.integers(1, budget + 1))
         blocks = sorted(rng.choice(nb, min(k, nb), replace=False).tolist())
         fail = None
@@ -134,6 +138,9 @@ def play(exe, lines, steps, n_slots):
     for st in steps:
         if st[0] == "reg":
             script.append(f"reg {st[1][0]} {len(st[1])}")
+            outputs_needed.append(("reg", st[1]))
+        elif st[0] == "regl":
+            script.append("regl " + " ".join(str(x) for x in [len(st[1])] + st[1]))
             outputs_needed.append(("reg", st[1]))
         elif st[0] == "evict":
             script.append(f"evict {st[1][0]} 1")
