@@ -938,10 +938,11 @@ def main():
     def run(n_steps, profile):
         times, stats = [], None
         for _ in range(n_steps):
+            k.kvm_profile_enable(False)       # the reset is not part of the step
             ws.reset_pool()
             torch.cuda.synchronize()
-            if profile and not times:
-                k.kvm_profile_enable(True)
+            if profile:
+                k.kvm_profile_enable(True)    # keeps the earlier steps' launches
             t0 = time.perf_counter()
             stats = ws.step()
             torch.cuda.synchronize()
