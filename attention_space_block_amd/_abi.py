@@ -18,6 +18,7 @@ KVM_F32, KVM_BF16, KVM_FP8_E4M3 = 0, 1, 2
 KVM_INDEX_DEVICE, KVM_INDEX_HOST_TILED = 0, 1
 KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE = 0, 1, 2
 KVM_TIER_LRU, KVM_TIER_LRFU = 0, 1
+KVM_RATE_COPY, KVM_RATE_MFMA_BF16, KVM_RATE_EXP, KVM_RATE_SCORE_MIX = 0, 1, 2, 3
 
 EXPORTED = [
     "kvm_version", "kvm_last_error", "kvm_build_index", "kvm_score_ws_bytes", "kvm_score_blocks",
@@ -26,7 +27,7 @@ EXPORTED = [
     "kvm_ctx_register_resident_list",
     "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
     "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_quantize_e4m3",
-    "kvm_profile_enable", "kvm_profile_read",
+    "kvm_profile_enable", "kvm_profile_read", "kvm_measure_rate",
 ]
 
 
@@ -104,6 +105,7 @@ def lib():
             "kvm_ctx_set_gather": (ctypes.c_int, [vp, i64, i64, GATHER_FN, vp]),
             "kvm_ctx_register_resident": (ctypes.c_int, [vp, i64, i64, vp, vp, i64, vp]),
             "kvm_ctx_register_resident_list": (ctypes.c_int, [vp, vp, i64, vp, vp, i64, vp]),
+            "kvm_measure_rate": (ctypes.c_int, [i32, i64, vp, sz, vp, vp]),
             "kvm_ctx_build_index_rope": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
             "kvm_rematerialize": (ctypes.c_int, [vp, vp, vp, vp, ctypes.POINTER(RematStats), vp]),
             "kvm_ctx_sync": (ctypes.c_int, [vp]),

@@ -11,6 +11,7 @@ from ._abi import (  # noqa: F401
     KVM_INDEX_HOST_TILED,
     KVM_SRC_NONE, KVM_SRC_HOST_PINNED, KVM_SRC_DEVICE,
     KVM_TIER_LRU, KVM_TIER_LRFU,
+    KVM_RATE_COPY, KVM_RATE_MFMA_BF16, KVM_RATE_EXP, KVM_RATE_SCORE_MIX,
 )
 
 
@@ -126,6 +127,16 @@ def kvm_profile_read() -> dict:
     _abi.check(_abi.lib().kvm_profile_read(buf, 64, ctypes.byref(n)), "kvm_profile_read")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
             for i in range(min(n.value, 64))}
+
+
+def kvm_measure_rate(kind: int, n: int, scratch, stream=None) -> float:
+    """Measured rate of one unit (see KVM_RATE_*); scratch: a device tensor."""
+    out = ctypes.c_double()
+    nbytes = scratch.numel() * scratch.element_size()
+    rc = _abi.lib().kvm_measure_rate(kind, n, _ptr(scratch), nbytes, ctypes.byref(out),
+                                     _stream(stream))
+    _abi.check(rc, "kvm_measure_rate")
+    return float(out.value)
 
 
 class KvmCtx:

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["api.hip", "profile.hip", "build_index.hip", "score.hip", "select.hip", "remat.hip",
-           "quantize.hip",
+           "quantize.hip", "probe.hip",
            # host-only C++ (no HIP headers): also built with g++ for the sanitizer tests
            "host_common.cpp", "pool.cpp", "dataplane.cpp", "tier.cpp"]
 LIB = os.path.join(HERE, "libkvm.so")

@@ -35,23 +35,30 @@
 
 namespace kvm {
 
-// (l, g) units of 32 token rows handled by one workgroup
-static constexpr int REMAT_UNITS = 8;
-// Units per workgroup scale inversely with the element size, so a thread holds
-// the same bytes of rows in every dtype: FP8 rows are half as long (16 units;
-// a thread's (cos, sin) pairs then serve as many bytes as in bf16), fp32 rows
-// twice as long (4 units; 8 would take all 256 registers, one wave per SIMD)
-static constexpr int REMAT_UNITS_FP8 = 16;
-static constexpr int REMAT_UNITS_F32 = 4;
-static constexpr int remat_units(int elem_bytes) {
-  return elem_bytes == 1 ? REMAT_UNITS_FP8 : elem_bytes == 4 ? REMAT_UNITS_F32 : REMAT_UNITS;
+// jobs per launch: the grid's y dimension holds them and their V rows
+static constexpr int32_t REMAT_JOBS_PER_LAUNCH = 16384;
+// (l, g) units a K work item covers with one load of its (cos, sin): FP8
+// pieces hold 8 pairs, so one unit per item would read 64 bytes of table per
+// 16 bytes of K
+#ifndef KVM_REMAT_R_FP8
+#define KVM_REMAT_R_FP8 8
+#endif
+#ifndef KVM_REMAT_R_BF16
+#define KVM_REMAT_R_BF16 1
+#endif
+static constexpr int remat_units_per_item(int elem_bytes) {
+  return elem_bytes == 1 ? KVM_REMAT_R_FP8 : elem_bytes == 2 ? KVM_REMAT_R_BF16 : 1;
 }
 
 struct RematArgs {
   const RematJob* jobs;
   int32_t n_jobs;
-  int32_t wg_per_job;        // ceil(L * Hkv / units) workgroups per block
-  int32_t rows_per_page;     // L * Hkv * B
+  int32_t first_v;           // jobs [first_v, n_jobs) may copy V (each checks its flag)
+  int32_t wg_k;              // workgroups per job for K: ceil(items per page / 256)
+  int32_t wg_v;              // workgroups per job for V: ceil(page_bytes / 16 / 256)
+  int64_t items;             // K work items per page (one piece or one piece pair, in
+                             // R units: ceil(units / R) * 32 * items per row)
+  int32_t units;             // (l, g) units per page: L * Hkv
   int64_t page_bytes;
   char* k_view;
   char* v_view;
@@ -107,110 +114,102 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
                     __float_as_uint(x[3]));
 }
 
-// Work split: a flat grid; workgroup w handles UNITS consecutive (l, g) units
-// (32 token rows each) of job w / units_per_wg_count, so concurrently running
-// workgroups stream neighbouring bytes of the same page (DRAM locality like a
-// plain copy). A thread always sees the same token index j of its rows, so its
-// (cos, sin) pairs for position pos + j are loaded once into registers.
-// Each thread owns two 16-byte pieces of a row:
-// LAYOUT 0 (pairs (2t, 2t+1)): pieces [t0, t0+P) and [t0+P, t0+2P);
-// LAYOUT 1 (pairs (t, t+d/2)): pieces [t0, t0+P) and [t0+d/2, t0+d/2+P).
-// All loads of a workgroup's rows are issued before the first store; loads and
-// stores are plain (cached) ones, faster here than the non-temporal forms.
+// Work split: one 16-byte piece of a page per thread (LAYOUT 0: its pairs
+// (2t, 2t+1) lie inside the piece), or one piece and its partner d/2 elements
+// on (LAYOUT 1), over a two-dimensional grid: row y < n_jobs of workgroups
+// rotates job y's K page in page order, and the rows after them copy the V
+// pages of jobs [first_v, n_jobs) that carry JOB_COPY_V (workgroups are
+// dispatched x first, so no division maps a workgroup to its job). The
+// workgroups in flight then cover one narrow stretch of each page, which the
+// DRAM serves best (a plain copy in this shape moves about 6.1 TB/s, against
+// 3.6 TB/s when each thread loads sixteen pieces before storing them); each
+// thread reads the (cos, sin) of its pairs from the fp32 table (L2-resident:
+// 32 positions of a job span at most 32 table rows). Loads and stores are
+// plain (cached) ones, faster here than the non-temporal forms.
 template <typename T, int D, int LAYOUT, bool DELTA, bool COPYV>
 __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
-  constexpr int TPR = D / (2 * P);               // threads per row
-  constexpr int RPI = 256 / TPR;                 // rows per workgroup pass
   constexpr int ROW_BYTES = D * sizeof(T);
+  constexpr int PPR = ROW_BYTES / 16;            // pieces per row
+  constexpr int IPR = LAYOUT == 0 ? PPR : PPR / 2;   // work items per row
   constexpr int HALF = D / 2;
-  constexpr int ROWS = remat_units(sizeof(T)) * 32;   // rows per workgroup
-  constexpr int NR = ROWS / RPI;                 // rows per thread
-  constexpr int NJ = RPI >= 32 ? 1 : 32 / RPI;   // distinct token indices per thread
-  constexpr int NC = P;                          // (cos, sin) pairs per piece pair
-  const int32_t jid = blockIdx.x / a.wg_per_job;
-  const int32_t wpart = blockIdx.x % a.wg_per_job;
-  if (jid >= a.n_jobs) return;
-  const RematJob job = a.jobs[jid];
-  const int trow = threadIdx.x / TPR;
-  const int tcol = threadIdx.x % TPR;
-  const int t0 = LAYOUT == 0 ? tcol * 2 * P : tcol * P;            // first element
-  const int off1 = LAYOUT == 0 ? P : D / 2;                         // second piece offset
-  // (cos, sin) of the pairs this thread rotates, for each of its token indices;
-  // launches of delta jobs turn every token by the job's signed shift instead
-  // (table entry |shift|, sin negated for a negative shift)
+  constexpr int NC = LAYOUT == 0 ? P / 2 : P;    // pairs per item
+  constexpr int R = remat_units_per_item(sizeof(T));
+  // grid: x = workgroup within the page, y = job (rows [n_jobs, ...) copy V)
+  const uint32_t part = blockIdx.x;
+  if ((int32_t)blockIdx.y >= a.n_jobs) {
+    if (!COPYV) return;
+    const int32_t jid = a.first_v + ((int32_t)blockIdx.y - a.n_jobs);
+    if (jid >= a.n_jobs || (int32_t)part >= a.wg_v) return;
+    const RematJob job = a.jobs[jid];
+    if ((job.flags & JOB_COPY_V) == 0) return;
+    const int64_t off = ((int64_t)part * 256 + threadIdx.x) * 16;
+    if (off >= a.page_bytes) return;
+    st_plain(a.v_view + (int64_t)job.slot * a.page_bytes + off, ld_plain(job.src_v + off));
+    // keeps this path's store its own: merged with the K path's stores, the
+    // compiler splits every 16-byte store into a 4- and a 12-byte one
+    asm volatile("" ::: "memory");
+    return;
+  }
+  if ((int32_t)part >= a.wg_k) return;
+  const RematJob job = a.jobs[blockIdx.y];
+  const uint32_t item = part * 256 + threadIdx.x;
+  if ((int64_t)item >= a.items) return;
+  // item -> (group of R (l, g) units, token j, piece p): the thread rotates
+  // piece p of token row j in each unit of the group with the same (cos, sin)
+  const int p = (int)(item % IPR);
+  const uint32_t t = item / IPR;
+  const int j = (int)(t & 31);
+  const int32_t unit0 = (int32_t)(t >> 5) * R;
+  // (cos, sin) of this item's pairs: pair index t0 + q; delta jobs turn every
+  // token by the job's signed shift (table entry |shift|, sin negated below 0)
+  const int t0 = LAYOUT == 0 ? p * (P / 2) : p * P;
   const int32_t shift = job.pos < 0 ? -job.pos : job.pos;
-  const float ssign = DELTA && job.pos < 0 ? -1.0f : 1.0f;
-  float2 cs[NJ][NC];
+  const float2* trow = a.table + (int64_t)(DELTA ? shift : job.pos + j) * HALF + t0;
+  float2 cs[NC];
 #pragma unroll
-  for (int s = 0; s < NJ; ++s) {
-    const int j = (trow + s * RPI) & 31;
-    const float2* row = a.table + (int64_t)(DELTA ? shift : job.pos + j) * HALF;
+  for (int q = 0; q < NC; ++q) cs[q] = trow[q];
+  if (DELTA && job.pos < 0) {
 #pragma unroll
-    for (int q = 0; q < NC; ++q) {
-      cs[s][q] = LAYOUT == 0 ? row[t0 / 2 + q] : row[t0 + q];
-      if (DELTA) cs[s][q].y *= ssign;
-    }
+    for (int q = 0; q < NC; ++q) cs[q].y = -cs[q].y;
   }
-  const int64_t page = (int64_t)job.slot * a.page_bytes;
-  const int64_t row0 = (int64_t)wpart * ROWS;
-  // launches of K-only jobs compile the V copy out (fewer registers, more
-  // waves per SIMD); launches that may copy V test each job's flag
-  const bool copyv = COPYV && (job.flags & JOB_COPY_V) != 0;
-  uint4 k0[NR], k1[NR], v0[NR], v1[NR];
+  char* kv = a.k_view + (int64_t)job.slot * a.page_bytes;
 #pragma unroll
-  for (int u = 0; u < NR; ++u) {
-    if (row0 + trow + u * RPI >= a.rows_per_page) continue;   // ragged last workgroup
-    const int64_t b0 = (row0 + trow + u * RPI) * ROW_BYTES + (int64_t)t0 * sizeof(T);
-    k0[u] = ld_plain(job.src_k + b0);
-    k1[u] = ld_plain(job.src_k + b0 + (int64_t)off1 * sizeof(T));
-    if (copyv) {
-      v0[u] = ld_plain(job.src_v + b0);
-      v1[u] = ld_plain(job.src_v + b0 + (int64_t)off1 * sizeof(T));
-    }
-  }
-  char* kv = a.k_view + page;
-  char* vv = a.v_view + page;
-#pragma unroll
-  for (int u = 0; u < NR; ++u) {
-    if (row0 + trow + u * RPI >= a.rows_per_page) continue;
-    const int64_t b0 = (row0 + trow + u * RPI) * ROW_BYTES + (int64_t)t0 * sizeof(T);
-    const int64_t b1 = b0 + (int64_t)off1 * sizeof(T);
-    const float2* c = cs[u % NJ];
-    float x0[P], x1[P], y0[P], y1[P];
-    unpack<T>(k0[u], x0);
-    unpack<T>(k1[u], x1);
+  for (int u = 0; u < R; ++u) {
+    if (R > 1 && unit0 + u >= a.units) break;
+    const int64_t row = (int64_t)(unit0 + u) * 32 + j;
+    const int64_t b0 = row * ROW_BYTES + (int64_t)p * 16;
+    const uint4 k0 = ld_plain(job.src_k + b0);
+    float x0[P], y0[P];
+    unpack<T>(k0, x0);
     if (LAYOUT == 0) {
 #pragma unroll
       for (int q = 0; q < P / 2; ++q) {
-        const float2 c0 = c[q];
-        const float2 c1 = c[P / 2 + q];
-        y0[2 * q] = x0[2 * q] * c0.x - x0[2 * q + 1] * c0.y;
-        y0[2 * q + 1] = x0[2 * q] * c0.y + x0[2 * q + 1] * c0.x;
-        y1[2 * q] = x1[2 * q] * c1.x - x1[2 * q + 1] * c1.y;
-        y1[2 * q + 1] = x1[2 * q] * c1.y + x1[2 * q + 1] * c1.x;
+        y0[2 * q] = x0[2 * q] * cs[q].x - x0[2 * q + 1] * cs[q].y;
+        y0[2 * q + 1] = x0[2 * q] * cs[q].y + x0[2 * q + 1] * cs[q].x;
       }
+      st_plain(kv + b0, pack<T>(y0));
     } else {
+      const int64_t b1 = b0 + HALF * (int64_t)sizeof(T);
+      const uint4 k1 = ld_plain(job.src_k + b1);
+      float x1[P], y1[P];
+      unpack<T>(k1, x1);
 #pragma unroll
       for (int q = 0; q < P; ++q) {
-        y0[q] = x0[q] * c[q].x - x1[q] * c[q].y;
-        y1[q] = x0[q] * c[q].y + x1[q] * c[q].x;
+        y0[q] = x0[q] * cs[q].x - x1[q] * cs[q].y;
+        y1[q] = x0[q] * cs[q].y + x1[q] * cs[q].x;
       }
-    }
-    st_plain(kv + b0, pack<T>(y0));
-    st_plain(kv + b1, pack<T>(y1));
-    if (copyv) {
-      st_plain(vv + b0, v0[u]);
-      st_plain(vv + b1, v1[u]);
+      st_plain(kv + b0, pack<T>(y0));
+      st_plain(kv + b1, pack<T>(y1));
     }
   }
 }
 
 static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, bool copy_v,
                          const RematArgs& a, hipStream_t s) {
-  const int64_t grid = (int64_t)a.n_jobs * a.wg_per_job;
-  if (grid <= 0) return;
-  dim3 g((uint32_t)grid), b(256);
+  const int32_t rows = a.n_jobs + (copy_v ? a.n_jobs - a.first_v : 0);
+  if (a.n_jobs <= 0 || rows <= 0) return;
+  dim3 g((uint32_t)std::max(a.wg_k, copy_v ? a.wg_v : 0), (uint32_t)rows), b(256);
   KernelTimer tm("remat", s);
 #define KVM_REMAT(T, D, LAY)                                                 \
   do {                                                                       \
@@ -381,12 +380,25 @@ class HipEngine final : public Engine {
     return a == hipSuccess && b == hipSuccess && v == hipSuccess ? KVM_OK : KVM_EHIP;
   }
   int launch(int32_t first, int32_t n, bool delta, bool copy_v) override {
-    RematArgs a = a_;
-    a.jobs = c_->d_jobs + first;
-    a.n_jobs = n;
     const kvm_dims& dm = c_->d.dims;
-    launch_remat(c_->d.dtype, dm.head_dim, c_->d.rope_layout, delta, copy_v, a, s_);
-    KVM_HIP(hipGetLastError());
+    // the grid's second dimension holds the jobs (and their V rows): at most
+    // REMAT_JOBS_PER_LAUNCH jobs per launch
+    for (int32_t c0 = 0; c0 < n; c0 += REMAT_JOBS_PER_LAUNCH) {
+      RematArgs a = a_;
+      a.jobs = c_->d_jobs + first + c0;
+      a.n_jobs = std::min(REMAT_JOBS_PER_LAUNCH, n - c0);
+      // V rows start at the first job that copies V (device misses follow the
+      // re-encodes in a plan; each job still checks its flag)
+      a.first_v = a.n_jobs;
+      if (copy_v)
+        for (int32_t i = 0; i < a.n_jobs; ++i)
+          if (c_->h_jobs[(size_t)(first + c0 + i)].flags & JOB_COPY_V) {
+            a.first_v = i;
+            break;
+          }
+      launch_remat(c_->d.dtype, dm.head_dim, c_->d.rope_layout, delta, copy_v, a, s_);
+      KVM_HIP(hipGetLastError());
+    }
     return KVM_OK;
   }
 
@@ -671,9 +683,14 @@ static int rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32_t* n_se
   // 2. Validate, plan and queue; a failure part way is rolled back.
   const kvm_dims& dm = c->d.dims;
   RematArgs a{};
-  a.rows_per_page = dm.n_layers * dm.n_kv_heads * B;
-  const int units = remat_units(dtype_bytes(c->d.dtype));
-  a.wg_per_job = (dm.n_layers * dm.n_kv_heads + units - 1) / units;
+  // work items per page: one 16-byte piece (interleaved pairs) or one piece
+  // pair (half-split pairs) of every row
+  const int32_t R = remat_units_per_item(dtype_bytes(c->d.dtype));
+  a.units = dm.n_layers * dm.n_kv_heads;
+  const int64_t ppr = (int64_t)dm.head_dim * dtype_bytes(c->d.dtype) / 16;
+  a.items = (int64_t)((a.units + R - 1) / R) * B * (c->d.rope_layout == 0 ? ppr : ppr / 2);
+  a.wg_k = (int32_t)((a.items + 255) / 256);
+  a.wg_v = (int32_t)((c->page_bytes / 16 + 255) / 256);
   a.page_bytes = c->page_bytes;
   a.k_view = (char*)c->d.k_view;
   a.v_view = (char*)c->d.v_view;

@@ -80,7 +80,7 @@ typedef struct {
   int32_t block_tokens; /* B: tokens per logical block (32) */
 } kvm_dims;
 
-/* Version of this interface (major*100 + minor): 102. */
+/* Version of this interface (major*100 + minor): 103. */
 int kvm_version(void);
 
 /* Text of the last error on the calling thread ("" if none). */
@@ -391,6 +391,28 @@ typedef struct {
 int kvm_tier_simulate(const kvm_tier_policy* policy, int32_t n_steps, const int64_t* new_off,
                       const int32_t* new_blk, const int64_t* sel_off, const int32_t* sel_blk,
                       const int64_t* miss_off, const int32_t* miss_blk, int32_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* Measured rates (measurement aid; not on the hot path). Runs one untimed and
+ * one timed kernel on `stream`, waits for them and returns in *rate:
+ *  KVM_RATE_COPY       bytes read + written per second by a STREAM-style copy
+ *                      of n bytes from scratch to scratch + n (n a multiple of
+ *                      16, scratch >= 2n bytes, device, 16-byte aligned);
+ *  KVM_RATE_MFMA_BF16  bf16 matrix flop/s of a register-only
+ *                      v_mfma_f32_32x32x16_bf16 loop, n iterations of two
+ *                      MFMAs per wave (8 waves per SIMD);
+ *  KVM_RATE_EXP        v_exp_f32 results per second, n iterations of eight;
+ *  KVM_RATE_SCORE_MIX  score elements per second of the score passes'
+ *                      instruction mix (per MFMA: two fused scale-and-shifts,
+ *                      two exps, two adds; 128 elements per MFMA and wave; two
+ *                      waves per SIMD), n iterations of two such slots.
+ * The ALU kinds write one float per thread to scratch (>= 2 MiB). Errors:
+ * KVM_EINVAL, KVM_EHIP. The figures bound what the score passes (MFMA and
+ * VALU), Mean-K build and rematerialization (HBM) can reach on this GPU. */
+enum { KVM_RATE_COPY = 0, KVM_RATE_MFMA_BF16 = 1, KVM_RATE_EXP = 2, KVM_RATE_SCORE_MIX = 3 };
+
+int kvm_measure_rate(int32_t kind, int64_t n, void* scratch, size_t scratch_bytes, double* rate,
+                     void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (tracing aid). While enabled, every kernel launch of the

@@ -1167,3 +1167,33 @@ def test_failed_gather_rolls_back_and_a_retry_is_exact(k, dev):
     assert st["hits"] == 16 and st["misses"] == 80
     gc.check_view(wl, s, pool.page.cpu().numpy()[:96], pool)
     pool.ctx.close()
+
+
+# ------------------------------------------------------- measured rates ----
+
+def test_measure_rate_kinds(k, dev):
+    """kvm_measure_rate: the copy moves the bytes it claims (scratch + n holds
+    scratch's first n bytes), every rate is finite and within the physically
+    possible range for one MI355X (below its datasheet peaks, above a tenth of
+    them), and malformed requests return KVM_EINVAL."""
+    import torch
+    n = 64 << 20
+    scratch = torch.zeros(2 * n, dtype=torch.uint8, device=dev)
+    scratch[:n] = torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev)
+    r = k.kvm_measure_rate(k.KVM_RATE_COPY, n, scratch)
+    torch.cuda.synchronize()
+    assert torch.equal(scratch[n:], scratch[:n])
+    assert 0.8e12 < r < 8.0e12
+    sink = torch.empty(4 << 20, dtype=torch.uint8, device=dev)
+    assert 0.25e15 < k.kvm_measure_rate(k.KVM_RATE_MFMA_BF16, 2000, sink) < 2.5e15
+    # v_exp_f32 on 64 lanes at 2.4 GHz on 1024 SIMDs: at most 1024 * 2.4e9 * 64 / 4
+    assert 1e12 < k.kvm_measure_rate(k.KVM_RATE_EXP, 2000, sink) < 1024 * 2.4e9 * 16
+    # the mix's MFMA work alone bounds its score rate: 128 elements per 32 cycles
+    mix = k.kvm_measure_rate(k.KVM_RATE_SCORE_MIX, 4000, sink)
+    assert 0.5e12 < mix < 1024 * 2.4e9 * 128 / 32
+    for kind, nn, buf in ((7, 16, sink), (k.KVM_RATE_COPY, 17, scratch),
+                          (k.KVM_RATE_COPY, 2 * n, scratch), (k.KVM_RATE_EXP, 0, sink),
+                          (k.KVM_RATE_EXP, 10, sink[:1024])):
+        with pytest.raises(k.KvmError) as e:
+            k.kvm_measure_rate(kind, nn, buf)
+        assert e.value.code == k.api._abi.KVM_EINVAL
