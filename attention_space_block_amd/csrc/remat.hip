@@ -236,10 +236,10 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, b
 // mode) and its V into the V view page, byte for byte. A launch takes up to
 // REG_MAX blocks; their pages travel in the kernel arguments, so a launch
 // needs no upload and leaves no buffer behind whose reuse would have to wait
-// for it. Each workgroup copies one REG_CHUNK of K and of V of one block,
-// every thread sixteen 16-byte pieces of each, all loads before the stores.
+// for it. Grid: x = 4 KiB stretch of the page, y = block; each thread copies
+// one 16-byte piece of K and the same piece of V (the copy shape that moves
+// bytes fastest here, as in the remat kernel).
 static constexpr int REG_MAX = 448;
-static constexpr int64_t REG_CHUNK = 64 * 1024;
 
 struct RegCopyArgs {
   const char* k_src;
@@ -248,37 +248,19 @@ struct RegCopyArgs {
   char* v_dst;
   int64_t stride;
   int64_t page_bytes;        // a multiple of 16
-  int32_t wg_per_page;       // ceil(page_bytes / REG_CHUNK)
   int32_t n;
   int32_t slot[REG_MAX];
 };
 
 __global__ __launch_bounds__(256) void register_copy_kernel(RegCopyArgs a) {
-  constexpr int PER = (int)(REG_CHUNK / (256 * 16));
-  const int32_t i = blockIdx.x / a.wg_per_page;
-  if (i >= a.n) return;
-  const int64_t base = (int64_t)(blockIdx.x % a.wg_per_page) * REG_CHUNK;
-  const char* ks = a.k_src + (int64_t)i * a.stride;
-  const char* vs = a.v_src + (int64_t)i * a.stride;
-  char* kd = a.k_dst + (int64_t)a.slot[i] * a.page_bytes;
-  char* vd = a.v_dst + (int64_t)a.slot[i] * a.page_bytes;
-  uint4 k[PER], v[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t off = base + ((int64_t)u * 256 + threadIdx.x) * 16;
-    if (off < a.page_bytes) {
-      k[u] = ld_plain(ks + off);
-      v[u] = ld_plain(vs + off);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int64_t off = base + ((int64_t)u * 256 + threadIdx.x) * 16;
-    if (off < a.page_bytes) {
-      st_plain(kd + off, k[u]);
-      st_plain(vd + off, v[u]);
-    }
-  }
+  const int32_t i = (int32_t)blockIdx.y;
+  const int64_t off = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (i >= a.n || off >= a.page_bytes) return;
+  const uint4 k = ld_plain(a.k_src + (int64_t)i * a.stride + off);
+  const uint4 v = ld_plain(a.v_src + (int64_t)i * a.stride + off);
+  const int64_t page = (int64_t)a.slot[i] * a.page_bytes;
+  st_plain(a.k_dst + page + off, k);
+  st_plain(a.v_dst + page + off, v);
 }
 
 // Run f(w) for w in [0, n) on up to n threads; a share whose thread cannot be
@@ -600,14 +582,14 @@ static int ctx_register(kvm_ctx* c, const int64_t* ids, int64_t n, const void* k
     a.v_dst = vdst;
     a.stride = block_stride;
     a.page_bytes = c->page_bytes;
-    a.wg_per_page = (int32_t)((c->page_bytes + REG_CHUNK - 1) / REG_CHUNK);
+    const uint32_t parts = (uint32_t)((c->page_bytes / 16 + 255) / 256);
     KernelTimer tm("register_copy", s);
     for (; at < n && e == hipSuccess; at += REG_MAX) {
       a.n = (int32_t)std::min<int64_t>(REG_MAX, n - at);
       a.k_src = (const char*)k_raw + at * block_stride;
       a.v_src = (const char*)v_raw + at * block_stride;
       for (int32_t j = 0; j < a.n; ++j) a.slot[j] = slots[(size_t)(at + j)];
-      register_copy_kernel<<<dim3((uint32_t)a.n * (uint32_t)a.wg_per_page), dim3(256), 0, s>>>(a);
+      register_copy_kernel<<<dim3(parts, (uint32_t)a.n), dim3(256), 0, s>>>(a);
       e = hipGetLastError();
     }
   } else {
