@@ -46,6 +46,18 @@ static constexpr int32_t REMAT_JOBS_PER_LAUNCH = 16384;
 #ifndef KVM_REMAT_R_BF16
 #define KVM_REMAT_R_BF16 1
 #endif
+// Threads per workgroup of the remat and registration copies: one wavefront.
+// Timed at the 1M-token view (4096 jobs of 4 MiB pages): 64 threads 8.26 ms,
+// 256 threads 8.81 ms; a plain device copy moves 6.4 TB/s in 64-thread
+// workgroups against 6.1 in 256-thread ones.
+static constexpr int REMAT_TPB = 64;
+// Page loads from a buffer other than the one written are non-temporal
+// (8.16 ms against 8.26 for the view above); the in-place delta rotation keeps
+// plain loads (5.47 ms against 5.74 non-temporal).
+template <bool NT>
+__device__ __forceinline__ uint4 ld_page(const void* p) {
+  return NT ? ld_nt(p) : ld_plain(p);
+}
 static constexpr int remat_units_per_item(int elem_bytes) {
   return elem_bytes == 1 ? KVM_REMAT_R_FP8 : elem_bytes == 2 ? KVM_REMAT_R_BF16 : 1;
 }
@@ -54,8 +66,8 @@ struct RematArgs {
   const RematJob* jobs;
   int32_t n_jobs;
   int32_t first_v;           // jobs [first_v, n_jobs) may copy V (each checks its flag)
-  int32_t wg_k;              // workgroups per job for K: ceil(items per page / 256)
-  int32_t wg_v;              // workgroups per job for V: ceil(page_bytes / 16 / 256)
+  int32_t wg_k;              // workgroups per job for K: ceil(items per page / REMAT_TPB)
+  int32_t wg_v;              // workgroups per job for V: ceil(page_bytes / 16 / REMAT_TPB)
   int64_t items;             // K work items per page (one piece or one piece pair, in
                              // R units: ceil(units / R) * 32 * items per row)
   int32_t units;             // (l, g) units per page: L * Hkv
@@ -121,13 +133,14 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
 // pages of jobs [first_v, n_jobs) that carry JOB_COPY_V (workgroups are
 // dispatched x first, so no division maps a workgroup to its job). The
 // workgroups in flight then cover one narrow stretch of each page, which the
-// DRAM serves best (a plain copy in this shape moves about 6.1 TB/s, against
-// 3.6 TB/s when each thread loads sixteen pieces before storing them); each
-// thread reads the (cos, sin) of its pairs from the fp32 table (L2-resident:
-// 32 positions of a job span at most 32 table rows). Loads and stores are
-// plain (cached) ones, faster here than the non-temporal forms.
+// DRAM serves best (a plain copy in this shape moves about 6.1-6.6 TB/s,
+// against 3.6 TB/s when each thread loads sixteen pieces before storing them);
+// each thread reads the (cos, sin) of its pairs from the fp32 table
+// (L2-resident: 32 positions of a job span at most 32 table rows). Stores are
+// plain (cached); page loads are non-temporal except in the in-place delta
+// rotation (see ld_page).
 template <typename T, int D, int LAYOUT, bool DELTA, bool COPYV>
-__global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
+__global__ __launch_bounds__(REMAT_TPB) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
   constexpr int ROW_BYTES = D * sizeof(T);
   constexpr int PPR = ROW_BYTES / 16;            // pieces per row
@@ -143,9 +156,9 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
     if (jid >= a.n_jobs || (int32_t)part >= a.wg_v) return;
     const RematJob job = a.jobs[jid];
     if ((job.flags & JOB_COPY_V) == 0) return;
-    const int64_t off = ((int64_t)part * 256 + threadIdx.x) * 16;
+    const int64_t off = ((int64_t)part * REMAT_TPB + threadIdx.x) * 16;
     if (off >= a.page_bytes) return;
-    st_plain(a.v_view + (int64_t)job.slot * a.page_bytes + off, ld_plain(job.src_v + off));
+    st_plain(a.v_view + (int64_t)job.slot * a.page_bytes + off, ld_page<true>(job.src_v + off));
     // keeps this path's store its own: merged with the K path's stores, the
     // compiler splits every 16-byte store into a 4- and a 12-byte one
     asm volatile("" ::: "memory");
@@ -153,7 +166,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
   }
   if ((int32_t)part >= a.wg_k) return;
   const RematJob job = a.jobs[blockIdx.y];
-  const uint32_t item = part * 256 + threadIdx.x;
+  const uint32_t item = part * REMAT_TPB + threadIdx.x;
   if ((int64_t)item >= a.items) return;
   // item -> (group of R (l, g) units, token j, piece p): the thread rotates
   // piece p of token row j in each unit of the group with the same (cos, sin)
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
     if (R > 1 && unit0 + u >= a.units) break;
     const int64_t row = (int64_t)(unit0 + u) * 32 + j;
     const int64_t b0 = row * ROW_BYTES + (int64_t)p * 16;
-    const uint4 k0 = ld_plain(job.src_k + b0);
+    const uint4 k0 = ld_page<!DELTA>(job.src_k + b0);
     float x0[P], y0[P];
     unpack<T>(k0, x0);
     if (LAYOUT == 0) {
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(256) void remat_kernel(RematArgs a) {
       st_plain(kv + b0, pack<T>(y0));
     } else {
       const int64_t b1 = b0 + HALF * (int64_t)sizeof(T);
-      const uint4 k1 = ld_plain(job.src_k + b1);
+      const uint4 k1 = ld_page<!DELTA>(job.src_k + b1);
       float x1[P], y1[P];
       unpack<T>(k1, x1);
 #pragma unroll
@@ -209,7 +222,7 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, b
                          const RematArgs& a, hipStream_t s) {
   const int32_t rows = a.n_jobs + (copy_v ? a.n_jobs - a.first_v : 0);
   if (a.n_jobs <= 0 || rows <= 0) return;
-  dim3 g((uint32_t)std::max(a.wg_k, copy_v ? a.wg_v : 0), (uint32_t)rows), b(256);
+  dim3 g((uint32_t)std::max(a.wg_k, copy_v ? a.wg_v : 0), (uint32_t)rows), b(REMAT_TPB);
   KernelTimer tm("remat", s);
 #define KVM_REMAT(T, D, LAY)                                                 \
   do {                                                                       \
@@ -236,7 +249,7 @@ static void launch_remat(int32_t dtype, int32_t d, int32_t layout, bool delta, b
 // mode) and its V into the V view page, byte for byte. A launch takes up to
 // REG_MAX blocks; their pages travel in the kernel arguments, so a launch
 // needs no upload and leaves no buffer behind whose reuse would have to wait
-// for it. Grid: x = 4 KiB stretch of the page, y = block; each thread copies
+// for it. Grid: x = 1 KiB stretch of the page, y = block; each thread copies
 // one 16-byte piece of K and the same piece of V (the copy shape that moves
 // bytes fastest here, as in the remat kernel).
 static constexpr int REG_MAX = 448;
@@ -252,12 +265,12 @@ struct RegCopyArgs {
   int32_t slot[REG_MAX];
 };
 
-__global__ __launch_bounds__(256) void register_copy_kernel(RegCopyArgs a) {
+__global__ __launch_bounds__(REMAT_TPB) void register_copy_kernel(RegCopyArgs a) {
   const int32_t i = (int32_t)blockIdx.y;
-  const int64_t off = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  const int64_t off = ((int64_t)blockIdx.x * REMAT_TPB + threadIdx.x) * 16;
   if (i >= a.n || off >= a.page_bytes) return;
-  const uint4 k = ld_plain(a.k_src + (int64_t)i * a.stride + off);
-  const uint4 v = ld_plain(a.v_src + (int64_t)i * a.stride + off);
+  const uint4 k = ld_page<true>(a.k_src + (int64_t)i * a.stride + off);
+  const uint4 v = ld_page<true>(a.v_src + (int64_t)i * a.stride + off);
   const int64_t page = (int64_t)a.slot[i] * a.page_bytes;
   st_plain(a.k_dst + page + off, k);
   st_plain(a.v_dst + page + off, v);
@@ -582,14 +595,14 @@ static int ctx_register(kvm_ctx* c, const int64_t* ids, int64_t n, const void* k
     a.v_dst = vdst;
     a.stride = block_stride;
     a.page_bytes = c->page_bytes;
-    const uint32_t parts = (uint32_t)((c->page_bytes / 16 + 255) / 256);
+    const uint32_t parts = (uint32_t)((c->page_bytes / 16 + REMAT_TPB - 1) / REMAT_TPB);
     KernelTimer tm("register_copy", s);
     for (; at < n && e == hipSuccess; at += REG_MAX) {
       a.n = (int32_t)std::min<int64_t>(REG_MAX, n - at);
       a.k_src = (const char*)k_raw + at * block_stride;
       a.v_src = (const char*)v_raw + at * block_stride;
       for (int32_t j = 0; j < a.n; ++j) a.slot[j] = slots[(size_t)(at + j)];
-      register_copy_kernel<<<dim3(parts, (uint32_t)a.n), dim3(256), 0, s>>>(a);
+      register_copy_kernel<<<dim3(parts, (uint32_t)a.n), dim3(REMAT_TPB), 0, s>>>(a);
       e = hipGetLastError();
     }
   } else {
@@ -671,8 +684,8 @@ static int rematerialize(kvm_ctx* c, const int32_t* sel_dev, const int32_t* n_se
   a.units = dm.n_layers * dm.n_kv_heads;
   const int64_t ppr = (int64_t)dm.head_dim * dtype_bytes(c->d.dtype) / 16;
   a.items = (int64_t)((a.units + R - 1) / R) * B * (c->d.rope_layout == 0 ? ppr : ppr / 2);
-  a.wg_k = (int32_t)((a.items + 255) / 256);
-  a.wg_v = (int32_t)((c->page_bytes / 16 + 255) / 256);
+  a.wg_k = (int32_t)((a.items + REMAT_TPB - 1) / REMAT_TPB);
+  a.wg_v = (int32_t)((c->page_bytes / 16 + REMAT_TPB - 1) / REMAT_TPB);
   a.page_bytes = c->page_bytes;
   a.k_view = (char*)c->d.k_view;
   a.v_view = (char*)c->d.v_view;
