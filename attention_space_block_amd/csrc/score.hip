@@ -839,7 +839,7 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
   }
   const char* base = reinterpret_cast<const char*>(a.index) + (int64_t)lg * a.lg_stride * sizeof(E);
   float* Sl = a.S + ((int64_t)lg * a.n_blocks + a.b_first) * a.TG;
-  extern __shared__ float stg_all[];           // STAGE: [4 waves][16*TU rows][TG]
+  extern __shared__ __attribute__((aligned(16))) float stg_all[];   // STAGE: [4 waves][16*TU rows][TG]
   float* stg = stg_all + wave * (16 * TU) * a.TG;
   // online (shift, sum-exp) of the lane's query rows over its scores
   float m_run[MAXCT], s_run[MAXCT];
@@ -898,7 +898,17 @@ __global__ __launch_bounds__(256) void score_stored_pass1_mfma(StoredArgs a) {
       const int32_t nrows = r_end - r0 < 16 * TU ? r_end - r0 : 16 * TU;
       const int n = nrows * a.TG;
       float* dst = Sl + (int64_t)r0 * a.TG;
-      for (int i = lane; i < n; i += 64) dst[i] = stg[i];
+      // 16-byte stores where the span starts 16-byte aligned (uniform: N*T*G
+      // a multiple of 4; every wave's LDS rows start 16-byte aligned), else
+      // 4-byte ones: 8.59-8.66 ms against 8.66-8.71 at 10M tokens
+      if (((uintptr_t)dst & 15) == 0) {
+        const int n4 = n >> 2;
+        for (int i = lane; i < n4; i += 64)
+          reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(stg)[i];
+        for (int i = 4 * n4 + lane; i < n; i += 64) dst[i] = stg[i];
+      } else {
+        for (int i = lane; i < n; i += 64) dst[i] = stg[i];
+      }
       __builtin_amdgcn_wave_barrier();
     }
   }
