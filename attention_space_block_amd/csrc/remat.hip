@@ -39,9 +39,10 @@ namespace kvm {
 static constexpr int32_t REMAT_JOBS_PER_LAUNCH = 16384;
 // (l, g) units a K work item covers with one load of its (cos, sin): FP8
 // pieces hold 8 pairs, so one unit per item would read 64 bytes of table per
-// 16 bytes of K
+// 16 bytes of K. FP8 view of the 1M-token workspace with one-wavefront
+// workgroups: R = 2 4.26 ms, 4 4.19-4.26, 8 4.33-4.44, 16 4.49.
 #ifndef KVM_REMAT_R_FP8
-#define KVM_REMAT_R_FP8 8
+#define KVM_REMAT_R_FP8 4
 #endif
 #ifndef KVM_REMAT_R_BF16
 #define KVM_REMAT_R_BF16 1

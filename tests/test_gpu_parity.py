@@ -633,6 +633,19 @@ def test_remat_half_split_pairs_match_oracle(k, dev, name, scale, src):
     _remat_two_steps(k, dev, wl, src)
 
 
+@pytest.mark.parametrize("layout,src", [(0, "device"), (1, "pinned"), (0, "gather")])
+def test_fp8_remat_partial_unit_groups_match_oracle(k, dev, layout, src):
+    """FP8 pages with 3 layers x 2 KV heads = 6 (layer, KV head) units: an FP8
+    work item rotates its piece in several units per (cos, sin) read, so its
+    last group here holds fewer units than the others. The two
+    rematerialization steps against the oracle, both pairings."""
+    wl = synth.get_workload("ctx64k_fp8").scaled(n_layers=3, n_kv_heads=2, n_q_heads=4,
+                                                 budget_blocks=96, n_recent=8,
+                                                 rope_layout=layout)
+    say("fp8 partial unit groups", layout, src)
+    _remat_two_steps(k, dev, wl, src)
+
+
 def _remat_two_steps(k, dev, wl, src):
     """Two rematerializations of a 96-block view over 130 pages: all misses,
     then a selection that keeps about half of the view (hits stay in place,
@@ -741,16 +754,23 @@ def test_delta_rerope_bounded_and_rebuilt(k, dev, src, layout):
     pool.ctx.close()
 
 
-def test_delta_rerope_fp8_pages_bounded(k, dev):
+@pytest.mark.parametrize("scale", [
+    {"n_layers": 2},
+    {"n_layers": 3, "n_kv_heads": 2, "n_q_heads": 4},   # 6 units: a partial unit group
+])
+def test_delta_rerope_fp8_pages_bounded(k, dev, scale):
     """Bounded delta re-RoPE over FP8 E4M3 pages (limit 2): the same tracked
     placements as the bf16 test. Each in-place rotation decodes E4M3 exactly,
     rotates in fp32 and stores one E4M3 value, so a pair's error after n deltas
     stays within (n + 1) half-spacings of E4M3 at the pair's length (subnormal
     spacing 2^-9 below 2^-6), plus the fp32 rotation's error; rebuilds from raw
-    K are within half a spacing of the exact value. V stays byte-exact."""
+    K are within half a spacing of the exact value. V stays byte-exact. The
+    second shape has 6 (layer, KV head) units, not a multiple of the units an
+    FP8 work item rotates per table read."""
     import torch
     from oracle import bounded_delta_rope, rope_rotate
-    wl = synth.get_workload("ctx64k_fp8").scaled(n_layers=2)
+    wl = synth.get_workload("ctx64k_fp8").scaled(**scale)
+    say("fp8 delta", scale)
     N, B, limit = 64, wl.block_tokens, 2
     pool, keep = _remat_setup(k, dev, wl, N, 40, "device", batch=4, staging=8,
                               delta_limit=limit, max_pos=N * B)
