@@ -25,7 +25,8 @@ EXPORTED = [
     "kvm_select_ws_bytes", "kvm_select", "kvm_select_noalloc", "kvm_ctx_create", "kvm_ctx_destroy",
     "kvm_ctx_set_source", "kvm_ctx_set_gather", "kvm_ctx_register_resident",
     "kvm_ctx_register_resident_list",
-    "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_block_state",
+    "kvm_ctx_build_index_rope", "kvm_rematerialize", "kvm_ctx_sync", "kvm_ctx_set_serialized",
+    "kvm_ctx_block_state",
     "kvm_ctx_block_deltas", "kvm_ctx_evict", "kvm_tier_simulate", "kvm_quantize_e4m3",
     "kvm_profile_enable", "kvm_profile_read", "kvm_measure_rate",
 ]
@@ -109,6 +110,7 @@ def lib():
             "kvm_ctx_build_index_rope": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
             "kvm_rematerialize": (ctypes.c_int, [vp, vp, vp, vp, ctypes.POINTER(RematStats), vp]),
             "kvm_ctx_sync": (ctypes.c_int, [vp]),
+            "kvm_ctx_set_serialized": (ctypes.c_int, [vp, ctypes.c_int32]),
             "kvm_ctx_block_state": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32),
                                                    ctypes.POINTER(i32)]),
             "kvm_ctx_block_deltas": (ctypes.c_int, [vp, i64, ctypes.POINTER(i32)]),

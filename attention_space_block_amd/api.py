@@ -242,6 +242,10 @@ class KvmCtx:
     def kvm_ctx_sync(self) -> None:
         _abi.check(_abi.lib().kvm_ctx_sync(self._h), "kvm_ctx_sync")
 
+    def kvm_ctx_set_serialized(self, on: bool) -> None:
+        _abi.check(_abi.lib().kvm_ctx_set_serialized(self._h, 1 if on else 0),
+                   "kvm_ctx_set_serialized")
+
     def kvm_ctx_block_state(self, block: int):
         s, p = ctypes.c_int32(), ctypes.c_int32()
         _abi.check(_abi.lib().kvm_ctx_block_state(self._h, block, ctypes.byref(s), ctypes.byref(p)),

@@ -38,6 +38,6 @@ int check_dims(const kvm_dims* d, int32_t dtype) {
 
 }  // namespace kvm
 
-extern "C" int kvm_version(void) { return 103; }
+extern "C" int kvm_version(void) { return 104; }
 
 extern "C" const char* kvm_last_error(void) { return kvm::last_error(); }

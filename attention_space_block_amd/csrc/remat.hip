@@ -307,6 +307,7 @@ struct kvm_ctx {
   int32_t* h_page = nullptr;         // pinned [n_slots]
   hipStream_t side = nullptr;        // H2D of K pages (and of gathered pages)
   hipStream_t side_v = nullptr;      // H2D of V pages from pinned sources
+  bool serialized = false;           // debug: every copy on the caller's stream
   std::vector<hipEvent_t> events;    // data-plane events (ids of dataplane.cpp)
   char* ring = nullptr;              // pinned [2][staging/2][2][page]
   std::unique_ptr<kvm::WorkerPool> workers;
@@ -399,7 +400,10 @@ class HipEngine final : public Engine {
   }
 
  private:
-  hipStream_t st(int id) const { return id == MAIN ? s_ : id == SIDE_K ? c_->side : c_->side_v; }
+  hipStream_t st(int id) const {
+    if (id == MAIN || c_->serialized) return s_;
+    return id == SIDE_K ? c_->side : c_->side_v;
+  }
   kvm_ctx* c_;
   hipStream_t s_;
   RematArgs a_;
@@ -782,6 +786,18 @@ extern "C" int kvm_ctx_sync(kvm_ctx* c) {
     KVM_CHECK_ARG(c, "ctx is NULL");
     KVM_HIP(hipStreamSynchronize(c->side));
     KVM_HIP(hipStreamSynchronize(c->side_v));
+    return KVM_OK;
+  });
+}
+
+extern "C" int kvm_ctx_set_serialized(kvm_ctx* c, int32_t on) {
+  using namespace kvm;
+  return guarded([&]() -> int {
+    KVM_CHECK_ARG(c, "ctx is NULL");
+    // earlier side-stream copies must not overlap work of the other mode
+    KVM_HIP(hipStreamSynchronize(c->side));
+    KVM_HIP(hipStreamSynchronize(c->side_v));
+    c->serialized = on != 0;
     return KVM_OK;
   });
 }

@@ -80,7 +80,7 @@ typedef struct {
   int32_t block_tokens; /* B: tokens per logical block (32) */
 } kvm_dims;
 
-/* Version of this interface (major*100 + minor): 103. */
+/* Version of this interface (major*100 + minor): 104. */
 int kvm_version(void);
 
 /* Text of the last error on the calling thread ("" if none). */
@@ -346,6 +346,16 @@ int kvm_rematerialize(kvm_ctx* ctx, const int32_t* sel_dev, const int32_t* n_sel
 
 /* Wait for the ctx's side-stream work (H2D batches). */
 int kvm_ctx_sync(kvm_ctx* ctx);
+
+/* Debug aid (race detection). With on != 0, later kvm_rematerialize calls
+ * issue every host-to-device copy on the caller's stream, in issue order,
+ * instead of the two side streams, so no copy runs alongside a kernel (each
+ * copy is issued before the wait and the kernel that consume it, so the
+ * order stays valid). The view, page table and stats must come out identical
+ * to the overlapped mode's: a difference points at a missing wait. Slower
+ * (no H2D/compute overlap). The call first waits for the ctx's side streams.
+ * Errors: KVM_EINVAL (ctx NULL), KVM_EHIP. */
+int kvm_ctx_set_serialized(kvm_ctx* ctx, int32_t on);
 
 /* Inspection: pool page of `block` (or -1) and its baked compact position
  * (-1 = K page stale). */

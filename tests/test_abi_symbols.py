@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     exported = set(re.findall(r"\b(kvm_\w+)$", out, flags=re.M))
     assert declared() <= exported
     assert set(k.EXPORTED) == declared()
-    assert k.kvm_version() == 103
+    assert k.kvm_version() == 104
 
 
 def test_validation_errors_need_no_gpu():

@@ -588,6 +588,53 @@ def _remat_setup(k, dev, wl, N, n_slots, src="device", batch=64, staging=0, delt
     return pool, keep
 
 
+@pytest.mark.parametrize("src,delta", [("pinned", 0), ("gather", 0), ("pinned", 2)])
+def test_serialized_copies_give_identical_views(k, dev, src, delta):
+    """Race check (KVMem Fig. 3: staged copies overlap the re-encode): three
+    rematerializations (all misses; about half of the view kept; half of that
+    kept again) on two fresh pools, one with the H2D batches on the side
+    streams and one with every copy on the caller's stream
+    (kvm_ctx_set_serialized). Stats, page tables and every K and V page of the
+    views agree byte for byte; without delta mode the serialized views also
+    match the oracle."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, budget_blocks=96, n_recent=8)
+    N, B = 400, wl.block_tokens
+    say("serialized vs overlapped", src, delta)
+    sels = []
+    keep_from = None
+    for t in range(3):
+        R = synth.scores_f32(31 + t, N)
+        if keep_from is not None:
+            R[keep_from] += 10.0
+        sel, n_sel, _ = gc.select_dev(k, gc.to_dev(R, dev), N, wl.n_sink, wl.n_recent,
+                                      wl.budget_blocks, dev)
+        s = sel.cpu().numpy()[:int(n_sel.item())]
+        sels.append((sel, n_sel, s))
+        keep_from = s[t % 2::2]
+    runs = []
+    for serialized in (False, True):
+        pool, keep = _remat_setup(k, dev, wl, N, 130, src, batch=16, staging=32,
+                                  delta_limit=delta, max_pos=N * B)
+        pool.ctx.kvm_ctx_set_serialized(serialized)
+        out = []
+        for sel, n_sel, s in sels:
+            st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+            torch.cuda.synchronize()
+            pg = pool.page.cpu().numpy()[:len(s)].copy()
+            idx = torch.as_tensor(pg.astype(np.int64), device=dev)
+            out.append((st, pg, pool.k_view[idx].cpu().numpy(), pool.v_view[idx].cpu().numpy()))
+        if serialized and delta == 0:
+            gc.check_view(wl, sels[-1][2], out[-1][1], pool)
+        pool.ctx.close()
+        runs.append(out)
+    for t, (a, b) in enumerate(zip(*runs)):
+        assert a[0] == b[0], (t, a[0], b[0])
+        assert np.array_equal(a[1], b[1]), t
+        assert np.array_equal(a[2], b[2]) and np.array_equal(a[3], b[3]), t
+    assert runs[0][1][0]["hits"] > 0 and runs[0][2][0]["misses"] > 0
+
+
 @pytest.mark.parametrize("name,src", [("ctx64k", "device"), ("ctx64k", "pinned"),
                                       ("ctx64k", "gather"), ("ctx64k_fp8", "device"),
                                       ("ctx64k_fp8", "pinned"), ("ctx64k_fp8", "gather")])
