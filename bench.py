@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-pairs", type=int, default=6,
                     help="(layer, KV head) pairs in the CPU oracle sample")
     ap.add_argument("--workload", default="ws1m", choices=["ws1m", "ctx64k", "churn", "ws10m"])
+    ap.add_argument("--host-tiled", type=int, default=1,
+                    help="10M-token workspace: also run the host-tiled legs (0: resident "
+                         "legs only, as for its counter runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="first run a plain device copy of 2 GiB (counter calibration)")
     return ap.parse_args()
@@ -408,11 +411,11 @@ def source_fingerprint(path: str) -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def counter_traffic() -> dict:
-    """HBM bytes per dispatch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, per kernel; a kernel whose source code (comments aside) changed
-    since the counters were taken maps to None."""
-    path = os.path.join(ROOT, "profiles", "ws1m_traffic.json")
+def counter_traffic(name: str = "ws1m_traffic.json") -> dict:
+    """HBM bytes per dispatch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (profiles/<name>), per kernel; a kernel whose source code (comments
+    aside) changed since the counters were taken maps to None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return {}
     data = json.load(open(path))
@@ -430,6 +433,8 @@ def counter_traffic() -> dict:
 SCORE_KERNEL_TAIL = "<unsigned short, 128>"
 REMAT_VIEW_KERNEL = ("remat_kernel", "<unsigned short, 128, 0, false, true>")
 REMAT_DELTA_KERNEL = ("remat_kernel", "<unsigned short, 128, 0, true, false>")
+# stored-score pass 1 of the 10M-token workspace: bf16, d = 128, LDS-staged stores
+STORED_KERNEL_TAIL = "<unsigned short, 128, true>"
 
 
 def traffic_for(traffic: dict, short: str, tail: str | None = None):
@@ -667,9 +672,11 @@ def run_ws10m(args, k, wl, dev):
         out = scores.clone()
         del ws
         return ms, {n: {"launches": c, "avg_ms": t / c} for n, (c, t) in prof.items()}, out
+    tiled = bool(args.host_tiled)
     ms_res, kern_res, r_res = leg(k.KVM_INDEX_DEVICE)
-    ms_til, kern_til, r_til = leg(k.KVM_INDEX_HOST_TILED)
-    assert torch.equal(r_res, r_til), "resident and host-tiled scores differ"
+    if tiled:
+        ms_til, kern_til, r_til = leg(k.KVM_INDEX_HOST_TILED)
+        assert torch.equal(r_res, r_til), "resident and host-tiled scores differ"
     # FP8 scoring ablation: the same index and query encoded to E4M3 on the GPU;
     # the host tiles reuse the pinned buffer (tile-major, 1 byte per element)
     i8 = torch.empty((nlg, N, d), dtype=torch.uint8, device=dev)
@@ -681,8 +688,9 @@ def run_ws10m(args, k, wl, dev):
         nb = min(tb, N - t * tb)
         h8[t, :, :nb, :].copy_(i8[:, t * tb:t * tb + nb, :].cpu())
     ms_f8, kern_f8, r_f8 = leg(k.KVM_INDEX_DEVICE, k.KVM_FP8_E4M3, q8, i8, h8)
-    ms_f8t, kern_f8t, r_f8t = leg(k.KVM_INDEX_HOST_TILED, k.KVM_FP8_E4M3, q8, i8, h8)
-    assert torch.equal(r_f8, r_f8t), "resident and host-tiled FP8 scores differ"
+    if tiled:
+        ms_f8t, kern_f8t, r_f8t = leg(k.KVM_INDEX_HOST_TILED, k.KVM_FP8_E4M3, q8, i8, h8)
+        assert torch.equal(r_f8, r_f8t), "resident and host-tiled FP8 scores differ"
     f8_rel = float(((r_f8.double() - r_res.double()).abs() / r_res.double()).max())
     idx_bytes = N * nlg * d * 2
     s_bytes = 2 * N * L * Hq * 4            # stored scores written and read back
@@ -694,14 +702,14 @@ def run_ws10m(args, k, wl, dev):
            "kernels": kern_res}
     til = {"ms_per_step": ms_til, "blocks_per_s": N / (ms_til * 1e-3),
            "h2d_GBps": idx_bytes / (ms_til * 1e-3) / 1e9, "tile_bytes": nlg * tb * d * 2,
-           "kernels": kern_til}
+           "kernels": kern_til} if tiled else None
     f8p1 = kern_f8.get("score_stored_pass1", {}).get("avg_ms")
     fp8 = {"resident": {"ms_per_step": ms_f8, "blocks_per_s": N / (ms_f8 * 1e-3),
                         "pass1_GBps": (idx_bytes / 2 + s_bytes / 2) / (f8p1 * 1e-3) / 1e9
                         if f8p1 else None, "kernels": kern_f8},
            "host_tiled": {"ms_per_step": ms_f8t, "blocks_per_s": N / (ms_f8t * 1e-3),
                           "h2d_GBps": idx_bytes / 2 / (ms_f8t * 1e-3) / 1e9,
-                          "tile_bytes": nlg * tb * d, "kernels": kern_f8t},
+                          "tile_bytes": nlg * tb * d, "kernels": kern_f8t} if tiled else None,
            "max_rel_diff_vs_bf16": f8_rel}
     # the dominant kernel, stored-score pass 1, is HBM-bound: the index read once
     # plus the stored scores written
@@ -711,12 +719,14 @@ def run_ws10m(args, k, wl, dev):
     roof = None
     if p1:
         ach = res["pass1_GBps"]
+        traffic = counter_traffic("ws10m_traffic.json")
         roof = {"kernel": "score_stored_pass1", "bound": "hbm", "achieved": ach,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                "traffic": None, "frac_of_measured": ach / copy_gbps}
-    log(f"resident: {ms_res:.2f} ms/step; host-tiled: {ms_til:.1f} ms/step "
-        f"({til['h2d_GBps']:.1f} GB/s of index over PCIe); FP8 resident {ms_f8:.2f}, "
-        f"host-tiled {ms_f8t:.1f} ms/step")
+                "traffic": traffic_for(traffic, "score_stored_pass1_mfma", STORED_KERNEL_TAIL),
+                "frac_of_measured": ach / copy_gbps}
+    log(f"resident: {ms_res:.2f} ms/step; FP8 resident {ms_f8:.2f} ms/step" +
+        (f"; host-tiled: {ms_til:.1f} ms/step ({til['h2d_GBps']:.1f} GB/s of index over "
+         f"PCIe); FP8 host-tiled {ms_f8t:.1f} ms/step" if tiled else ""))
     print(json.dumps({
         "metric": "history blocks scored/s, 10M-token workspace", "value": N / (ms_res * 1e-3),
         "unit": "blocks/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -882,18 +892,27 @@ def summarize_rocprof(d: str) -> dict:
     return out
 
 
-KERNEL_SOURCES = {"score": "attention_space_block_amd/csrc/score.hip",
-                  "remat": "attention_space_block_amd/csrc/remat.hip",
-                  "build": "attention_space_block_amd/csrc/build_index.hip",
-                  "quantize": "attention_space_block_amd/csrc/quantize.hip",
-                  "sel": "attention_space_block_amd/csrc/select.hip"}
+# the library's kernels by name prefix (after "kvm::") and the file each is defined in
+KERNEL_SOURCES = {"score_": "attention_space_block_amd/csrc/score.hip",
+                  "remat_kernel": "attention_space_block_amd/csrc/remat.hip",
+                  "register_copy_kernel": "attention_space_block_amd/csrc/remat.hip",
+                  "build_index": "attention_space_block_amd/csrc/build_index.hip",
+                  "quantize_": "attention_space_block_amd/csrc/quantize.hip",
+                  "sel_": "attention_space_block_amd/csrc/select.hip",
+                  "select_": "attention_space_block_amd/csrc/select.hip",
+                  "probe_": "attention_space_block_amd/csrc/probe.hip"}
 
 
-def _source_of(kernel: str) -> str:
-    for key, path in KERNEL_SOURCES.items():
-        if key in kernel:
+def _source_of(kernel: str) -> str | None:
+    """Source file of a library kernel (None for kernels the library does not
+    define, e.g. the calibration copy)."""
+    if not kernel.startswith("kvm::"):
+        return None
+    name = kernel[len("kvm::"):]
+    for prefix, path in KERNEL_SOURCES.items():
+        if name.startswith(prefix):
             return path
-    return KERNEL_SOURCES["sel"]
+    return None
 
 
 def write_traffic_profile(value_dir: str, delta_dir: str, out_path: str) -> dict:
@@ -912,13 +931,35 @@ def write_traffic_profile(value_dir: str, delta_dir: str, out_path: str) -> dict
     per = {}
     for k, x in traffic.items():
         src = _source_of(k)
-        per[k] = dict(x, source=src, source_sha256_16=source_fingerprint(os.path.join(ROOT, src)))
+        if src:
+            per[k] = dict(x, source=src,
+                          source_sha256_16=source_fingerprint(os.path.join(ROOT, src)))
     out = {"workload": "1M-token workspace step (bench.py defaults; the delta-mode kernel from "
                        "the delta leg)", "calibration": v["calibration"], "per_dispatch": per}
     json.dump(out, open(out_path, "w"), indent=1)
     return out
 
+def write_traffic_profile_ws10m(run_dir: str, out_path: str) -> dict:
+    """profiles/ws10m_traffic.json: calibrated read/write bytes per dispatch of
+    the 10M-token workspace's resident legs (a run with --host-tiled 0), with
+    source fingerprints as above."""
+    v = json.load(open(os.path.join(run_dir, "summary.json")))
+    per = {}
+    for k, x in v["traffic"].items():
+        src = _source_of(k)
+        if src:
+            per[k] = dict(x, source=src,
+                          source_sha256_16=source_fingerprint(os.path.join(ROOT, src)))
+    out = {"workload": "10M-token workspace, resident index legs (bench.py --workload ws10m "
+                       "--host-tiled 0)", "calibration": v["calibration"], "per_dispatch": per}
+    json.dump(out, open(out_path, "w"), indent=1)
+    return out
+
+
 def main():
+    if len(sys.argv) > 3 and sys.argv[1] == "--write-traffic-ws10m":
+        write_traffic_profile_ws10m(sys.argv[2], sys.argv[3])
+        return
     if len(sys.argv) > 2 and sys.argv[1] == "--summarize-rocprof":
         print(json.dumps(summarize_rocprof(sys.argv[2])["calibration"]))
         return
@@ -935,12 +976,6 @@ def main():
     k._abi.lib()
     wl = synth.get_workload(args.workload)
     dev = torch.device("cuda:0")
-    if args.workload == "churn":
-        run_churn(args, k, wl, dev)
-        return
-    if args.workload == "ws10m":
-        run_ws10m(args, k, wl, dev)
-        return
     if args.calibrate_copy:
         # a plain elementwise copy of known size: 2 GiB read + 2 GiB written
         a = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -949,6 +984,12 @@ def main():
             torch.add(a, 0.0, out=b)
         torch.cuda.synchronize()
         del a, b
+    if args.workload == "churn":
+        run_churn(args, k, wl, dev)
+        return
+    if args.workload == "ws10m":
+        run_ws10m(args, k, wl, dev)
+        return
     t_setup = time.time()
     ws = Workspace(k, wl, dev)
     ws.score_select()

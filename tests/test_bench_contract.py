@@ -58,3 +58,22 @@ def test_traffic_lookups_name_profiled_kernels():
     for _, tail in (bench.REMAT_VIEW_KERNEL, bench.REMAT_DELTA_KERNEL):
         delta, copy_v = tail.strip("<>").split(", ")[3:]
         assert f"remat_kernel<T, D, LAY, {delta}, {copy_v}>" in src
+
+
+def test_every_kernel_maps_to_the_file_that_defines_it():
+    """Counter traffic is tied to the source file of its kernel: every
+    __global__ kernel of the library maps to the file it is defined in, and
+    kernels the library does not define (the calibration copy) map to none."""
+    import glob
+    import re
+    sys.path.insert(0, ROOT)
+    import bench
+    pat = re.compile(r"__global__\s+(?:__launch_bounds__\([^)]*\)\s+)?void\s+(\w+)\s*\(")
+    seen = 0
+    for path in glob.glob(os.path.join(ROOT, "attention_space_block_amd", "csrc", "*.hip")):
+        rel = os.path.relpath(path, ROOT)
+        for name in pat.findall(open(path).read()):
+            assert bench._source_of(f"kvm::{name}<int>") == rel, name
+            seen += 1
+    assert seen >= 20
+    assert bench._source_of("at::native::vectorized_elementwise_kernel<4>") is None
