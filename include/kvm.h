@@ -177,7 +177,8 @@ int kvm_quantize_e4m3(const void* src, int32_t src_dtype, int64_t n, void* dst, 
  *           score, exact ties to the lower block id; every block when
  *           n_blocks <= budget_blocks.
  * ws        device workspace of at least kvm_select_ws_bytes(n_blocks) bytes.
- * Errors: KVM_ERANGE (n_sink + n_recent > budget_blocks), KVM_EINVAL, KVM_ENOMEM. */
+ * Errors: KVM_ERANGE (n_sink + n_recent > budget_blocks), KVM_EINVAL (null
+ * pointers, n_blocks < 1, budget_blocks < 1), KVM_ENOMEM. */
 size_t kvm_select_ws_bytes(int64_t n_blocks);
 
 int kvm_select(const float* scores, int64_t n_blocks, int32_t n_sink, int32_t n_recent,
@@ -333,7 +334,8 @@ int kvm_ctx_build_index_rope(kvm_ctx* ctx, const void* k_rope, int64_t block_str
  * position changed, and v_view = raw V for misses. page_table_dev (device
  * int32[n_sel]) receives the pool page of sel[i]. Selected block i occupies
  * positions [i*B, i*B + B). Returns once everything is enqueued; later work on
- * `stream` sees the finished view. stats_host may be NULL.
+ * `stream` sees the finished view. n_sel = 0 is an empty view: nothing is
+ * staged or launched and resident pages stay. stats_host may be NULL.
  * Errors: KVM_ERANGE (selection invalid, a miss without a source, or a gather
  * callback that failed; n_sel reported as KVM_ERANGE by kvm_select), KVM_ENOMEM
  * (pool smaller than the view), KVM_EHIP, KVM_EINTERNAL. An error after

@@ -977,6 +977,58 @@ def test_remat_error_paths(k, dev):
     assert e.value.code == k.api._abi.KVM_ERANGE
 
 
+def test_empty_inputs(k, dev):
+    """Empty inputs: a Mean-K build of no blocks writes nothing; scoring and
+    selection of no blocks are argument errors that leave their outputs alone;
+    an empty selection is an empty view that stages, launches and changes
+    nothing (the resident pages stay, and the next view reuses them)."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2)
+    dims, dt = k.dims_for(wl), k.KVM_BF16
+    raw = gc.raw_to_device(wl, "K", 0, 8, dev)
+    idx = torch.full((wl.n_layers, wl.n_kv_heads, 16, wl.head_dim), 0x1234, dtype=torch.int16,
+                     device=dev)
+    k.kvm_build_index(dims, dt, raw, wl.block_bytes, 3, 0, idx, 16)
+    torch.cuda.synchronize()
+    assert bool((idx == 0x1234).all())
+    q = gc.to_dev(synth.query(wl.scaled(n_q_tokens=1)), dev)
+    scores = torch.full((4,), -3.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_score_blocks(dims, dt, q, 1, idx, 16, 0, 0, 0, scores, ws, ws.numel())
+    assert e.value.code == k.api._abi.KVM_EINVAL
+    sel = torch.full((8,), -7, dtype=torch.int32, device=dev)
+    n_sel = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    with pytest.raises(k.KvmError) as e:
+        k.kvm_select(scores, 0, 0, 0, 8, 32, sel, n_sel, sel, ws, ws.numel())
+    assert e.value.code == k.api._abi.KVM_EINVAL
+    torch.cuda.synchronize()
+    assert bool((scores == -3.0).all()) and int(n_sel.item()) == -7
+    # an empty view between two views of the same blocks
+    wv = wl.scaled(budget_blocks=8, n_recent=2)
+    pool, keep = _remat_setup(k, dev, wv, 32, 12, "device")
+    view = torch.arange(4, 12, dtype=torch.int32, device=dev)
+    n8 = torch.tensor([8], dtype=torch.int32, device=dev)
+    st = pool.ctx.kvm_rematerialize(view, n8, pool.page)
+    torch.cuda.synchronize()
+    pg = pool.page.cpu().numpy()[:8].copy()
+    before_k, before_v = pool.k_view.clone(), pool.v_view.clone()
+    pool.page.fill_(-9)
+    st0 = pool.ctx.kvm_rematerialize(view, torch.zeros(1, dtype=torch.int32, device=dev),
+                                     pool.page)
+    torch.cuda.synchronize()
+    assert st0["n_sel"] == 0 and st0["hits"] == st0["misses"] == st0["rotated"] == 0
+    assert st0["batches"] == 0 and st0["h2d_bytes"] == 0 and st0["d2d_bytes"] == 0
+    assert bool((pool.page == -9).all())
+    assert torch.equal(pool.k_view, before_k) and torch.equal(pool.v_view, before_v)
+    st2 = pool.ctx.kvm_rematerialize(view, n8, pool.page)
+    torch.cuda.synchronize()
+    assert st["misses"] == 8 and st2["hits"] == 8 and st2["misses"] == 0 and st2["rotated"] == 0
+    assert np.array_equal(pool.page.cpu().numpy()[:8], pg)
+    gc.check_view(wv, np.arange(4, 12), pg, pool)
+    pool.ctx.close()
+
+
 # ------------------------------------------------------------ end to end ----
 
 @pytest.mark.parametrize("name", ["tiny", "ctx64k", "ctx64k_fp8"])
