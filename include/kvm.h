@@ -18,6 +18,9 @@
  *    device work is enqueued on it; calls return once the work is enqueued.
  *    No entry point synchronises the device; only kvm_rematerialize waits for
  *    `stream` (to read the selection) and kvm_ctx_sync waits for ctx work.
+ *  - kvm_build_index, kvm_score_blocks with KVM_INDEX_DEVICE, kvm_select and
+ *    kvm_select_noalloc enqueue kernels only (no allocation, copy, memset or
+ *    wait), so a caller may capture them into a HIP graph and replay it.
  *  - The caller owns every buffer it passes (inputs, outputs, workspaces,
  *    pools). The library never frees caller memory and allocates device memory
  *    only inside kvm_ctx_create.

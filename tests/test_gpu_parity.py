@@ -1029,6 +1029,64 @@ def test_empty_inputs(k, dev):
     pool.ctx.close()
 
 
+@pytest.mark.parametrize("T", [77, 1])
+def test_scoring_and_selection_replay_in_a_hip_graph(k, dev, T):
+    """Scoring (T = 77: the two matrix-core passes; T = 1: the stored-score
+    form) and the allocation-free selector enqueue only kernels on the
+    caller's stream, so they can be captured in a HIP graph. Five replays,
+    each after new queries are copied into the captured buffer and with eager
+    scoring and selection on other buffers in between, equal the eager results
+    for the same queries bit for bit."""
+    import torch
+    wl = synth.get_workload("ctx64k").scaled(n_layers=2, n_q_tokens=T)
+    N, budget = 1000, 64
+    say("hip graph replay", T)
+    raw = gc.raw_to_device(wl, "K", 0, N, dev)
+    idx = gc.build_index_dev(k, wl, raw, dev)
+    dims, dt = k.dims_for(wl), k.KVM_BF16
+    ws_b = k.kvm_score_ws_bytes(dims, dt, T, N, 0, 0)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    qs = [gc.to_dev(synth.query(wl.scaled(seed=wl.seed + 100 + t)), dev) for t in range(5)]
+    q = qs[0].clone()
+
+    def bufs():
+        return (torch.empty(N, dtype=torch.float32, device=dev),
+                torch.empty(budget, dtype=torch.int32, device=dev),
+                torch.empty(1, dtype=torch.int32, device=dev),
+                torch.empty(budget, dtype=torch.int32, device=dev))
+
+    def run(qq, out):
+        sc, se, ns, bs = out
+        k.kvm_score_blocks(dims, dt, qq, T, idx, N, N, 0, 0, sc, ws, ws_b)
+        k.kvm_select_noalloc(sc, N, 1, 8, budget, wl.block_tokens, se, ns, bs)
+
+    cap = bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(q, cap)                               # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(q, cap)
+    eager = bufs()
+    for t in range(5):
+        q.copy_(qs[t])
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in cap]
+        run(qs[t], eager)
+        torch.cuda.synchronize()
+        for a, b in zip(got, eager):
+            assert torch.equal(a, b), t
+        n = int(got[2].item())
+        assert n == budget
+        want = select_blocks(got[0].cpu().numpy().astype(np.float64), 1, 8, budget)
+        assert np.array_equal(got[1].cpu().numpy()[:n], want)
+    del g
+
+
 # ------------------------------------------------------------ end to end ----
 
 @pytest.mark.parametrize("name", ["tiny", "ctx64k", "ctx64k_fp8"])
