@@ -109,6 +109,41 @@ def test_ws1m_full_step(k, dev):
     torch._C._host_emptyCache()       # give the 16 GiB of pinned memory back
 
 
+@pytest.mark.timeout(300)
+def test_ws1m_build_index_rope_sampled(k, dev):
+    """Mean-K from K that carries RoPE (KVMem Sec. 5) at the 1M-token
+    workspace's shape (64 layers x 8 KV heads, d 128) with the context's table
+    covering all of its 2^20 positions: runs of 4 blocks at the start, middle
+    and end of the history (positions up to 2^20 - 1), bit-exact against the
+    oracle's float64 de-rotation with the fp32 table, and within half an ulp
+    plus the table's error of the exact rotation."""
+    import torch
+    from oracle import mean_k_from_rope
+    from oracle.numerics import bf16_bits
+    wl = synth.get_workload("ws1m")
+    N, B = wl.n_blocks, wl.block_tokens
+    pool = gc.Pool(k, wl, 2, N, N * B, dev)
+    for b0 in (0, N // 2 - 4, N - 4):
+        n = 4
+        say("ws1m post-RoPE Mean-K, blocks", b0, b0 + n)
+        k_rope = synth.kv_blocks(wl, "K", b0, n)            # stands for cached K
+        kd = gc.to_dev(k_rope.reshape(n, -1), dev)
+        index = torch.zeros((wl.n_layers, wl.n_kv_heads, n, wl.head_dim), dtype=torch.int16,
+                            device=dev)
+        pool.ctx.kvm_ctx_build_index_rope(kd, wl.block_bytes, 0, n, B * b0, index, n)
+        got = gc.to_host_bits(index)
+        kf = op.as_f64(k_rope, wl.dtype)
+        want = np.transpose(mean_k_from_rope(kf, B * b0, "bf16", wl.theta, wl.rope_layout),
+                            (1, 2, 0, 3))
+        assert np.array_equal(got, bf16_bits(want)), b0
+        exact = np.transpose(mean_k_from_rope(kf, B * b0, "f64", wl.theta, wl.rope_layout,
+                                              table_fp32=False), (1, 2, 0, 3))
+        ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - 7)
+        table_err = 2.0 * np.abs(kf).max() * 2.0 ** -24
+        assert np.all(np.abs(op.as_f64(got, "bf16") - exact) <= 0.5 * ulp + table_err), b0
+    pool.ctx.close()
+
+
 @pytest.mark.timeout(600)
 def test_ws10m_scores_resident_match_oracle(k, dev):
     """The 10M-token workspace (312,500 blocks, index in HBM, one query token):
