@@ -220,3 +220,21 @@ def check_selection(sel: np.ndarray, R_oracle: np.ndarray, n_sink: int, n_recent
     assert set(above.tolist()) <= s, "a block clearly above the cutoff was not selected"
     assert not (set(below.tolist()) & s), "a block clearly below the cutoff was selected"
     return int(len(cand) - len(above) - len(below))
+
+
+def pair_error_in_bound(got, exact, n_delta, layout):
+    """Per (a, b) pair: |stored - exact| <= (n + 1) * sqrt(2)/2 ulp_bf16 of the
+    pair's length (each store rounds, rotations keep earlier error's length),
+    plus the fp32 rotation's own error. Returns the worst error in ulps."""
+    if layout == 0:
+        ea, eb = got[..., 0::2] - exact[..., 0::2], got[..., 1::2] - exact[..., 1::2]
+        na, nb = exact[..., 0::2], exact[..., 1::2]
+    else:
+        h = got.shape[-1] // 2
+        ea, eb = got[..., :h] - exact[..., :h], got[..., h:] - exact[..., h:]
+        na, nb = exact[..., :h], exact[..., h:]
+    err, norm = np.hypot(ea, eb), np.hypot(na, nb)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(1.1 * norm, 2.0 ** -100))) - 7)
+    bound = (n_delta + 1) * (np.sqrt(2) / 2 * ulp + 1e-6 * norm)
+    assert np.all(err <= bound)
+    return float(np.max(err / (2.0 ** (np.floor(np.log2(np.maximum(norm, 2.0 ** -100))) - 7))))

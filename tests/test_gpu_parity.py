@@ -731,24 +731,6 @@ def _remat_two_steps(k, dev, wl, src):
     pool.ctx.close()
 
 
-def _pair_error_in_bound(got, exact, n_delta, layout):
-    """Per (a, b) pair: |stored - exact| <= (n + 1) * sqrt(2)/2 ulp_bf16 of the
-    pair's length (each store rounds, rotations keep earlier error's length),
-    plus the fp32 rotation's own error. Returns the worst error in ulps."""
-    if layout == 0:
-        ea, eb = got[..., 0::2] - exact[..., 0::2], got[..., 1::2] - exact[..., 1::2]
-        na, nb = exact[..., 0::2], exact[..., 1::2]
-    else:
-        h = got.shape[-1] // 2
-        ea, eb = got[..., :h] - exact[..., :h], got[..., h:] - exact[..., h:]
-        na, nb = exact[..., :h], exact[..., h:]
-    err, norm = np.hypot(ea, eb), np.hypot(na, nb)
-    ulp = 2.0 ** (np.floor(np.log2(np.maximum(1.1 * norm, 2.0 ** -100))) - 7)
-    bound = (n_delta + 1) * (np.sqrt(2) / 2 * ulp + 1e-6 * norm)
-    assert np.all(err <= bound)
-    return float(np.max(err / (2.0 ** (np.floor(np.log2(np.maximum(norm, 2.0 ** -100))) - 7))))
-
-
 @pytest.mark.parametrize("src,layout", [("device", 0), ("pinned", 0), ("gather", 0),
                                         ("device", 1)])
 def test_delta_rerope_bounded_and_rebuilt(k, dev, src, layout):
@@ -784,7 +766,7 @@ def test_delta_rerope_bounded_and_rebuilt(k, dev, src, layout):
             got = op.as_f64(gc.to_host_bits(pool.k_view[int(pg[i])]).reshape(raw_k[b].shape),
                             "bf16")
             exact = rope_rotate(raw_k[b], i * B + np.arange(B), layout=wl.rope_layout)
-            worst = max(worst, _pair_error_in_bound(got, exact, counts[-1], wl.rope_layout))
+            worst = max(worst, gc.pair_error_in_bound(got, exact, counts[-1], wl.rope_layout))
             if kinds[-1] == "full":
                 assert np.max(np.abs(got - exact)) <= 2e-2
             v = gc.to_host_bits(pool.v_view[int(pg[i])])
@@ -878,7 +860,7 @@ def test_delta_rerope_error_growth(k, dev):
         exact = rope_rotate(raw, a * B + np.arange(B))
         n = pool.ctx.kvm_ctx_block_deltas(39)
         assert n == t
-        growth.append((n, _pair_error_in_bound(got, exact, n, wl.rope_layout),
+        growth.append((n, gc.pair_error_in_bound(got, exact, n, wl.rope_layout),
                        float(np.max(np.abs(got - exact)))))
     say("delta count, worst pair error (ulp of the pair length), worst abs error:")
     for n, e_ulp, e_abs in growth:

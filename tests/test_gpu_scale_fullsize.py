@@ -144,6 +144,69 @@ def test_ws1m_build_index_rope_sampled(k, dev):
     pool.ctx.close()
 
 
+@pytest.mark.timeout(300)
+def test_ws1m_delta_rerope_full_pages(k, dev):
+    """Bounded delta re-RoPE (KVMem Sec. 4.4, limit 2) on pages of the 1M-token
+    workspace's shape (64 layers x 8 KV heads, 512 (layer, KV head) units per
+    page), with raw K/V in HBM: three tracked blocks stay selected while up
+    to 390 earlier blocks enter and leave the view, so their compact positions
+    shift by up to 12K positions and every third change rebuilds from raw K.
+    Their K within the delta bound of the exact rotation (and within 2e-2 when
+    rebuilt), V byte-exact, and every step's delta, rebuild and miss counts as
+    the oracle's bounded_delta_rope gives them for the whole view."""
+    import torch
+    from oracle import bounded_delta_rope, rope_rotate
+    wl = synth.get_workload("ws1m")
+    B, limit = wl.block_tokens, 2
+    tracked = [400, 401, 450]
+    prefix = [5, 300, 40, 390, 390, 120, 3, 200]
+    M = max(tracked) + 1
+    n_slots = max(prefix) + len(tracked) + 8
+    say("ws1m delta re-RoPE: raw K/V of", M, "blocks")
+    rk = gc.raw_to_device(wl, "K", 0, M, dev)
+    rv = gc.raw_to_device(wl, "V", 0, M, dev)
+    pool = gc.Pool(k, wl, n_slots, wl.n_blocks, n_slots * B, dev, delta_limit=limit)
+    pool.ctx.kvm_ctx_set_source(0, M, rk, rv, wl.block_bytes, k.KVM_SRC_DEVICE)
+    raw_k = {b: op.as_f64(synth.kv_blocks(wl, "K", b, 1)[0], "bf16") for b in tracked}
+    dummy = np.ones((B, 2))                      # kinds and counts do not depend on values
+    placements = {}
+    for t, a in enumerate(prefix):
+        sel_list = list(range(a)) + tracked
+        for i, b in enumerate(sel_list):
+            placements.setdefault(b, []).append(i * B)
+        sel = torch.tensor(sel_list, dtype=torch.int32, device=dev)
+        n_sel = torch.tensor([len(sel_list)], dtype=torch.int32, device=dev)
+        st = pool.ctx.kvm_rematerialize(sel, n_sel, pool.page)
+        torch.cuda.synchronize()
+        pg = pool.page.cpu().numpy()[:len(sel_list)]
+        kinds = {b: bounded_delta_rope(dummy, placements[b], limit, "f64")[1][-1]
+                 for b in sel_list}
+        worst = 0.0
+        for i, b in enumerate(sel_list):
+            if b not in raw_k:
+                continue
+            _, kb, counts = bounded_delta_rope(raw_k[b], placements[b], limit, "bf16",
+                                               layout=wl.rope_layout)
+            assert kb[-1] == kinds[b] and pool.ctx.kvm_ctx_block_deltas(b) == counts[-1]
+            got = op.as_f64(gc.to_host_bits(pool.k_view[int(pg[i])]).reshape(raw_k[b].shape),
+                            "bf16")
+            exact = rope_rotate(raw_k[b], i * B + np.arange(B), layout=wl.rope_layout)
+            worst = max(worst, gc.pair_error_in_bound(got, exact, counts[-1], wl.rope_layout))
+            if kinds[b] == "full":
+                assert np.max(np.abs(got - exact)) <= 2e-2
+            v = gc.to_host_bits(pool.v_view[int(pg[i])])
+            assert np.array_equal(v, synth.kv_blocks(wl, "V", b, 1).reshape(-1))
+        misses = sum(1 for b in sel_list if len(placements[b]) == 1)
+        n_delta = sum(1 for x in kinds.values() if x == "delta")
+        n_full = sum(1 for x in kinds.values() if x == "full")
+        assert st["misses"] == misses and st["deltas"] == n_delta
+        assert st["rebuilds"] == n_full - misses
+        say(f"step {t}: prefix {a}, deltas {st['deltas']}, rebuilds {st['rebuilds']}, "
+            f"misses {st['misses']}, worst tracked pair error {worst:.2f} ulp")
+    pool.ctx.close()
+    del rk, rv
+
+
 @pytest.mark.timeout(600)
 def test_ws10m_scores_resident_match_oracle(k, dev):
     """The 10M-token workspace (312,500 blocks, index in HBM, one query token):
