@@ -207,6 +207,50 @@ def test_ws1m_delta_rerope_full_pages(k, dev):
     del rk, rv
 
 
+@pytest.mark.timeout(300)
+def test_ws1m_fp8_scores_one_pair(k, dev):
+    """The FP8 scoring ablation at the 1M-token shape of one (layer, KV head)
+    pair (KVMem Sec. 4.3 Eq. (10) per pair; Sec. 6.1 FP8): all 32768 blocks and
+    T*G = 3072 query rows (512 query tokens x 6 heads), E4M3 queries and Mean-K
+    encoded by the oracle, scored through the same entry point on the pair's
+    slices, against the oracle's float64 Eq. (10) of the decoded values within
+    1e-5, and the bf16 form of the same slices against the oracle too. The
+    pair's index rows are drawn directly (a full Mean-K build would need all
+    128 GiB of the workspace's raw K)."""
+    import torch
+    from oracle.numerics import fp8_decode, fp8_encode
+    from oracle.scores import block_scores
+    wl = synth.get_workload("ws1m")
+    N, T, d, G = wl.n_blocks, wl.n_q_tokens, wl.head_dim, wl.n_q_heads // wl.n_kv_heads
+    l, g = 37, 5
+    say("ws1m FP8 scores of pair", (l, g))
+    idx = synth.index_direct(wl, 0, N, lg0=l * wl.n_kv_heads + g, n_lg=1)   # [1][N][d] bits
+    q_all = synth.query(wl)                                                  # [L][Hq][T][d]
+    qp = np.ascontiguousarray(q_all[l:l + 1, g * G:(g + 1) * G])             # [1][G][T][d]
+    del q_all
+    pw = wl.scaled(n_layers=1, n_kv_heads=1, n_q_heads=G)
+    dims = k.dims_for(pw)
+    for dt in ("fp8", "bf16"):
+        if dt == "fp8":
+            qb = fp8_encode(op.as_f64(qp, "bf16"))
+            ib = fp8_encode(op.as_f64(idx, "bf16")).reshape(1, 1, N, d)
+            ref = block_scores(fp8_decode(qb), fp8_decode(ib))
+            code, qd, idd = k.KVM_FP8_E4M3, torch.from_numpy(qb), torch.from_numpy(ib)
+        else:
+            ref = block_scores(op.as_f64(qp, "bf16"), op.as_f64(idx, "bf16").reshape(1, 1, N, d))
+            code = k.KVM_BF16
+            qd = torch.from_numpy(qp.view(np.int16))
+            idd = torch.from_numpy(idx.view(np.int16).reshape(1, 1, N, d))
+        ws_b = k.kvm_score_ws_bytes(dims, code, T, N, 0, 0)
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+        scores = torch.empty(N, dtype=torch.float32, device=dev)
+        k.kvm_score_blocks(dims, code, qd.to(dev), T, idd.to(dev), N, N, 0, 0, scores, ws, ws_b)
+        got = scores.cpu().numpy().astype(np.float64)
+        rel = np.abs(got - ref) / ref
+        say(dt, "max rel err", rel.max(), "sum", got.sum())
+        assert rel.max() <= 1e-5 and abs(got.sum() - T) <= 1e-5 * T
+
+
 @pytest.mark.timeout(600)
 def test_ws10m_scores_resident_match_oracle(k, dev):
     """The 10M-token workspace (312,500 blocks, index in HBM, one query token):
