@@ -290,6 +290,71 @@ def test_ws10m_scores_resident_match_oracle(k, dev):
     gc.check_selection(s, g["R"], wl.n_sink, wl.n_recent, wl.budget_blocks)
 
 
+@pytest.mark.timeout(300)
+def test_ws10m_host_tiled_one_pair(k, dev):
+    """Host-tiled scoring at the 10M-token length (KVMem Sec. 5: the index in
+    host memory, streamed in fixed tiles, with the global softmax kept) on one
+    (layer, KV head) pair: all 312,500 blocks in 611 tiles of 512 from pinned
+    host memory, one query token x 6 heads, bf16 and FP8 E4M3. Each equals the
+    resident index's scores bit for bit, and the oracle's float64 Eq. (10)
+    within 1e-5 (bf16) or 1e-4 (FP8: the matrix core accumulates E4M3 products
+    about 11-13 bits below the largest one, and with 6 query rows per block R_b
+    does not average those errors as it does over a whole workspace); the
+    selection equals the oracle's selector on the GPU's scores."""
+    import torch
+    from oracle.numerics import fp8_decode, fp8_encode
+    from oracle.scores import block_scores
+    wl = synth.get_workload("ws10m")
+    N, tb, d, G = wl.n_blocks, wl.tile_blocks, wl.head_dim, wl.n_q_heads // wl.n_kv_heads
+    ntile = (N + tb - 1) // tb
+    l, g = 50, 3
+    say("ws10m host-tiled, pair", (l, g), ntile, "tiles")
+    idx = synth.index_direct(wl, 0, N, lg0=l * wl.n_kv_heads + g, n_lg=1)   # [1][N][d] bits
+    qp = np.ascontiguousarray(synth.query(wl)[l:l + 1, g * G:(g + 1) * G])   # [1][G][1][d]
+    dims = k.dims_for(wl.scaled(n_layers=1, n_kv_heads=1, n_q_heads=G))
+    for dt in ("bf16", "fp8"):
+        if dt == "bf16":
+            code, esz = k.KVM_BF16, 2
+            qh, ih = qp.view(np.int16), idx.view(np.int16).reshape(N, d)
+            ref = block_scores(op.as_f64(qp, "bf16"), op.as_f64(idx, "bf16").reshape(1, 1, N, d))
+            tdt = torch.int16
+        else:
+            code, esz = k.KVM_FP8_E4M3, 1
+            qh = fp8_encode(op.as_f64(qp, "bf16"))
+            ih = fp8_encode(op.as_f64(idx, "bf16")).reshape(N, d)
+            ref = block_scores(fp8_decode(qh), fp8_decode(ih).reshape(1, 1, N, d))
+            tdt = torch.uint8
+        host = torch.zeros((ntile, 1, tb, d), dtype=tdt).pin_memory()
+        hv = host.numpy()
+        for t in range(ntile):
+            nb = min(tb, N - t * tb)
+            hv[t, 0, :nb] = ih[t * tb:t * tb + nb]
+        q = torch.from_numpy(np.ascontiguousarray(qh)).to(dev)
+        index = torch.from_numpy(np.ascontiguousarray(ih)).to(dev)
+        out = {}
+        for loc, src, tiles in ((0, index, 0), (1, host, tb)):
+            ws_b = k.kvm_score_ws_bytes(dims, code, 1, N, loc, tiles)
+            ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+            sc = torch.empty(N, dtype=torch.float32, device=dev)
+            k.kvm_score_blocks(dims, code, q, 1, src, N, N, loc, tiles, sc, ws, ws_b)
+            out[loc] = sc
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], out[1]), dt
+        got = out[1].cpu().numpy().astype(np.float64)
+        rel = np.abs(got - ref) / ref
+        say(dt, "max rel err", rel.max(), "sum", got.sum())
+        tol = 1e-5 if dt == "bf16" else 1e-4
+        assert rel.max() <= tol and abs(got.sum() - 1.0) <= tol
+        sel, n_sel, _ = gc.select_dev(k, out[1], N, wl.n_sink, wl.n_recent, wl.budget_blocks,
+                                      dev)
+        n = int(n_sel.item())
+        assert n == wl.budget_blocks
+        assert np.array_equal(sel.cpu().numpy()[:n],
+                              select_blocks(got, wl.n_sink, wl.n_recent, wl.budget_blocks))
+        del host, index, q
+    torch._C._host_emptyCache()
+
+
 @pytest.mark.timeout(660)
 @pytest.mark.skipif(os.environ.get("KVM_HOST_TILED_10M_ALONE") != "1",
                     reason="runs only when asked for, with nothing before it in the process "
