@@ -52,12 +52,19 @@ static constexpr int32_t REMAT_JOBS_PER_LAUNCH = 16384;
 // 256 threads 8.81 ms; a plain device copy moves 6.4 TB/s in 64-thread
 // workgroups against 6.1 in 256-thread ones.
 static constexpr int REMAT_TPB = 64;
-// Page loads from a buffer other than the one written are non-temporal
-// (8.16 ms against 8.26 for the view above); the in-place delta rotation keeps
-// plain loads (5.47 ms against 5.74 non-temporal).
+// Pages read from a buffer other than the one written are loaded and stored
+// non-temporally (8.16 ms against 8.26 with plain loads for the view above,
+// then 8.03 against 8.16 with the stores too; FP8 view 4.20 against 4.38);
+// the in-place delta rotation keeps plain loads and stores (5.47 ms against
+// 5.74 with non-temporal loads).
 template <bool NT>
 __device__ __forceinline__ uint4 ld_page(const void* p) {
   return NT ? ld_nt(p) : ld_plain(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_page(void* p, const uint4& v) {
+  if (NT) st_nt(p, v);
+  else st_plain(p, v);
 }
 static constexpr int remat_units_per_item(int elem_bytes) {
   return elem_bytes == 1 ? KVM_REMAT_R_FP8 : elem_bytes == 2 ? KVM_REMAT_R_BF16 : 1;
@@ -137,9 +144,9 @@ __device__ __forceinline__ uint4 pack<float>(const float* x) {
 // DRAM serves best (a plain copy in this shape moves about 6.1-6.6 TB/s,
 // against 3.6 TB/s when each thread loads sixteen pieces before storing them);
 // each thread reads the (cos, sin) of its pairs from the fp32 table
-// (L2-resident: 32 positions of a job span at most 32 table rows). Stores are
-// plain (cached); page loads are non-temporal except in the in-place delta
-// rotation (see ld_page).
+// (L2-resident: 32 positions of a job span at most 32 table rows). Page loads
+// and stores are non-temporal except in the in-place delta rotation (see
+// ld_page).
 template <typename T, int D, int LAYOUT, bool DELTA, bool COPYV>
 __global__ __launch_bounds__(REMAT_TPB) void remat_kernel(RematArgs a) {
   constexpr int P = 16 / sizeof(T);              // elements per piece
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(REMAT_TPB) void remat_kernel(RematArgs a) {
     if ((job.flags & JOB_COPY_V) == 0) return;
     const int64_t off = ((int64_t)part * REMAT_TPB + threadIdx.x) * 16;
     if (off >= a.page_bytes) return;
-    st_plain(a.v_view + (int64_t)job.slot * a.page_bytes + off, ld_page<true>(job.src_v + off));
+    st_page<true>(a.v_view + (int64_t)job.slot * a.page_bytes + off, ld_page<true>(job.src_v + off));
     // keeps this path's store its own: merged with the K path's stores, the
     // compiler splits every 16-byte store into a 4- and a 12-byte one
     asm volatile("" ::: "memory");
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(REMAT_TPB) void remat_kernel(RematArgs a) {
         y0[2 * q] = x0[2 * q] * cs[q].x - x0[2 * q + 1] * cs[q].y;
         y0[2 * q + 1] = x0[2 * q] * cs[q].y + x0[2 * q + 1] * cs[q].x;
       }
-      st_plain(kv + b0, pack<T>(y0));
+      st_page<!DELTA>(kv + b0, pack<T>(y0));
     } else {
       const int64_t b1 = b0 + HALF * (int64_t)sizeof(T);
       const uint4 k1 = ld_page<!DELTA>(job.src_k + b1);
@@ -213,8 +220,8 @@ __global__ __launch_bounds__(REMAT_TPB) void remat_kernel(RematArgs a) {
         y0[q] = x0[q] * cs[q].x - x1[q] * cs[q].y;
         y1[q] = x0[q] * cs[q].y + x1[q] * cs[q].x;
       }
-      st_plain(kv + b0, pack<T>(y0));
-      st_plain(kv + b1, pack<T>(y1));
+      st_page<!DELTA>(kv + b0, pack<T>(y0));
+      st_page<!DELTA>(kv + b1, pack<T>(y1));
     }
   }
 }
