@@ -21,18 +21,19 @@ static constexpr int PROBE_WG_MIX = 512;     // 2 per CU: two waves per SIMD, as
 static constexpr int PROBE_THREADS = 256;
 
 // n16 16-byte words from src to dst, one per thread over a grid of one-wave
-// workgroups that covers them all, read with non-temporal loads: the fastest
-// copy shape measured here (6.6-6.7 TB/s for 2 GiB, against 6.4 with plain
-// loads, 6.1 with 256-thread workgroups, 5.6 with four words per thread, 3.6
-// with sixteen loaded before their stores, 4.5-4.9 with grid-stride loops and
-// 4.9-5.0 for the runtime's device copy), since the workgroups in flight then
-// cover one narrow address range.
+// workgroups that covers them all, with non-temporal loads and stores: the
+// fastest copy shape measured here (medians of 20: 6.68 TB/s for 2 GiB,
+// against 6.60 with plain stores, 6.4 with plain loads and stores, 6.1 with
+// 256-thread workgroups, 5.6 with four words per thread, 3.6 with sixteen
+// loaded before their stores, 4.5-4.9 with grid-stride loops and 4.9-5.0 for
+// the runtime's device copy), since the workgroups in flight then cover one
+// narrow address range.
 static constexpr int PROBE_COPY_TPB = 64;
 __global__ __launch_bounds__(PROBE_COPY_TPB) void probe_copy_kernel(const uint4* __restrict__ src,
                                                                     uint4* __restrict__ dst,
                                                                     int64_t n16) {
   const int64_t i = (int64_t)blockIdx.x * PROBE_COPY_TPB + threadIdx.x;
-  if (i < n16) dst[i] = ld_nt(src + i);
+  if (i < n16) st_nt(dst + i, ld_nt(src + i));
 }
 
 // MODE 0: two MFMA chains; 1: eight exp chains; 2: the score passes' mix.

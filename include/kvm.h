@@ -414,7 +414,7 @@ int kvm_tier_simulate(const kvm_tier_policy* policy, int32_t n_steps, const int6
  *                      of n bytes from scratch to scratch + n (n a multiple of
  *                      16, scratch >= 2n bytes, device, 16-byte aligned): one
  *                      16-byte word per thread, one-wave workgroups,
- *                      non-temporal loads;
+ *                      non-temporal loads and stores;
  *  KVM_RATE_MFMA_BF16  bf16 matrix flop/s of a register-only
  *                      v_mfma_f32_32x32x16_bf16 loop, n iterations of two
  *                      MFMAs per wave (8 waves per SIMD);
