@@ -163,12 +163,18 @@ class KvmCtx:
         h = ctypes.c_void_p()
         _abi.check(_abi.lib().kvm_ctx_create(ctypes.byref(d), ctypes.byref(h)), "kvm_ctx_create")
         self._h = h
-        self._keep = []           # callbacks and buffers the library points at
+        # objects the library keeps pointers to: the pool pages for the ctx's
+        # life, gather callbacks, and the lower-tier buffers of each recorded
+        # block range (replaced when the same range is recorded again)
+        self._keep = [k_view, v_view, k_shadow]
+        self._sources = {}
 
     def close(self):
         if self._h:
             _abi.lib().kvm_ctx_destroy(self._h)
             self._h = None
+        self._keep = []
+        self._sources = {}
 
     def __del__(self):
         try:
@@ -181,6 +187,7 @@ class KvmCtx:
         rc = _abi.lib().kvm_ctx_set_source(self._h, first_block, n_blocks, _ptr(k_base),
                                            _ptr(v_base), block_stride, loc)
         _abi.check(rc, "kvm_ctx_set_source")
+        self._sources[(first_block, n_blocks)] = (k_base, v_base)
 
     def kvm_ctx_set_gather(self, first_block: int, n_blocks: int, fn) -> None:
         """fn(block, which, dst_ptr) -> int, called from library worker threads."""
