@@ -939,10 +939,16 @@ def write_traffic_profile(value_dir: str, delta_dir: str, out_path: str) -> dict
     json.dump(out, open(out_path, "w"), indent=1)
     return out
 
-def write_traffic_profile_ws10m(run_dir: str, out_path: str) -> dict:
-    """profiles/ws10m_traffic.json: calibrated read/write bytes per dispatch of
-    the 10M-token workspace's resident legs (a run with --host-tiled 0), with
-    source fingerprints as above."""
+# workloads with a traffic file of their own: profiles/<name>_traffic.json
+# written from one counter run by --write-traffic-run <dir> <name>
+TRAFFIC_RUNS = {"ws10m": "10M-token workspace, resident index legs (bench.py --workload ws10m "
+                         "--host-tiled 0)",
+                "ctx64k": "64K-token history step (bench.py --workload ctx64k)"}
+
+
+def write_traffic_profile_run(run_dir: str, name: str) -> dict:
+    """profiles/<name>_traffic.json: calibrated read/write bytes per dispatch of
+    one workload's counter run, with source fingerprints as above."""
     v = json.load(open(os.path.join(run_dir, "summary.json")))
     per = {}
     for k, x in v["traffic"].items():
@@ -950,15 +956,14 @@ def write_traffic_profile_ws10m(run_dir: str, out_path: str) -> dict:
         if src:
             per[k] = dict(x, source=src,
                           source_sha256_16=source_fingerprint(os.path.join(ROOT, src)))
-    out = {"workload": "10M-token workspace, resident index legs (bench.py --workload ws10m "
-                       "--host-tiled 0)", "calibration": v["calibration"], "per_dispatch": per}
-    json.dump(out, open(out_path, "w"), indent=1)
+    out = {"workload": TRAFFIC_RUNS[name], "calibration": v["calibration"], "per_dispatch": per}
+    json.dump(out, open(os.path.join(ROOT, "profiles", f"{name}_traffic.json"), "w"), indent=1)
     return out
 
 
 def main():
-    if len(sys.argv) > 3 and sys.argv[1] == "--write-traffic-ws10m":
-        write_traffic_profile_ws10m(sys.argv[2], sys.argv[3])
+    if len(sys.argv) > 3 and sys.argv[1] == "--write-traffic-run":
+        write_traffic_profile_run(sys.argv[2], sys.argv[3])
         return
     if len(sys.argv) > 2 and sys.argv[1] == "--summarize-rocprof":
         print(json.dumps(summarize_rocprof(sys.argv[2])["calibration"]))
@@ -1034,10 +1039,10 @@ def main():
         # kernel time of one step's rematerialization (all its remat launches)
         remat["per_step_ms"] = remat["avg_ms"] * remat["launches"] / args.steps
     remat_gbps = remat_bytes / (remat["per_step_ms"] * 1e-3) / 1e9 if remat else None
-    # rooflines: the dominant kernel of the step, and the other kernels of the path
-    # the committed counters were taken on the 1M-token workspace: other
-    # workloads report no traffic rather than that workload's bytes
-    traffic = counter_traffic() if args.workload == "ws1m" else {}
+    # rooflines: the dominant kernel of the step, and the other kernels of the path;
+    # each workload reads the counters taken on its own runs (none: null traffic)
+    traffic = (counter_traffic() if args.workload == "ws1m" else
+               counter_traffic(f"{args.workload}_traffic.json"))
 
     def roofline(name, info):
         if name.startswith("score_pass"):

@@ -54,6 +54,13 @@ def test_traffic_lookups_name_profiled_kernels():
     for short, tail in looks:
         hits = [n for n in per if n.split("<")[0].endswith(short) and n.endswith(tail)]
         assert len(hits) == 1, (short, tail)
+    # the 10M- and 64K-token lines read their own counter files
+    for name, (short, tail) in (("ws10m", ("score_stored_pass1_mfma", bench.STORED_KERNEL_TAIL)),
+                                ("ctx64k", bench.REMAT_VIEW_KERNEL)):
+        per_w = json.load(open(os.path.join(ROOT, "profiles", f"{name}_traffic.json")))
+        hits = [n for n in per_w["per_dispatch"]
+                if n.split("<")[0].endswith(short) and n.endswith(tail)]
+        assert len(hits) == 1, (name, short, tail)
     src = open(os.path.join(ROOT, "attention_space_block_amd", "csrc", "remat.hip")).read()
     for _, tail in (bench.REMAT_VIEW_KERNEL, bench.REMAT_DELTA_KERNEL):
         delta, copy_v = tail.strip("<>").split(", ")[3:]
